@@ -1,0 +1,156 @@
+"""CPU oracle for the NVFP4 skinny GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this package. It
+shares no code with the HIP library and imports nothing from it. Every function takes and returns
+numpy arrays; the arithmetic is in nvfp4_oracle.c (decoders by closed form, rounding by
+enumeration, the quantisation recipe in fp32 one step at a time, the GEMM in double).
+
+What it computes, from the pages and the workload recipe:
+  "Qwen3.8-27B-NVFP4-RTX5090" model card, table "Recipe (NVIDIA ModelOpt)": NVFP4 weights with group
+  size 16; section "Why lm_head is NVFP4": decode streams every weight once per token.
+  Per tensor g = amax / (6*448); per 16-block along K an E4M3 scale s = round(block_amax / (6g));
+  codes = round-to-nearest E2M1 of w / (s*g); Y = X . (e2m1(code) * s * g).
+Pins for every function live in tests/test_oracle_*.py; none is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    """Load the compiled oracle, compiling it first if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB) or (
+            os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    c_u8p = ctypes.POINTER(ctypes.c_uint8)
+    c_fp = ctypes.POINTER(ctypes.c_float)
+    c_dp = ctypes.POINTER(ctypes.c_double)
+    L.oracle_e2m1_value.argtypes = [ctypes.c_int]
+    L.oracle_e2m1_value.restype = ctypes.c_double
+    L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+    L.oracle_e4m3_value.restype = ctypes.c_double
+    L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    L.oracle_bf16_value.restype = ctypes.c_double
+    L.oracle_e2m1_round.argtypes = [ctypes.c_float]
+    L.oracle_e2m1_round.restype = ctypes.c_uint8
+    L.oracle_e4m3_round.argtypes = [ctypes.c_float]
+    L.oracle_e4m3_round.restype = ctypes.c_uint8
+    L.oracle_e2m1_round_array.argtypes = [c_fp, ctypes.c_size_t, c_u8p]
+    L.oracle_e2m1_round_array.restype = None
+    L.oracle_e4m3_round_array.argtypes = [c_fp, ctypes.c_size_t, c_u8p]
+    L.oracle_e4m3_round_array.restype = None
+    L.oracle_quantize.argtypes = [ctypes.c_int, ctypes.c_int, c_fp, c_u8p, c_u8p, c_fp]
+    L.oracle_quantize.restype = None
+    L.oracle_dequantize.argtypes = [ctypes.c_int, ctypes.c_int, c_u8p, c_u8p, ctypes.c_float, c_dp]
+    L.oracle_dequantize.restype = None
+    L.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.POINTER(ctypes.c_uint16), c_u8p, c_u8p, ctypes.c_float,
+                              ctypes.POINTER(ctypes.c_int), ctypes.c_int, c_dp, c_dp]
+    L.oracle_gemm.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(int(code))
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().oracle_e4m3_value(int(byte))
+
+
+def bf16_value(bits: int) -> float:
+    return lib().oracle_bf16_value(int(bits))
+
+
+def e2m1_round(q) -> np.ndarray:
+    """Nearest E2M1 code (ties to even, saturating) for every float32 in q."""
+    q = np.ascontiguousarray(q, dtype=np.float32).reshape(-1)
+    out = np.empty(q.size, dtype=np.uint8)
+    lib().oracle_e2m1_round_array(_ptr(q, ctypes.c_float), q.size, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def e4m3_round(t) -> np.ndarray:
+    """Nearest finite E4M3 byte (ties to even, saturating at 448) for every float32 in t."""
+    t = np.ascontiguousarray(t, dtype=np.float32).reshape(-1)
+    out = np.empty(t.size, dtype=np.uint8)
+    lib().oracle_e4m3_round_array(_ptr(t, ctypes.c_float), t.size, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def quantize(W: np.ndarray):
+    """fp32 W[K][N] -> (Wq uint8 [N][K/2], Ws uint8 [N][K/16], g float32)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    K, N = W.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    Wq = np.empty((N, K // 2), dtype=np.uint8)
+    Ws = np.empty((N, K // 16), dtype=np.uint8)
+    g = np.zeros(1, dtype=np.float32)
+    lib().oracle_quantize(K, N, _ptr(W, ctypes.c_float), _ptr(Wq, ctypes.c_uint8),
+                          _ptr(Ws, ctypes.c_uint8), _ptr(g, ctypes.c_float))
+    return Wq, Ws, np.float32(g[0])
+
+
+def dequantize(Wq: np.ndarray, Ws: np.ndarray, g) -> np.ndarray:
+    """Exact dequantised weights, float64 [K][N]."""
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    Ws = np.ascontiguousarray(Ws, dtype=np.uint8)
+    N, Kh = Wq.shape
+    K = 2 * Kh
+    if Ws.shape != (N, K // 16):
+        raise ValueError("scale shape does not match the codes")
+    Wd = np.empty((K, N), dtype=np.float64)
+    lib().oracle_dequantize(K, N, _ptr(Wq, ctypes.c_uint8), _ptr(Ws, ctypes.c_uint8),
+                            ctypes.c_float(float(g)), _ptr(Wd, ctypes.c_double))
+    return Wd
+
+
+def gemm(X_bits: np.ndarray, Wq: np.ndarray, Ws: np.ndarray, g, cols=None):
+    """Y and A = sum |x*w| in float64, shape [M][len(cols)] (all N columns if cols is None).
+
+    X_bits is the bf16 bit pattern as uint16 [M][K].
+    """
+    X_bits = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    Ws = np.ascontiguousarray(Ws, dtype=np.uint8)
+    M, K = X_bits.shape
+    N = Wq.shape[0]
+    if Wq.shape != (N, K // 2) or Ws.shape != (N, K // 16):
+        raise ValueError("weight shapes do not match X")
+    if cols is None:
+        cols_arr = None
+        ncols = N
+    else:
+        cols_arr = np.ascontiguousarray(cols, dtype=np.int32)
+        if cols_arr.size and (cols_arr.min() < 0 or cols_arr.max() >= N):
+            raise ValueError("column index out of range")
+        ncols = cols_arr.size
+    Y = np.empty((M, ncols), dtype=np.float64)
+    A = np.empty((M, ncols), dtype=np.float64)
+    rc = lib().oracle_gemm(M, N, K, _ptr(X_bits, ctypes.c_uint16), _ptr(Wq, ctypes.c_uint8),
+                           _ptr(Ws, ctypes.c_uint8), ctypes.c_float(float(g)),
+                           None if cols_arr is None else _ptr(cols_arr, ctypes.c_int), ncols,
+                           _ptr(Y, ctypes.c_double), _ptr(A, ctypes.c_double))
+    if rc:
+        raise MemoryError("oracle_gemm could not allocate its buffers")
+    return Y, A
+
+
+def tolerance(A: np.ndarray) -> np.ndarray:
+    """Per-output acceptance bound |Y - Y_ref| <= 2e-3 * sum|x*w| + 1e-6."""
+    return 2e-3 * A + 1e-6
