@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 skinny GEMM on one MI355X: achieved HBM GB/s and % of the 8 TB/s peak.
+
+Workload of the headline line: one dense 5120-hidden decoder layer at M = 1 (plain decode),
+seeds 1-6: q/k/v N=7168, o_proj N=5120, gate/up N=34816 (K=5120) and down K=17408 N=5120,
+x in bf16 with 4 outlier channels x20. One step = the four GEMMs of the layer (the whole path:
+stream packed codes and scales, decode, multiply-accumulate, scale, store). The weights are
+quantised once on the GPU before timing (set-up, untimed).
+
+Protocol
+  * Cold weights: C distinct copies of the packed layer (C x 186 MB > 2 x the 256 MB Infinity
+    Cache) are rotated, so every step streams its weights from HBM.
+  * The step is captured once per copy in a HIP graph; warmup replays, then exactly `steps`
+    replays bracketed by torch.cuda.synchronize(), timed on the host clock.
+  * Per-kernel durations: HIP events around every GEMM launch, on the stream the kernels run on,
+    over `steps` eager steps; the dominant kernel (gate/up) gives the roofline object.
+  * The GPU output is checked against the oracle, and the oracle itself is timed on the host
+    cores on the same layer (cpu_baseline).
+  * "also": the verify shapes at M = 16 and M = 128, timed the same way (per-kernel events).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for NVFP4 skinny GEMM at M=1/16/128"
+EQUIV_MODEL_GB = 17.9     # the page's checkpoint size, for the tokens/s-equivalent figure
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "skinny_gemm_nvfp4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it was taken on the
+    current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(f"{kernel}@{workload}")
+    if not entry or entry.get("source_hash") != source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+class Layer:
+    """Packed weights (C cold copies), activations and outputs of a list of GEMMs on the GPU."""
+
+    def __init__(self, gemms, copies, dev):
+        import torch
+        import skinny_gemm_nvfp4_amd as nv
+        self.names = [g.name for g in gemms]
+        self.shapes = [g.shape for g in gemms]
+        self.X = [g.X.to(dev) for g in gemms]
+        self.Y = [torch.empty((m, n), dtype=torch.float32, device=dev) for m, n, _ in self.shapes]
+        self.packed = []
+        for g in gemms:
+            W = g.W.to(dev)
+            p = nv.pack(W)
+            del W
+            self.packed.append([p] + [tuple(t.clone() for t in p) for _ in range(copies - 1)])
+        torch.cuda.synchronize()
+        self.copies = copies
+
+    def run(self, c: int, i: int) -> None:
+        import skinny_gemm_nvfp4_amd as nv
+        Wq, Ws, g = self.packed[i][c]
+        nv.gemm(self.X[i], Wq, Ws, g, out=self.Y[i])
+
+    def step(self, c: int) -> None:
+        for i in range(len(self.names)):
+            self.run(c, i)
+
+    def kernel_times_us(self, reps: int):
+        """Average duration of every GEMM, from HIP events around each launch."""
+        import torch
+        stream = torch.cuda.current_stream()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)] for _ in self.names]
+        for r in range(reps):
+            for i in range(len(self.names)):
+                ev[i][r][0].record(stream)
+                self.run(r % self.copies, i)
+                ev[i][r][1].record(stream)
+        torch.cuda.synchronize()
+        return [1e3 * sum(a.elapsed_time(b) for a, b in ev[i]) / reps
+                for i in range(len(self.names))]
+
+
+def gemm_report(shape, us):
+    from skinny_gemm_nvfp4_amd import roofline as rl
+    M, N, K = shape
+    gbs = rl.compulsory_bytes(M, N, K) / (us * 1e-6) / 1e9
+    roof_s = max(rl.hbm_time_s(M, N, K), rl.mfma_time_s(M, N, K))
+    return {"M": M, "N": N, "K": K, "us": round(us, 3), "GB_s": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / rl.HBM_PEAK_GBS, 2),
+            "binding_roof": rl.binding_roof(M, N, K),
+            "pct_binding_roof": round(100 * roof_s / (us * 1e-6), 2)}
+
+
+def cpu_baseline(workload, seconds: float):
+    """The oracle as it stands, timed on the host cores on the same layer (weights quantised by
+    the oracle itself, untimed). Also returns the oracle outputs for the parity check."""
+    import oracle
+    from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+    packed = [oracle.quantize(g.W.numpy()) for g in workload.gemms]
+    xbits = [inputs.bf16_bits(g.X) for g in workload.gemms]
+    bytes_per_pass = sum(rl.compulsory_bytes(*g.shape) for g in workload.gemms)
+    refs = None
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        out = [oracle.gemm(x, *p) for x, p in zip(xbits, packed)]
+        passes += 1
+        refs = refs or out
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    rec = {"value": round(bytes_per_pass * passes / dt / 1e9, 4), "unit": "GB/s",
+           "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"whole layer (4 GEMMs) at M=1, {passes} pass(es) in {dt:.1f} s, "
+                     "double accumulation, OpenMP over output columns"}
+    return rec, refs
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cold-copies", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true", help="skip the M=16 / M=128 shapes")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMM would "
+              "shard by output columns with no exchange); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import skinny_gemm_nvfp4_amd as nv
+    from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+
+    nv.load_library()
+    dev = torch.device("cuda:0")
+    C = max(1, args.cold_copies)
+
+    log("generating and packing the M=1 dense layer (seeds 1-6)")
+    wl = inputs.dense_layer_m1()
+    layer = Layer(wl.gemms, C, dev)
+    bytes_per_step = sum(rl.compulsory_bytes(*s) for s in layer.shapes)
+
+    # Capture one step per cold copy in a HIP graph.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(C):
+            layer.step(c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager_Y = [y.clone() for y in layer.Y]
+    graphs = []
+    for c in range(C):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.step(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} graph-replayed steps after {args.warmup} warmup")
+    for i in range(args.warmup):
+        graphs[i % C].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % C].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = 1e3 * (t1 - t0) / args.steps
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    for y, ye in zip(layer.Y, eager_Y):
+        if not torch.equal(y, ye):
+            raise RuntimeError("graph replay differs from the eager result")
+
+    log("per-kernel event timing")
+    kus = layer.kernel_times_us(args.steps)
+    per_gemm = {n: gemm_report(s, us) for n, s, us in zip(layer.names, layer.shapes, kus)}
+    dom = max(range(len(layer.names)), key=lambda i: rl.compulsory_bytes(*layer.shapes[i]))
+    dom_bytes = rl.compulsory_bytes(*layer.shapes[dom])
+    achieved = dom_bytes / (kus[dom] * 1e-6) / 1e9
+    traffic = load_traffic(f"gemm_{layer.names[dom]}", "dense_layer_m1")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rl.HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / rl.HBM_PEAK_GBS, 4),
+            "traffic": traffic, "kernel": f"nvfp4 GEMM {layer.names[dom]} M=1 "
+            f"K={layer.shapes[dom][2]} N={layer.shapes[dom][1]}",
+            "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(kus[dom], 3)}
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        cpu, refs = cpu_baseline(wl, args.cpu_seconds)
+        worst = 0.0
+        import oracle
+        for (Yref, A), y in zip(refs, eager_Y):
+            err = np.abs(y.cpu().numpy().astype(np.float64) - Yref)
+            worst = max(worst, float((err / oracle.tolerance(A)).max()))
+        parity = {"worst_err_over_bound": round(worst, 4), "pass": worst <= 1.0}
+        if worst > 1.0:
+            raise RuntimeError(f"GPU output outside tolerance (worst ratio {worst})")
+
+    also = {}
+    if not args.no_also:
+        for wname, make in (("verify_m16", inputs.verify_m16),
+                            ("batched_verify_m128", inputs.batched_verify_m128)):
+            log(f"timing {wname}")
+            w = make()
+            lay = Layer(w.gemms, C, dev)
+            us = lay.kernel_times_us(max(20, args.steps // 4))
+            also[wname] = {n: gemm_report(s, t) for n, s, t in zip(lay.names, lay.shapes, us)}
+            del lay
+            torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dense_layer_m1", "M": 1, "K": [s[2] for s in layer.shapes],
+                   "N": [s[1] for s in layer.shapes], "gemms": layer.names, "seeds": "1-6",
+                   "weights": "nvfp4 (e2m1 codes, e4m3 scale per 16 along K, fp32 tensor scale)",
+                   "accumulate": "f32", "cold_copies": C, "bytes_per_step": bytes_per_step,
+                   "timing": "HIP-graph replay of the 4-GEMM step, host clock"},
+        "pct_hbm_peak": round(100 * value / rl.HBM_PEAK_GBS, 2),
+        "equiv_tok_s_17_9GB": round(value / EQUIV_MODEL_GB, 1),
+        "kernel_us_per_step": round(sum(kus), 3),
+        "per_gemm": per_gemm,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "also": also,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

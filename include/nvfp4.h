@@ -1,0 +1,135 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so, the MI355X (gfx950) NVFP4 skinny-GEMM library.
+ *
+ * The library computes the decode / speculative-verify hot path of a single-model LLM engine:
+ *
+ *     Y[M,N] = X[M,K] . dequant(W)[K,N]
+ *
+ * with NVFP4 weights, bf16 activations, fp32 accumulation and fp32 output. M is small: 1 for
+ * plain decode, 16 for the verify pass of one request with 15 drafted tokens, 128 when 8 requests
+ * verify together ("SparkInfer" README, sections on speculative decoding and on up to eight
+ * concurrent requests speculating together). Decode at concurrency 1 is bound by the weight
+ * stream: every weight is read once per token ("Qwen3.8-27B-NVFP4-RTX5090" model card, section
+ * "Why lm_head is NVFP4"). The weights are "NVFP4 W4A4, group size 16" stored as packed U8
+ * tensors (same model card, table "Recipe (NVIDIA ModelOpt)" and section "Serving"); this library
+ * keeps activations in bf16 (W4A16).
+ *
+ * NVFP4 as stored here
+ *   - code: FP4 E2M1 (OCP MX v1.0): sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0;
+ *     values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives.
+ *   - block scale: one FP8 E4M3 byte (OCP OFP8 "E4M3FN": bias 7, max 448, NaN = 0x7F/0xFF) per 16
+ *     consecutive k of one output column n.
+ *   - tensor scale g: one fp32 per weight matrix.
+ *   - dequantised weight: w(k,n) = e2m1(code(k,n)) * e4m3(Ws[n][k/16]) * g.
+ *
+ * Layout (all row-major, element (i,j) of an [R][C] array at offset i*C + j)
+ *   W      fp32  [K][N]     input of nvfp4_pack
+ *   Wq     uint8 [N][K/2]   byte (n, k/2) holds k even in bits 3..0 and k odd in bits 7..4
+ *   Wscale uint8 [N][K/16]  E4M3 byte of block (n, k/16)
+ *   gscale fp32  [1]        g, in device memory
+ *   X      bf16  [M][K]     passed as uint16_t bit patterns
+ *   Y      fp32  [M][N]     fully overwritten
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library keeps none of them past
+ *     the call and allocates no device memory.
+ *   - Sizes: 1 <= M, 1 <= N, 16 <= K, K % 16 == 0, and every array must have fewer than 2^62
+ *     bytes. Anything else returns NVFP4_ERROR_INVALID_VALUE.
+ *   - Alignment: X, Wq, Wscale and W must be 16-byte aligned, Y and gscale 4-byte aligned;
+ *     otherwise NVFP4_ERROR_MISALIGNED. K % 256 == 0 takes the fastest loads; any K % 16 == 0 is
+ *     correct.
+ *   - Y must not overlap any input. Outputs of nvfp4_pack must not overlap W or each other.
+ *   - Validation happens on the host before any HIP call: an error return has no side effects.
+ *   - Calls are stream-ordered on `stream` (a hipStream_t; NULL is the null stream) and never
+ *     synchronise. A failed kernel launch returns NVFP4_ERROR_LAUNCH; faults during execution
+ *     surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - Results are deterministic: the same inputs give the same bits on every call.
+ *   - Calls are re-entrant and thread-safe; the library has no mutable global state.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_SUCCESS = 0,
+    NVFP4_ERROR_INVALID_VALUE = 1,  /* bad size, null pointer or unknown path */
+    NVFP4_ERROR_MISALIGNED = 2,     /* a pointer breaks the alignment rules above */
+    NVFP4_ERROR_LAUNCH = 3          /* the HIP runtime refused a kernel launch */
+} nvfp4_status_t;
+
+/*
+ * nvfp4_pack -- quantise fp32 W[K][N] to NVFP4 (codes Wq, block scales Wscale, tensor scale).
+ *
+ * The recipe of the workloads: g = amax(|W|) / (6*448); per block of 16 consecutive k of column n,
+ * s = E4M3(block_amax / (6g)); code = E2M1(w / (s*g)). Each step is one fp32 operation rounded to
+ * nearest-even, in that order (6*g is rounded before the division; s*g before w/(s*g)); both
+ * roundings to E4M3 and E2M1 go to the nearest value, ties to the even code, saturating at 448 and
+ * at 6. A tensor with g == 0 packs to all-zero bytes; a block whose s*g is 0 gets all-zero codes.
+ * The page's checkpoint was quantised this way offline with NVIDIA ModelOpt ("Qwen3.8-27B-NVFP4-
+ * RTX5090" model card, table "Recipe (NVIDIA ModelOpt)"); here it is the untimed set-up step.
+ *
+ *   K, N    sizes of W (K % 16 == 0)
+ *   W       in:  fp32 [K][N], device
+ *   Wq      out: uint8 [N][K/2], device
+ *   Wscale  out: uint8 [N][K/16], device
+ *   gscale  out: fp32 [1], device; it also holds the running amax while the call executes
+ *   stream  hipStream_t
+ */
+nvfp4_status_t nvfp4_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Wscale,
+                          float *gscale, void *stream);
+
+/*
+ * nvfp4_gemm -- Y = X . dequant(Wq, Wscale, *gscale), fp32 accumulation, fp32 output.
+ *
+ * Each weight is decoded to the exact value e2m1(code) * e4m3(scale) (at most 6 significant bits,
+ * so exact in bf16 and fp32); products with x are accumulated in fp32 and g is applied once to
+ * each finished output. The tolerance the results meet against a double-precision sum is
+ * |Y - Y_ref| <= 2e-3 * sum_k |x*w| + 1e-6 per output. The kernel is chosen from (M, N, K): a
+ * wavefront dot product for the smallest M and bf16 MFMA tiles otherwise.
+ *
+ *   M, N, K  sizes (K % 16 == 0)
+ *   X        in:  bf16 bits [M][K], device
+ *   Wq       in:  uint8 [N][K/2], device (as written by nvfp4_pack)
+ *   Wscale   in:  uint8 [N][K/16], device
+ *   gscale   in:  fp32 [1], device (read by the kernel; the host never reads it)
+ *   Y        out: fp32 [M][N], device
+ *   stream   hipStream_t
+ */
+nvfp4_status_t nvfp4_gemm(int M, int N, int K, const uint16_t *X, const uint8_t *Wq,
+                          const uint8_t *Wscale, const float *gscale, float *Y, void *stream);
+
+/* Kernel families nvfp4_gemm chooses between (for nvfp4_gemm_path). */
+typedef enum {
+    NVFP4_PATH_AUTO = 0,  /* what nvfp4_gemm does */
+    NVFP4_PATH_DOT = 1,   /* VALU: E2M1->bf16 decode, v_dot2_f32_bf16, fp32 block partial * s */
+    NVFP4_PATH_MFMA = 2   /* E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 tiles */
+} nvfp4_path_t;
+
+/*
+ * nvfp4_gemm_path -- nvfp4_gemm with the kernel family forced, for testing and tuning.
+ *
+ * Same operation, arguments, rules and results as nvfp4_gemm. `path` is an nvfp4_path_t;
+ * NVFP4_PATH_DOT accepts M <= 8 only (else NVFP4_ERROR_INVALID_VALUE). `split` is the number of
+ * waves of one workgroup that share the K loop (1, 2, 4 or 8; 0 picks it like nvfp4_gemm).
+ */
+nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,
+                               const uint8_t *Wq, const uint8_t *Wscale, const float *gscale,
+                               float *Y, void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *nvfp4_status_string(nvfp4_status_t status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define NVFP4_ABI_VERSION 1
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -56,6 +56,8 @@ def lib():
                               ctypes.POINTER(ctypes.c_uint16), c_u8p, c_u8p, ctypes.c_float,
                               ctypes.POINTER(ctypes.c_int), ctypes.c_int, c_dp, c_dp]
     L.oracle_gemm.restype = ctypes.c_int
+    L.oracle_num_threads.argtypes = []
+    L.oracle_num_threads.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -149,6 +151,11 @@ def gemm(X_bits: np.ndarray, Wq: np.ndarray, Ws: np.ndarray, g, cols=None):
     if rc:
         raise MemoryError("oracle_gemm could not allocate its buffers")
     return Y, A
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return lib().oracle_num_threads()
 
 
 def tolerance(A: np.ndarray) -> np.ndarray:

@@ -38,6 +38,9 @@
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ------------------------------------------------------------------------------------------ */
 /* Element decoders, written from the bit-field definitions.                                   */
@@ -282,4 +285,14 @@ int oracle_gemm(int M, int N, int K, const uint16_t *X, const uint8_t *Wq, const
     }
     free(xd);
     return failed;
+}
+
+/* Number of threads the parallel loops above use (for reporting CPU timings). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -1,1 +1,13 @@
-"""MI355X-native NVFP4 skinny GEMM: Y[M,N] = X[M,K] . dequant(W)[K,N] for M = 1 .. 128."""
+"""MI355X-native NVFP4 skinny GEMM: Y[M,N] = X[M,K] . dequant(W)[K,N] for M = 1 .. 128.
+
+The computation is the weight stream of LLM decode and speculative verification with NVFP4
+weights (E2M1 codes, an E4M3 scale per 16 weights along K, an fp32 tensor scale), bf16 activations
+and fp32 accumulation. The kernels are hand-written HIP for gfx950 in ``csrc/``, behind the C ABI of
+``include/nvfp4.h`` (``libnvfp4.so``); ``binding`` marshals torch tensors into it.
+
+The library is loaded on first use; nothing here runs on the CPU in its place.
+"""
+from .binding import (  # noqa: F401
+    ERROR_INVALID_VALUE, ERROR_LAUNCH, ERROR_MISALIGNED, PATH_AUTO, PATH_DOT, PATH_MFMA, SUCCESS,
+    NVFP4Error, abi_version, gemm, library_path, load_library, nvfp4_gemm, nvfp4_gemm_path,
+    nvfp4_pack, pack, status_string)

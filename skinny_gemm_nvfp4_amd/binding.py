@@ -1,0 +1,150 @@
+"""Thin ctypes binding of libnvfp4.so (include/nvfp4.h).
+
+Argument marshalling only: every step of quantisation and of the GEMM runs in the HIP kernels.
+PyTorch supplies device memory and the current stream. There is no fallback: if the library is
+not built, or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from . import build as _build
+
+SUCCESS = 0
+ERROR_INVALID_VALUE = 1
+ERROR_MISALIGNED = 2
+ERROR_LAUNCH = 3
+
+PATH_AUTO = 0
+PATH_DOT = 1
+PATH_MFMA = 2
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree libnvfp4.so. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m skinny_gemm_nvfp4_amd.build` "
+            "(the NVFP4 GEMM has no CPU fallback)")
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    ci = ctypes.c_int
+    L.nvfp4_pack.argtypes = [ci, ci, vp, vp, vp, vp, vp]
+    L.nvfp4_pack.restype = ci
+    L.nvfp4_gemm.argtypes = [ci, ci, ci, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_gemm.restype = ci
+    L.nvfp4_gemm_path.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_gemm_path.restype = ci
+    L.nvfp4_status_string.argtypes = [ci]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_abi_version.argtypes = []
+    L.nvfp4_abi_version.restype = ci
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load_library().nvfp4_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return load_library().nvfp4_abi_version()
+
+
+# ---- raw entry points: same names and arguments as the C ABI (ints are device addresses) ----
+
+def nvfp4_pack(K: int, N: int, W: int, Wq: int, Wscale: int, gscale: int,
+               stream: Optional[int]) -> int:
+    return load_library().nvfp4_pack(K, N, W, Wq, Wscale, gscale, stream)
+
+
+def nvfp4_gemm(M: int, N: int, K: int, X: int, Wq: int, Wscale: int, gscale: int, Y: int,
+               stream: Optional[int]) -> int:
+    return load_library().nvfp4_gemm(M, N, K, X, Wq, Wscale, gscale, Y, stream)
+
+
+def nvfp4_gemm_path(path: int, split: int, M: int, N: int, K: int, X: int, Wq: int, Wscale: int,
+                    gscale: int, Y: int, stream: Optional[int]) -> int:
+    return load_library().nvfp4_gemm_path(path, split, M, N, K, X, Wq, Wscale, gscale, Y, stream)
+
+
+# ---- tensor-level helpers ----
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check_device(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pack(W: torch.Tensor, stream=None, out=None) -> Tuple[torch.Tensor, torch.Tensor,
+                                                           torch.Tensor]:
+    """Quantise fp32 W[K, N] (device) to (Wq uint8 [N, K/2], Ws uint8 [N, K/16], g fp32 [1])."""
+    K, N = W.shape
+    _check_device(W, "W", torch.float32, (K, N))
+    if out is None:
+        Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+        Ws = torch.empty((N, K // 16), dtype=torch.uint8, device=W.device)
+        g = torch.empty(1, dtype=torch.float32, device=W.device)
+    else:
+        Wq, Ws, g = out
+    st = nvfp4_pack(K, N, W.data_ptr(), Wq.data_ptr(), Ws.data_ptr(), g.data_ptr(),
+                    _stream(stream))
+    if st != SUCCESS:
+        raise NVFP4Error(st, "nvfp4_pack")
+    return Wq, Ws, g
+
+
+def gemm(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Tensor, stream=None,
+         out: Optional[torch.Tensor] = None, path: int = PATH_AUTO, split: int = 0
+         ) -> torch.Tensor:
+    """Y[M, N] = X[M, K] . dequant(Wq, Ws, g) in fp32. X is bf16 on the device."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    _check_device(X, "X", torch.bfloat16, (M, K))
+    _check_device(Wq, "Wq", torch.uint8, (N, K // 2))
+    _check_device(Ws, "Ws", torch.uint8, (N, K // 16))
+    _check_device(g, "g", torch.float32, (1,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        _check_device(out, "out", torch.float32, (M, N))
+    if path == PATH_AUTO and split == 0:
+        st = nvfp4_gemm(M, N, K, X.data_ptr(), Wq.data_ptr(), Ws.data_ptr(), g.data_ptr(),
+                        out.data_ptr(), _stream(stream))
+    else:
+        st = nvfp4_gemm_path(path, split, M, N, K, X.data_ptr(), Wq.data_ptr(), Ws.data_ptr(),
+                             g.data_ptr(), out.data_ptr(), _stream(stream))
+    if st != SUCCESS:
+        raise NVFP4Error(st, "nvfp4_gemm")
+    return out

@@ -1,0 +1,105 @@
+// api.cpp -- the extern "C" boundary of libnvfp4.so (declared in include/nvfp4.h).
+//
+// Every argument is checked on the host before the first HIP call, so an error return has no side
+// effects and needs no GPU. Then the call enqueues its kernels on the caller's stream and returns
+// without synchronising.
+#include "nvfp4.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr unsigned long long kMaxBytes = 1ULL << 62;
+
+bool aligned(const void *p, uintptr_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Sizes allowed by the ABI: 1 <= M, N; 16 <= K; K % 16 == 0; every array below 2^62 bytes.
+bool sizes_ok(long long M, long long N, long long K)
+{
+    if (M < 1 || N < 1 || K < 16 || (K % 16) != 0)
+        return false;
+    const unsigned long long m = (unsigned long long)M, n = (unsigned long long)N,
+                             k = (unsigned long long)K;
+    return m * k * 2ULL < kMaxBytes && n * k * 4ULL < kMaxBytes && m * n * 4ULL < kMaxBytes;
+}
+
+nvfp4_status_t from_hip(hipError_t e)
+{
+    return e == hipSuccess ? NVFP4_SUCCESS : NVFP4_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status_t nvfp4_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Wscale,
+                          float *gscale, void *stream)
+{
+    if (!sizes_ok(1, N, K))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!W || !Wq || !Wscale || !gscale)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4))
+        return NVFP4_ERROR_MISALIGNED;
+    return from_hip(nvfp4::launch_pack(K, N, W, Wq, Wscale, gscale,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,
+                               const uint8_t *Wq, const uint8_t *Wscale, const float *gscale,
+                               float *Y, void *stream)
+{
+    if (!sizes_ok(M, N, K))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!X || !Wq || !Wscale || !gscale || !Y)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_MFMA)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
+        !aligned(Y, 4))
+        return NVFP4_ERROR_MISALIGNED;
+    int p = path, s = split;
+    if (!nvfp4::choose_config(M, N, K, &p, &s))
+        return NVFP4_ERROR_INVALID_VALUE;
+    nvfp4::GemmArgs a;
+    a.X = X;
+    a.Wq = Wq;
+    a.Ws = Wscale;
+    a.gscale = gscale;
+    a.Y = Y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    return from_hip(nvfp4::launch_gemm(p, s, a, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_gemm(int M, int N, int K, const uint16_t *X, const uint8_t *Wq,
+                          const uint8_t *Wscale, const float *gscale, float *Y, void *stream)
+{
+    return nvfp4_gemm_path(NVFP4_PATH_AUTO, 0, M, N, K, X, Wq, Wscale, gscale, Y, stream);
+}
+
+const char *nvfp4_status_string(nvfp4_status_t status)
+{
+    switch (status) {
+    case NVFP4_SUCCESS: return "success";
+    case NVFP4_ERROR_INVALID_VALUE: return "invalid value (size, null pointer or path)";
+    case NVFP4_ERROR_MISALIGNED: return "misaligned pointer";
+    case NVFP4_ERROR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int nvfp4_abi_version(void)
+{
+    return NVFP4_ABI_VERSION;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: libnvfp4.so loads, exports every function include/nvfp4.h declares,
+and rejects bad arguments on the host before any HIP call (so these run in a CPU container).
+
+No call here reaches a kernel: every argument set is invalid by construction, and the ABI
+validates before touching the runtime.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import skinny_gemm_nvfp4_amd as nv
+from skinny_gemm_nvfp4_amd import binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+# Plausible-looking device addresses; never dereferenced because validation fails first.
+A16 = 0x7F0000000000
+A16B = 0x7F0000100000
+A16C = 0x7F0000200000
+A16D = 0x7F0000300000
+A16E = 0x7F0000400000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB):
+        build.build()
+    return binding.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) >= {"nvfp4_pack", "nvfp4_gemm", "nvfp4_gemm_path", "nvfp4_status_string",
+                          "nvfp4_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)", out))
+    for name in names:
+        assert name in exported, f"{name} declared in nvfp4.h but not exported"
+        assert hasattr(lib, name)
+
+
+def test_abi_version_and_strings(lib):
+    assert nv.abi_version() == 1
+    for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH):
+        assert nv.status_string(st)
+    assert nv.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 16, 256), (-1, 16, 256), (1, 0, 256), (1, -5, 256),
+                                   (1, 16, 0), (1, 16, 8), (1, 16, 17), (1, 16, 264 + 1),
+                                   (1, 16, -16)])
+def test_gemm_rejects_bad_sizes(lib, M, N, K):
+    st = nv.nvfp4_gemm(M, N, K, A16, A16B, A16C, A16D, A16E, None)
+    assert st == nv.ERROR_INVALID_VALUE
+
+
+def test_gemm_rejects_null_pointers(lib):
+    args = [A16, A16B, A16C, A16D, A16E]
+    for i in range(5):
+        bad = list(args)
+        bad[i] = None
+        assert nv.nvfp4_gemm(1, 16, 256, *bad, None) == nv.ERROR_INVALID_VALUE
+
+
+def test_gemm_rejects_misaligned_pointers(lib):
+    # X, Wq, Wscale need 16 bytes; gscale and Y need 4.
+    for i, off in [(0, 8), (1, 4), (2, 1), (3, 2), (4, 2)]:
+        bad = [A16, A16B, A16C, A16D, A16E]
+        bad[i] += off
+        assert nv.nvfp4_gemm(1, 16, 256, *bad, None) == nv.ERROR_MISALIGNED, i
+
+
+def test_gemm_path_rejects_bad_options(lib):
+    ptrs = [A16, A16B, A16C, A16D, A16E]
+    assert nv.nvfp4_gemm_path(3, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_gemm_path(-1, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    for split in (3, 16, -1):
+        assert nv.nvfp4_gemm_path(0, split, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    # the dot-product family covers M <= 8 only
+    assert nv.nvfp4_gemm_path(nv.PATH_DOT, 0, 9, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+
+
+def test_gemm_rejects_overflowing_sizes(lib):
+    # M * K * 2 bytes of X exceeds the documented 2^62-byte limit.
+    big = 2 ** 31 - 1
+    st = nv.nvfp4_gemm(big, big, 2 ** 31 - 16, A16, A16B, A16C, A16D, A16E, None)
+    assert st == nv.ERROR_INVALID_VALUE
+
+
+def test_pack_rejects_bad_arguments(lib):
+    ok = [A16, A16B, A16C, A16D]
+    assert nv.nvfp4_pack(8, 16, *ok, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_pack(24, 16, *ok, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_pack(256, 0, *ok, None) == nv.ERROR_INVALID_VALUE
+    for i in range(4):
+        bad = list(ok)
+        bad[i] = None
+        assert nv.nvfp4_pack(256, 16, *bad, None) == nv.ERROR_INVALID_VALUE
+    for i, off in [(0, 4), (1, 8), (2, 2), (3, 2)]:
+        bad = list(ok)
+        bad[i] += off
+        assert nv.nvfp4_pack(256, 16, *bad, None) == nv.ERROR_MISALIGNED
+
+
+def test_tensor_helpers_require_device_tensors(lib):
+    import torch
+    with pytest.raises(ValueError):
+        nv.gemm(torch.zeros(1, 32, dtype=torch.bfloat16), torch.zeros(4, 16, dtype=torch.uint8),
+                torch.zeros(4, 2, dtype=torch.uint8), torch.ones(1))
+    with pytest.raises(ValueError):
+        nv.pack(torch.zeros(32, 4))
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(build, "LIB", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(ImportError):
+        binding.load_library()

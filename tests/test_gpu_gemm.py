@@ -1,0 +1,119 @@
+"""GPU GEMM (nvfp4_gemm / nvfp4_gemm_path through the C ABI) against the oracle.
+
+Bars:
+  * floating point: |Y - Y_ref| <= 2e-3 * sum_k |x*w| + 1e-6 for every output;
+  * exact cases (integer sums, one-hot rows): bit equality.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import skinny_gemm_nvfp4_amd as nv
+from skinny_gemm_nvfp4_amd import inputs
+from parity import (FINITE_SCALES, check_close, gpu_gemm, random_case, say, to_device_packed)
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [(nv.PATH_DOT, 1), (nv.PATH_DOT, 2), (nv.PATH_DOT, 4), (nv.PATH_DOT, 8),
+         (nv.PATH_MFMA, 1), (nv.PATH_MFMA, 2), (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
+         (nv.PATH_AUTO, 0)]
+SMALL_M = [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 130]
+SMALL_N = [1, 15, 16, 17, 65]
+SMALL_K = [16, 48, 256, 272, 528, 1024]
+
+
+def _paths_for(M):
+    return [(p, s) for p, s in PATHS if not (p == nv.PATH_DOT and M > 8)]
+
+
+@pytest.mark.parametrize("path,split", PATHS)
+def test_small_shapes(device, path, split):
+    """Brute force over tiny shapes, every path and split forced, ragged N, K and M."""
+    seed = 0
+    for K in SMALL_K:
+        for M in SMALL_M:
+            if path == nv.PATH_DOT and M > 8:
+                continue
+            for N in SMALL_N:
+                seed += 1
+                X, Wq, Ws, g = random_case(seed, M, N, K, FINITE_SCALES)
+                Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
+                say(f"small path={path} split={split} M={M} N={N} K={K}")
+                Y = gpu_gemm(X, to_device_packed(Wq, Ws, g, device), device, path, split)
+                check_close(Y, Yref, A, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (4, 33, 528), (16, 48, 1024),
+                                   (128, 40, 512), (7, 16, 17408), (1, 17, 5120)])
+def test_exact_integer_sums(device, M, N, K):
+    """Scales in {0.5, 1, 2}, g = 1, X integers in [-8, 8]: every partial sum is a multiple of
+    0.25 below 2^22, exact in fp32 in any order, so Y must equal the oracle bit for bit."""
+    gen = inputs.generator(1000 + M + N + K)
+    Wq, Ws = inputs.random_packed(gen, N, K, scale_bytes=[0x30, 0x38, 0x40])
+    X = inputs.integer_activations(gen, M, K)
+    Yref, _ = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), 1.0)
+    for path, split in _paths_for(M):
+        say(f"exact path={path} split={split} M={M} N={N} K={K}")
+        Y = gpu_gemm(X, to_device_packed(Wq, Ws, 1.0, device), device, path, split)
+        assert np.array_equal(Y, Yref), f"path {path} split {split}: not bit-exact"
+
+
+@pytest.mark.parametrize("K", [32, 272, 5120])
+def test_one_hot_rows_give_dequantised_weights(device, K):
+    """x[m, k_m] = 1 and 0 elsewhere: Y[m, n] must be fp32(code * s * g) exactly, for every code
+    and every finite scale byte."""
+    N = 96
+    gen = inputs.generator(77 + K)
+    Wq, Ws = inputs.random_packed(gen, N, K, scale_bytes=FINITE_SCALES)
+    g = np.float32(0.0137)
+    Wd = oracle.dequantize(Wq.numpy(), Ws.numpy(), g)    # exact double [K][N]
+    ks = torch.randperm(K, generator=gen)[:16]
+    M = len(ks)
+    X = torch.zeros(M, K, dtype=torch.bfloat16)
+    X[torch.arange(M), ks] = 1.0
+    expect = Wd[ks.numpy(), :].astype(np.float32).astype(np.float64)
+    for path, split in _paths_for(M) + [(nv.PATH_DOT, 4)]:
+        if path == nv.PATH_DOT and M > 8:
+            Xs, ex = X[:8], expect[:8]
+        else:
+            Xs, ex = X, expect
+        say(f"one-hot path={path} split={split} K={K}")
+        Y = gpu_gemm(Xs, to_device_packed(Wq, Ws, g, device), device, path, split)
+        diff = np.argwhere(Y != ex)
+        assert diff.size == 0, f"path {path}: {len(diff)} mismatches, first {diff[:3].tolist()}"
+
+
+def test_nan_scale_propagates(device):
+    K, N, M = 64, 16, 2
+    gen = inputs.generator(5)
+    Wq, Ws = inputs.random_packed(gen, N, K, scale_bytes=[0x38])
+    Ws[3, 1] = 0x7F
+    Ws[9, 0] = 0xFF
+    X = inputs.activations(gen, M, K)
+    Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), 1.0)
+    for path, split in _paths_for(M):
+        Y = gpu_gemm(X, to_device_packed(Wq, Ws, 1.0, device), device, path, split)
+        check_close(Y, Yref, A, "nan")
+        assert np.isnan(Y[:, 3]).all() and np.isnan(Y[:, 9]).all()
+
+
+def test_negative_scale_bytes(device):
+    """The GEMM decodes every scale byte as E4M3, including ones with the sign bit set."""
+    K, N, M = 256, 40, 3
+    gen = inputs.generator(6)
+    Wq, Ws = inputs.random_packed(gen, N, K, scale_bytes=list(range(0x80, 0xFF)))
+    X = inputs.activations(gen, M, K)
+    Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), 0.5)
+    for path, split in _paths_for(M):
+        Y = gpu_gemm(X, to_device_packed(Wq, Ws, 0.5, device), device, path, split)
+        check_close(Y, Yref, A, "negative scales")
+
+
+def test_deterministic(device):
+    X, Wq, Ws, g = random_case(9, 16, 2048, 5120, FINITE_SCALES)
+    packed = to_device_packed(Wq, Ws, g, device)
+    for path, split in _paths_for(16):
+        a = gpu_gemm(X, packed, device, path, split)
+        b = gpu_gemm(X, packed, device, path, split)
+        assert np.array_equal(a, b), f"path {path} split {split} not reproducible"
