@@ -33,10 +33,10 @@
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer owned by the caller; the library keeps none of them past
  *     the call and allocates no device memory.
- *   - Sizes: 1 <= M, 1 <= N, 16 <= K, K % 16 == 0, and every array must have fewer than 2^62
- *     bytes. Anything else returns NVFP4_ERROR_INVALID_VALUE.
+ *   - Sizes: 1 <= M, 1 <= N, 16 <= K <= 4194304 (2^22), K % 16 == 0, and every array must have
+ *     fewer than 2^62 bytes. Anything else returns NVFP4_ERROR_INVALID_VALUE.
  *   - Alignment: X, Wq, Wscale and W must be 16-byte aligned, Y and gscale 4-byte aligned;
- *     otherwise NVFP4_ERROR_MISALIGNED. K % 256 == 0 takes the fastest loads; any K % 16 == 0 is
+ *     otherwise NVFP4_ERROR_MISALIGNED. K % 512 == 0 takes the fastest loads; any K % 16 == 0 is
  *     correct.
  *   - Y must not overlap any input. Outputs of nvfp4_pack must not overlap W or each other.
  *   - Validation happens on the host before any HIP call: an error return has no side effects.
@@ -105,17 +105,22 @@ nvfp4_status_t nvfp4_gemm(int M, int N, int K, const uint16_t *X, const uint8_t 
 
 /* Kernel families nvfp4_gemm chooses between (for nvfp4_gemm_path). */
 typedef enum {
-    NVFP4_PATH_AUTO = 0,  /* what nvfp4_gemm does */
-    NVFP4_PATH_DOT = 1,   /* VALU: E2M1->bf16 decode, v_dot2_f32_bf16, fp32 block partial * s */
-    NVFP4_PATH_MFMA = 2   /* E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 tiles */
+    NVFP4_PATH_AUTO = 0,   /* what nvfp4_gemm does */
+    NVFP4_PATH_DOT = 1,    /* VALU, tiled: E2M1->bf16 decode, v_dot2_f32_bf16, fp32 partial * s */
+    NVFP4_PATH_MFMA = 2,   /* E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 tiles */
+    NVFP4_PATH_STREAM = 3  /* VALU, persistent: one workgroup per compute unit, X in LDS */
 } nvfp4_path_t;
 
 /*
  * nvfp4_gemm_path -- nvfp4_gemm with the kernel family forced, for testing and tuning.
  *
- * Same operation, arguments, rules and results as nvfp4_gemm. `path` is an nvfp4_path_t;
- * NVFP4_PATH_DOT accepts M <= 8 only (else NVFP4_ERROR_INVALID_VALUE). `split` is the number of
- * waves of one workgroup that share the K loop (1, 2, 4 or 8; 0 picks it like nvfp4_gemm).
+ * Same operation, arguments, rules and results as nvfp4_gemm. `path` is an nvfp4_path_t.
+ * NVFP4_PATH_DOT and NVFP4_PATH_STREAM accept M <= 8 only (else NVFP4_ERROR_INVALID_VALUE).
+ * `split` (0 picks it like nvfp4_gemm):
+ *   NVFP4_PATH_DOT, NVFP4_PATH_MFMA: waves of one workgroup that share the K loop: 1, 2, 4 or 8;
+ *   NVFP4_PATH_STREAM: waves of the one workgroup per compute unit: 4, 8 or 16. If X does not
+ *   fit in LDS (M * K too large) the call runs NVFP4_PATH_DOT with its own split instead.
+ * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
 nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,
                                const uint8_t *Wq, const uint8_t *Wscale, const float *gscale,

@@ -18,10 +18,11 @@ bool aligned(const void *p, uintptr_t a)
     return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
-// Sizes allowed by the ABI: 1 <= M, N; 16 <= K; K % 16 == 0; every array below 2^62 bytes.
+// Sizes allowed by the ABI: 1 <= M, N; 16 <= K <= 2^22; K % 16 == 0; every array below 2^62
+// bytes.
 bool sizes_ok(long long M, long long N, long long K)
 {
-    if (M < 1 || N < 1 || K < 16 || (K % 16) != 0)
+    if (M < 1 || N < 1 || K < 16 || K > nvfp4::kMaxK || (K % 16) != 0)
         return false;
     const unsigned long long m = (unsigned long long)M, n = (unsigned long long)N,
                              k = (unsigned long long)K;
@@ -58,9 +59,9 @@ nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const u
         return NVFP4_ERROR_INVALID_VALUE;
     if (!X || !Wq || !Wscale || !gscale || !Y)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_MFMA)
+    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_STREAM)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8)
+    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 16)
         return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
         !aligned(Y, 4))

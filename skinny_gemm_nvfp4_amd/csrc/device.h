@@ -8,6 +8,10 @@
 //     (bias 7, max 448, NaN at 0x7F/0xFF), the block-scale format of NVFP4 ("Qwen3.8-27B-NVFP4-
 //     RTX5090" model card, table "Recipe (NVIDIA ModelOpt)": NVFP4, group size 16).
 //   * e2m1 * s has at most 2 + 4 significant bits, so it is exact in fp32 and in bf16.
+//
+// Memory helpers: packed weights are read exactly once per call, so their loads carry the
+// non-temporal hint and do not displace the activations, which every workgroup re-reads, from
+// the caches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,9 +27,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;          // lanes per wavefront on CDNA
-constexpr int kTileN = 16;         // output columns n per workgroup tile
-constexpr int kStepK = 256;        // k covered by one wave in one step (4 lane groups x 2 chunks x 32)
-constexpr int kChunkK = 32;        // k per chunk: 16 bytes of codes, two 16-element blocks
 
 // E4M3 byte SEL of w, decoded to fp32.
 template <int SEL>
@@ -67,6 +68,18 @@ __device__ __forceinline__ bf16x8_t decode8_scaled(uint32_t w, float s)
     return r;
 }
 
+// Four words of 8 codes -> 16 bf16 pairs; pair 4 d + b holds k = 8 d + 2 b and 8 d + 2 b + 1.
+__device__ __forceinline__ void decode32_bf16(const uint32_t code[4], bf16x2_t w[16])
+{
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        w[4 * d + 0] = e2m1x2_to_bf16<0>(code[d]);
+        w[4 * d + 1] = e2m1x2_to_bf16<1>(code[d]);
+        w[4 * d + 2] = e2m1x2_to_bf16<2>(code[d]);
+        w[4 * d + 3] = e2m1x2_to_bf16<3>(code[d]);
+    }
+}
+
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u)
 {
     return __builtin_bit_cast(bf16x2_t, u);
@@ -77,58 +90,114 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u)
     return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// ------------------------------------------------------------------------------------------
+// Loads through raw buffer descriptors. A descriptor covers one workgroup's rows of an array
+// (base pointer and byte count); a load whose offset is at or past the count returns zeros
+// without touching memory. Ragged rows, ragged K and the prefetch past a wave's last window are
+// all expressed that way, so the K loops carry no branches and no exec-masked loads, and the
+// loads retire in the order they were issued.
+// ------------------------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kRawBufferFlags = 0x00020000;     // word 3 of an unformatted gfx9 descriptor
+constexpr int kAuxStream = 2;                    // "nt": read-once data
+constexpr int kAuxNormal = 0;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // beyond every byte count used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRawBufferFlags);
+}
+
+__device__ __forceinline__ uint32_t off_if(bool valid, uint32_t off)
+{
+    return valid ? off : kOutOfRange;
+}
+
 // One chunk of one output column: 32 consecutive k, i.e. 16 code bytes and 2 scale bytes.
 struct Chunk {
     uint32_t code[4];   // code[d] holds k = 8d .. 8d+7 of the chunk
     uint32_t scale;     // byte 0: block of k 0..15, byte 1: block of k 16..31
 };
 
-// Loads the chunk of row (wq_row, ws_row) that starts at k = kc (a multiple of 32).
-// NARROW is for K % 32 == 16, where rows are only 8-byte aligned and the last chunk of a row may
-// hold a single block. Blocks at or beyond K read as code 0 with scale byte 0.
+// Loads the chunk that starts at k = kc (a multiple of 32) of a row whose codes start at byte
+// qrow of rq and whose scales start at byte srow of rs. Blocks at or beyond K read as code 0
+// with scale byte 0, which add exactly zero.
+// Wide layout (K % 64 == 0): one 16-byte code load and the aligned 4-byte word that holds the
+// chunk's two scale bytes; rows are 4-byte aligned, so that word never leaves the row.
+// NARROW (any other K % 16 == 0): two 8-byte code loads and two 1-byte scale loads; code rows
+// are 8-byte aligned and the last chunk of a row may hold a single block.
 template <bool NARROW>
-__device__ __forceinline__ Chunk load_chunk(const uint8_t *wq_row, const uint8_t *ws_row, int kc,
-                                            int K, bool row_ok)
+__device__ __forceinline__ Chunk load_chunk(rsrc_t rq, rsrc_t rs, uint32_t qrow, uint32_t srow,
+                                            int kc, int K)
 {
     Chunk c;
-    c.code[0] = c.code[1] = c.code[2] = c.code[3] = 0u;
-    c.scale = 0u;
-    if (!row_ok)
-        return c;
     if (!NARROW) {
-        if (kc < K) {  // K % 32 == 0: the chunk is either whole or absent
-            u32x4_t v = *reinterpret_cast<const u32x4_t *>(wq_row + kc / 2);
-            c.code[0] = v[0];
-            c.code[1] = v[1];
-            c.code[2] = v[2];
-            c.code[3] = v[3];
-            c.scale = *reinterpret_cast<const uint16_t *>(ws_row + kc / 16);
-        }
+        const bool v = kc < K;  // K % 64 == 0: the chunk is either whole or absent
+        const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(
+            rq, off_if(v, qrow + (uint32_t)kc / 2), 0, kAuxStream);
+        c.code[0] = q[0];
+        c.code[1] = q[1];
+        c.code[2] = q[2];
+        c.code[3] = q[3];
+        // The 4-byte word holding this chunk's two scale bytes (and the neighbouring chunk's);
+        // scale_pair() picks the right half once the data is there. A 2-byte load would need a
+        // zero-extension right after it, which stalls on the load.
+        c.scale = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, off_if(v, (srow + (uint32_t)kc / 16) & ~3u), 0, kAuxStream);
     } else {
-        if (kc < K) {
-            u32x2_t v = *reinterpret_cast<const u32x2_t *>(wq_row + kc / 2);
-            c.code[0] = v[0];
-            c.code[1] = v[1];
-            c.scale = ws_row[kc / 16];
-        }
-        if (kc + 16 < K) {
-            u32x2_t v = *reinterpret_cast<const u32x2_t *>(wq_row + kc / 2 + 8);
-            c.code[2] = v[0];
-            c.code[3] = v[1];
-            c.scale |= (uint32_t)ws_row[kc / 16 + 1] << 8;
-        }
+        const bool v0 = kc < K, v1 = kc + 16 < K;
+        const u32x2_t q0 = __builtin_amdgcn_raw_buffer_load_b64(
+            rq, off_if(v0, qrow + (uint32_t)kc / 2), 0, kAuxStream);
+        const u32x2_t q1 = __builtin_amdgcn_raw_buffer_load_b64(
+            rq, off_if(v1, qrow + (uint32_t)kc / 2 + 8), 0, kAuxStream);
+        c.code[0] = q0[0];
+        c.code[1] = q0[1];
+        c.code[2] = q1[0];
+        c.code[3] = q1[1];
+        const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(
+            rs, off_if(v0, srow + (uint32_t)kc / 16), 0, kAuxStream);
+        const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(
+            rs, off_if(v1, srow + (uint32_t)kc / 16 + 1), 0, kAuxStream);
+        c.scale = b0 | (b1 << 8);
     }
     return c;
 }
 
-// Eight bf16 of X row m at k .. k+7 (16 bytes), or zeros if the row or the k range is outside.
-// K % 16 == 0 and k % 8 == 0, so k < K implies k + 8 <= K.
-__device__ __forceinline__ u32x4_t load_x8(const uint16_t *X, int m, int M, int k, int K)
+// The two scale bytes of a chunk loaded by load_chunk, in bits 0..15. In the wide layout the
+// byte offset srow + kc / 16 is even (K / 16 and kc / 16 are even and the descriptor base is
+// 4-byte aligned, see scale_rsrc), so the pair is the low or the high half of the loaded word.
+template <bool NARROW>
+__device__ __forceinline__ uint32_t scale_pair(uint32_t word, uint32_t srow, int kc)
 {
-    if (m < M && k < K)
-        return *reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k);
-    u32x4_t z = {0u, 0u, 0u, 0u};
-    return z;
+    if (NARROW)
+        return word;
+    return word >> (((srow + (uint32_t)kc / 16) & 2u) * 8u);
+}
+
+// Descriptor over rows [first, first + rows) of the scale array Ws[.][K/16]. Its base is rounded
+// down to 4 bytes (Ws itself is 16-byte aligned, so the base stays inside Ws) and *bias is the
+// byte offset of the first row from that base; a row's scales start at *bias + row * (K / 16).
+__device__ __forceinline__ rsrc_t scale_rsrc(const uint8_t *Ws, size_t first, int rows, int K,
+                                             uint32_t *bias)
+{
+    const size_t start = first * (size_t)(K / 16);
+    *bias = (uint32_t)(start & 3u);
+    return make_rsrc(Ws + (start - *bias), (uint32_t)rows * (uint32_t)(K / 16) + *bias);
+}
+
+// Eight bf16 of X (16 bytes) at byte offset off of rx, or zeros if k is at or beyond K.
+// K % 16 == 0 and k % 8 == 0, so k < K implies k + 8 <= K.
+__device__ __forceinline__ u32x4_t load_x8(rsrc_t rx, uint32_t off, int k, int K)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(rx, off_if(k < K, off), 0, kAuxNormal);
+}
+
+// A value the compiler may keep in a scalar register (it is the same in every lane).
+__device__ __forceinline__ int uniform(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
 }
 
 }  // namespace nvfp4

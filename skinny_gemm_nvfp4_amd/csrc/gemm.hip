@@ -1,219 +1,86 @@
-// gemm.hip -- NVFP4 skinny GEMM kernels for gfx950: Y[M,N] = X[M,K] . dequant(W)[K,N].
+// gemm.hip -- kernel selection and launch for the NVFP4 skinny GEMM Y[M,N] = X[M,K] . dequant(W)[K,N].
 //
-// The operation is the per-token weight stream of decode and of speculative verification: every
-// NVFP4 weight is read once per forward ("Qwen3.8-27B-NVFP4-RTX5090" model card, section "Why
-// lm_head is NVFP4"), with M = 1 for plain decode and M = 16 or 128 when drafted tokens of one or
-// eight requests are verified together ("SparkInfer" README, speculative decoding sections).
-//
-// Work split, shared by both kernel families
-//   * A workgroup owns kTileN = 16 consecutive output columns n0 .. n0+15 and W wavefronts.
-//   * In every wave, lane l = 16 g + r (r = 0..15, g = 0..3) works on column n0 + r.
-//   * K is cut into steps of 256; wave w takes steps w, w+W, w+2W, ...
-//   * In the step at k0, lane group g reads two chunks of 32 k (16 code bytes + 2 scale bytes):
-//     chunk 0 at k0 + 32 g and chunk 1 at k0 + 128 + 32 g. For one column the four lanes read
-//     64 contiguous bytes per load instruction, and a wave covers 16 columns x 256 k per step.
-//   * The W partial results of a workgroup are summed through LDS in wave order, then multiplied
-//     by the tensor scale g once and stored. Every sum has a fixed order, so results are
-//     bit-reproducible.
-//
-// DOT family (M <= 8): E2M1 -> bf16 through the gfx950 converter, v_dot2_f32_bf16 against the
-// matching bf16 pairs of X, one fp32 partial per 16-element block times its E4M3 scale.
-// MFMA family (any M): each 8-code dword becomes the bf16 B operand e2m1 * s (exact) of
-// v_mfma_f32_16x16x32_bf16; lane group g supplies MFMA k-slots 8g..8g+7, which map to the
-// physical k of its own chunk, and the A operand (X) is read with the same mapping.
-#include "device.h"
+// Three kernel families (headers in this directory):
+//   * gemv_stream.h (NVFP4_PATH_STREAM): persistent dot-product kernel, one workgroup per compute
+//     unit with an equal share of the columns, X staged in LDS. Decode (M = 1) and the smallest M.
+//   * gemv.h (NVFP4_PATH_DOT): tiled dot-product kernel, one workgroup per 4 C columns. Used
+//     when X does not fit in LDS for the persistent kernel.
+//   * mfma.h (NVFP4_PATH_MFMA): bf16 matrix-core kernel for M >= 16 (speculative verification).
+#include <algorithm>
+#include <atomic>
+
+#include "gemv.h"
+#include "gemv_stream.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace nvfp4 {
 
-// Four words of 8 codes -> 16 bf16 pairs, pair index 4 d + b covers k = 8 d + 2 b, +1.
-__device__ __forceinline__ void decode_chunk_bf16(const Chunk &c, bf16x2_t w[16])
-{
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-        w[4 * d + 0] = e2m1x2_to_bf16<0>(c.code[d]);
-        w[4 * d + 1] = e2m1x2_to_bf16<1>(c.code[d]);
-        w[4 * d + 2] = e2m1x2_to_bf16<2>(c.code[d]);
-        w[4 * d + 3] = e2m1x2_to_bf16<3>(c.code[d]);
-    }
-}
+namespace {
 
-template <int MR, int W, bool NARROW>
-__global__ __launch_bounds__(kWave *W) void gemm_dot_kernel(GemmArgs a)
-{
-    __shared__ float red[W][MR][kTileN];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const int K = a.K;
-    const int n0 = blockIdx.x * kTileN;
-    const int n = n0 + r;
-    const bool row_ok = n < a.N;
-    const uint8_t *wq_row = a.Wq + (size_t)(row_ok ? n : 0) * (size_t)(K / 2);
-    const uint8_t *ws_row = a.Ws + (size_t)(row_ok ? n : 0) * (size_t)(K / 16);
-
-    float acc[MR];
-#pragma unroll
-    for (int m = 0; m < MR; m++)
-        acc[m] = 0.0f;
-
-    const int nsteps = (K + kStepK - 1) / kStepK;
-    for (int s = wave; s < nsteps; s += W) {
-        const int k0 = s * kStepK;
-#pragma unroll
-        for (int c = 0; c < 2; c++) {
-            const int kc = k0 + 128 * c + 32 * g;
-            const Chunk ch = load_chunk<NARROW>(wq_row, ws_row, kc, K, row_ok);
-            const float s0 = e4m3_to_f32<0>(ch.scale);
-            const float s1 = e4m3_to_f32<1>(ch.scale);
-            bf16x2_t w[16];
-            decode_chunk_bf16(ch, w);
-#pragma unroll
-            for (int m = 0; m < MR; m++) {
-                u32x4_t xv[4];
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-                    xv[q] = load_x8(a.X, m, a.M, kc + 8 * q, K);
-                float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; i++)
-                    p0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(xv[i / 4][i % 4]), p0,
-                                                          false);
-#pragma unroll
-                for (int i = 8; i < 16; i++)
-                    p1 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(xv[i / 4][i % 4]), p1,
-                                                          false);
-                acc[m] = acc[m] + p0 * s0;
-                acc[m] = acc[m] + p1 * s1;
-            }
-        }
-    }
-
-    // Sum the four lane groups of each column, then the W waves, in a fixed order.
-#pragma unroll
-    for (int m = 0; m < MR; m++) {
-        float v = acc[m];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (g == 0)
-            red[wave][m][r] = v;
-    }
-    __syncthreads();
-    const float gs = *a.gscale;
-    for (int idx = threadIdx.x; idx < MR * kTileN; idx += kWave * W) {
-        const int m = idx / kTileN;
-        const int rr = idx % kTileN;
-        if (m < a.M && n0 + rr < a.N) {
-            float sum = red[0][m][rr];
-#pragma unroll
-            for (int w = 1; w < W; w++)
-                sum += red[w][m][rr];
-            a.Y[(size_t)m * a.N + n0 + rr] = sum * gs;
-        }
-    }
-}
-
-template <int MT, int W, bool NARROW>
-__global__ __launch_bounds__(kWave *W) void gemm_mfma_kernel(GemmArgs a)
-{
-    __shared__ float red[W][kTileN][kTileN];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const int K = a.K;
-    const int n0 = blockIdx.x * kTileN;
-    const int n = n0 + r;
-    const bool row_ok = n < a.N;
-    const int m_base = blockIdx.y * 16 * MT;
-    const uint8_t *wq_row = a.Wq + (size_t)(row_ok ? n : 0) * (size_t)(K / 2);
-    const uint8_t *ws_row = a.Ws + (size_t)(row_ok ? n : 0) * (size_t)(K / 16);
-
-    f32x4_t acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; t++)
-        acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int nsteps = (K + kStepK - 1) / kStepK;
-    for (int s = wave; s < nsteps; s += W) {
-        const int k0 = s * kStepK;
-#pragma unroll
-        for (int c = 0; c < 2; c++) {
-            const int kc = k0 + 128 * c + 32 * g;
-            const Chunk ch = load_chunk<NARROW>(wq_row, ws_row, kc, K, row_ok);
-            const float s0 = e4m3_to_f32<0>(ch.scale);
-            const float s1 = e4m3_to_f32<1>(ch.scale);
-#pragma unroll
-            for (int d = 0; d < 4; d++) {
-                const bf16x8_t b = decode8_scaled(ch.code[d], d < 2 ? s0 : s1);
-#pragma unroll
-                for (int t = 0; t < MT; t++) {
-                    const bf16x8_t x =
-                        as_bf16x8(load_x8(a.X, m_base + 16 * t + r, a.M, kc + 8 * d, K));
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, b, acc[t], 0, 0, 0);
-                }
-            }
-        }
-    }
-
-    // acc[t][i] is Y[m_base + 16 t + 4 g + i][n0 + r]. Sum the W waves in order, tile by tile.
-    const float gs = *a.gscale;
-    if (W == 1) {
-#pragma unroll
-        for (int t = 0; t < MT; t++) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int m = m_base + 16 * t + 4 * g + i;
-                if (m < a.M && row_ok)
-                    a.Y[(size_t)m * a.N + n] = acc[t][i] * gs;
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int t = 0; t < MT; t++) {
-        __syncthreads();  // the previous tile's readers are done with red
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            red[wave][4 * g + i][r] = acc[t][i];
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < kTileN * kTileN; idx += kWave * W) {
-            const int row = idx / kTileN;
-            const int col = idx % kTileN;
-            const int m = m_base + 16 * t + row;
-            if (m < a.M && n0 + col < a.N) {
-                float sum = red[0][row][col];
-#pragma unroll
-                for (int w = 1; w < W; w++)
-                    sum += red[w][row][col];
-                a.Y[(size_t)m * a.N + n0 + col] = sum * gs;
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------------------
-// Launch tables.
-// ------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(GemmArgs);
+typedef void (*StreamFn)(GemmArgs, StreamLayout);
 
-#define NVFP4_SPLITS(KERN, R, NARROW) \
-    { &KERN<R, 1, NARROW>, &KERN<R, 2, NARROW>, &KERN<R, 4, NARROW>, &KERN<R, 8, NARROW> }
-#define NVFP4_TABLE(KERN, NARROW)                                                              \
-    {                                                                                          \
-        NVFP4_SPLITS(KERN, 1, NARROW), NVFP4_SPLITS(KERN, 2, NARROW),                          \
-            NVFP4_SPLITS(KERN, 3, NARROW), NVFP4_SPLITS(KERN, 4, NARROW),                      \
-            NVFP4_SPLITS(KERN, 5, NARROW), NVFP4_SPLITS(KERN, 6, NARROW),                      \
-            NVFP4_SPLITS(KERN, 7, NARROW), NVFP4_SPLITS(KERN, 8, NARROW)                       \
+constexpr int kStreamDepth = 4;             // units in flight per wavefront
+constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
+constexpr int kDefaultLds = 64 * 1024;      // above this a kernel must opt in
+
+// ---- tiled dot-product kernels: [MR - 1][split index], C columns per quad ----
+#define NVFP4_DOT_SPLITS(R, C, NARROW)                                                     \
+    {                                                                                      \
+        &gemv_kernel<R, C, 1, NARROW>, &gemv_kernel<R, C, 2, NARROW>,                      \
+            &gemv_kernel<R, C, 4, NARROW>, &gemv_kernel<R, C, 8, NARROW>                   \
     }
+#define NVFP4_DOT_TABLE(NARROW)                                                            \
+    {                                                                                      \
+        NVFP4_DOT_SPLITS(1, 4, NARROW), NVFP4_DOT_SPLITS(2, 2, NARROW),                    \
+            NVFP4_DOT_SPLITS(3, 2, NARROW), NVFP4_DOT_SPLITS(4, 2, NARROW),                \
+            NVFP4_DOT_SPLITS(5, 1, NARROW), NVFP4_DOT_SPLITS(6, 1, NARROW),                \
+            NVFP4_DOT_SPLITS(7, 1, NARROW), NVFP4_DOT_SPLITS(8, 1, NARROW)                 \
+    }
+const KernelFn kDotWide[8][4] = NVFP4_DOT_TABLE(false);
+const KernelFn kDotNarrow[8][4] = NVFP4_DOT_TABLE(true);
+const int kDotColumns[8] = {4, 2, 2, 2, 1, 1, 1, 1};  // C of each MR
 
-static const KernelFn kDotWide[8][4] = NVFP4_TABLE(gemm_dot_kernel, false);
-static const KernelFn kDotNarrow[8][4] = NVFP4_TABLE(gemm_dot_kernel, true);
-static const KernelFn kMfmaWide[8][4] = NVFP4_TABLE(gemm_mfma_kernel, false);
-static const KernelFn kMfmaNarrow[8][4] = NVFP4_TABLE(gemm_mfma_kernel, true);
+// ---- persistent dot-product kernels: [variant][MR - 1][wave index] ----
+// variant 0: K % 512 == 0 (FAST); 1: K % 64 == 0; 2: any other K % 16 == 0 (NARROW).
+#define NVFP4_STREAM_WAVES(R, FAST, NARROW)                                                \
+    {                                                                                      \
+        &gemv_stream_kernel<R, 4, kStreamDepth, FAST, NARROW>,                             \
+            &gemv_stream_kernel<R, 8, kStreamDepth, FAST, NARROW>,                         \
+            &gemv_stream_kernel<R, 16, kStreamDepth, FAST, NARROW>                         \
+    }
+#define NVFP4_STREAM_TABLE(FAST, NARROW)                                                   \
+    {                                                                                      \
+        NVFP4_STREAM_WAVES(1, FAST, NARROW), NVFP4_STREAM_WAVES(2, FAST, NARROW),          \
+            NVFP4_STREAM_WAVES(3, FAST, NARROW), NVFP4_STREAM_WAVES(4, FAST, NARROW),      \
+            NVFP4_STREAM_WAVES(5, FAST, NARROW), NVFP4_STREAM_WAVES(6, FAST, NARROW),      \
+            NVFP4_STREAM_WAVES(7, FAST, NARROW), NVFP4_STREAM_WAVES(8, FAST, NARROW)       \
+    }
+const StreamFn kStream[3][8][3] = {NVFP4_STREAM_TABLE(true, false),
+                                   NVFP4_STREAM_TABLE(false, false),
+                                   NVFP4_STREAM_TABLE(false, true)};
+constexpr int kMaxDevices = 64;
+std::atomic<bool> g_stream_lds_ready[kMaxDevices][3][8][3];
 
-static int split_index(int split)
+// ---- MFMA kernels: [MT - 1][split index], NT column tiles ----
+#define NVFP4_MFMA_SPLITS(T, NT, NARROW)                                                   \
+    {                                                                                      \
+        &mfma_kernel<T, NT, 1, NARROW>, &mfma_kernel<T, NT, 2, NARROW>,                    \
+            &mfma_kernel<T, NT, 4, NARROW>, &mfma_kernel<T, NT, 8, NARROW>                 \
+    }
+#define NVFP4_MFMA_TABLE(NARROW)                                                           \
+    {                                                                                      \
+        NVFP4_MFMA_SPLITS(1, 2, NARROW), NVFP4_MFMA_SPLITS(2, 2, NARROW),                  \
+            NVFP4_MFMA_SPLITS(3, 1, NARROW), NVFP4_MFMA_SPLITS(4, 1, NARROW),              \
+            NVFP4_MFMA_SPLITS(5, 1, NARROW), NVFP4_MFMA_SPLITS(6, 1, NARROW),              \
+            NVFP4_MFMA_SPLITS(7, 1, NARROW), NVFP4_MFMA_SPLITS(8, 1, NARROW)               \
+    }
+const KernelFn kMfmaWide[8][4] = NVFP4_MFMA_TABLE(false);
+const KernelFn kMfmaNarrow[8][4] = NVFP4_MFMA_TABLE(true);
+const int kMfmaColumnTiles[8] = {2, 2, 1, 1, 1, 1, 1, 1};  // NT of each MT
+
+int split_index(int split)
 {
     switch (split) {
     case 1: return 0;
@@ -224,21 +91,105 @@ static int split_index(int split)
     }
 }
 
+int wave_index(int waves)
+{
+    switch (waves) {
+    case 4: return 0;
+    case 8: return 1;
+    case 16: return 2;
+    default: return -1;
+    }
+}
+
+// Compute units of the current device, read once per device.
+int compute_units()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 256;
+    if (dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0)
+            return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// Workgroups and LDS layout of the persistent kernel; false if X does not fit in LDS.
+bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L)
+{
+    const int G = std::max(1, std::min(compute_units(), (N + 3) / 4));
+    L->nwin = (K + kStreamWindow - 1) / kStreamWindow;
+    L->row_bytes = L->nwin * (kStreamWindow / 32) * kStreamSlot;
+    const long long x_bytes = (long long)M * L->row_bytes;
+    const int cmax = (N + G - 1) / G;
+    L->ngroups = (cmax + 3) / 4;
+    // A group of nwin consecutive units touches every wavefront whose run starts inside it.
+    L->slots = 1;
+    const int sizes[2] = {N / G, cmax};
+    for (int i = 0; i < 2; i++) {
+        const long long units = (long long)((sizes[i] + 3) / 4) * L->nwin;
+        if (units == 0)
+            continue;
+        for (long long first = 0; first < units; first += L->nwin) {
+            const int n = stream_owner(first + L->nwin - 1, W, units) -
+                          stream_owner(first, W, units) + 1;
+            L->slots = std::max(L->slots, n);
+        }
+    }
+    const long long part_bytes = (long long)L->ngroups * L->slots * MR * 4 * 4;
+    if (x_bytes + part_bytes > kMaxLds)
+        return false;
+    if ((long long)cmax * (K / 2) >= (1LL << 31))  // a workgroup's byte range must fit a buffer
+        return false;
+    L->x_bytes = (int)x_bytes;
+    L->part_bytes = (int)part_bytes;
+    *grid = G;
+    return true;
+}
+
+}  // namespace
+
 bool choose_config(int M, int N, int K, int *path, int *split)
 {
     if (*path == kPathAuto)
-        *path = (M <= 4) ? kPathDot : kPathMfma;
+        *path = (M <= 4) ? kPathStream : kPathMfma;
+    if (*path == kPathStream) {
+        if (M > kDotMaxM)
+            return false;
+        if (*split == 0)
+            *split = 16;
+        StreamLayout L;
+        int grid;
+        if (wave_index(*split) < 0)
+            return false;
+        if (stream_plan(M, N, K, M, *split, &grid, &L))
+            return true;
+        *path = kPathDot;  // X does not fit in LDS: tiled kernel
+        *split = 0;
+    }
     if (*path == kPathDot && M > kDotMaxM)
         return false;
     if (*path != kPathDot && *path != kPathMfma)
         return false;
     if (*split == 0) {
-        // Enough waves to keep every CU streaming: aim for >= 2048 waves (8 per CU), with at
-        // least two K steps per wave.
-        const long long tiles = (N + kTileN - 1) / kTileN;
-        const int steps = (K + kStepK - 1) / kStepK;
+        // Enough waves to keep every compute unit streaming: aim for >= 2048 waves (8 per CU),
+        // with at least two K windows per wave.
+        const bool dot = *path == kPathDot;
+        const int mt = M >= 128 ? 8 : (M + 15) / 16;
+        const int cols = dot ? 4 * kDotColumns[M - 1] : 16 * kMfmaColumnTiles[mt - 1];
+        const long long tiles = (N + cols - 1) / cols;
+        const int window = dot ? kGemvWindow : kMfmaWindow;
+        const int steps = (K + window - 1) / window;
         int w = 1;
-        while (w < 8 && tiles * w < 2048 && steps >= 4 * w)
+        while (w < 8 && tiles * w < 2048 && steps >= 2 * w)
             w *= 2;
         *split = w;
     }
@@ -247,22 +198,52 @@ bool choose_config(int M, int N, int K, int *path, int *split)
 
 hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t stream)
 {
-    const bool narrow = (a.K % 32) != 0;
+    (void)hipGetLastError();  // start from a clean error state
+    if (path == kPathStream) {
+        StreamLayout L;
+        int grid = 0;
+        if (!stream_plan(a.M, a.N, a.K, a.M, split, &grid, &L))
+            return hipErrorInvalidValue;
+        const int variant = (a.K % kStreamWindow == 0) ? 0 : (a.K % 64 == 0 ? 1 : 2);
+        const int wi = wave_index(split);
+        const StreamFn fn = kStream[variant][a.M - 1][wi];
+        const int lds = L.x_bytes + L.part_bytes;
+        if (lds > kDefaultLds) {
+            // Opt in to more than 64 KB of LDS, once per kernel and device.
+            int dev = 0;
+            (void)hipGetDevice(&dev);
+            std::atomic<bool> *ready =
+                (dev >= 0 && dev < kMaxDevices) ? &g_stream_lds_ready[dev][variant][a.M - 1][wi]
+                                                : nullptr;
+            if (!ready || !ready->load()) {
+                const hipError_t e = hipFuncSetAttribute(
+                    reinterpret_cast<const void *>(fn),
+                    hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+                if (e != hipSuccess)
+                    return e;
+                if (ready)
+                    ready->store(true);
+            }
+        }
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * split), lds, stream, a, L);
+        return hipGetLastError();
+    }
+    const bool narrow = (a.K % 64) != 0;
     const int si = split_index(split);
     const dim3 block(kWave * split);
-    const unsigned tiles = (unsigned)((a.N + kTileN - 1) / kTileN);
     KernelFn fn;
     dim3 grid;
     if (path == kPathDot) {
+        const int cols = 4 * kDotColumns[a.M - 1];
         fn = (narrow ? kDotNarrow : kDotWide)[a.M - 1][si];
-        grid = dim3(tiles, 1, 1);
+        grid = dim3((unsigned)((a.N + cols - 1) / cols), 1, 1);
     } else {
         const int mt = a.M >= 128 ? 8 : (a.M + 15) / 16;
+        const int cols = 16 * kMfmaColumnTiles[mt - 1];
         const unsigned mchunks = (unsigned)((a.M + 16 * mt - 1) / (16 * mt));
         fn = (narrow ? kMfmaNarrow : kMfmaWide)[mt - 1][si];
-        grid = dim3(tiles, mchunks, 1);
+        grid = dim3((unsigned)((a.N + cols - 1) / cols), mchunks, 1);
     }
-    (void)hipGetLastError();  // start from a clean error state
     hipLaunchKernelGGL(fn, grid, block, 0, stream, a);
     return hipGetLastError();
 }

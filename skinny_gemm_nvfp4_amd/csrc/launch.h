@@ -15,12 +15,16 @@ struct GemmArgs {
     int M, N, K;
 };
 
-enum Path { kPathAuto = 0, kPathDot = 1, kPathMfma = 2 };
+enum Path { kPathAuto = 0, kPathDot = 1, kPathMfma = 2, kPathStream = 3 };
 
-// Largest M the dot-product kernel family is instantiated for.
+// Largest M the dot-product kernel families are instantiated for.
 constexpr int kDotMaxM = 8;
 
+// Largest K: keeps every per-workgroup byte range of the buffer loads below 2^31.
+constexpr int kMaxK = 1 << 22;
+
 // Resolves path/split (0 = automatic) for this shape. Returns false for an unsupported pair.
+// A persistent (stream) request whose X does not fit in LDS becomes the tiled dot-product path.
 bool choose_config(int M, int N, int K, int *path, int *split);
 
 // Launch the GEMM with a resolved path and split. Returns the hipError_t of the launch.

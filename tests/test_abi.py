@@ -59,7 +59,7 @@ def test_abi_version_and_strings(lib):
 
 @pytest.mark.parametrize("M,N,K", [(0, 16, 256), (-1, 16, 256), (1, 0, 256), (1, -5, 256),
                                    (1, 16, 0), (1, 16, 8), (1, 16, 17), (1, 16, 264 + 1),
-                                   (1, 16, -16)])
+                                   (1, 16, -16), (1, 16, 2 ** 22 + 16)])
 def test_gemm_rejects_bad_sizes(lib, M, N, K):
     st = nv.nvfp4_gemm(M, N, K, A16, A16B, A16C, A16D, A16E, None)
     assert st == nv.ERROR_INVALID_VALUE
@@ -83,12 +83,14 @@ def test_gemm_rejects_misaligned_pointers(lib):
 
 def test_gemm_path_rejects_bad_options(lib):
     ptrs = [A16, A16B, A16C, A16D, A16E]
-    assert nv.nvfp4_gemm_path(3, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_gemm_path(4, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
     assert nv.nvfp4_gemm_path(-1, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
-    for split in (3, 16, -1):
+    for split in (3, 32, -1):
         assert nv.nvfp4_gemm_path(0, split, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
-    # the dot-product family covers M <= 8 only
+    # the dot-product families cover M <= 8 only
     assert nv.nvfp4_gemm_path(nv.PATH_DOT, 0, 9, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_gemm_path(nv.PATH_STREAM, 0, 9, 16, 256, *ptrs, None) == \
+        nv.ERROR_INVALID_VALUE
 
 
 def test_gemm_rejects_overflowing_sizes(lib):

@@ -15,16 +15,18 @@ from parity import (FINITE_SCALES, check_close, gpu_gemm, random_case, say, to_d
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [(nv.PATH_DOT, 1), (nv.PATH_DOT, 2), (nv.PATH_DOT, 4), (nv.PATH_DOT, 8),
+PATHS = [(nv.PATH_STREAM, 4), (nv.PATH_STREAM, 8), (nv.PATH_STREAM, 16),
+         (nv.PATH_DOT, 1), (nv.PATH_DOT, 2), (nv.PATH_DOT, 4), (nv.PATH_DOT, 8),
          (nv.PATH_MFMA, 1), (nv.PATH_MFMA, 2), (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
          (nv.PATH_AUTO, 0)]
+VALU_PATHS = (nv.PATH_DOT, nv.PATH_STREAM)   # dot-product families: M <= 8
 SMALL_M = [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 130]
 SMALL_N = [1, 15, 16, 17, 65]
 SMALL_K = [16, 48, 256, 272, 528, 1024]
 
 
 def _paths_for(M):
-    return [(p, s) for p, s in PATHS if not (p == nv.PATH_DOT and M > 8)]
+    return [(p, s) for p, s in PATHS if not (p in VALU_PATHS and M > 8)]
 
 
 @pytest.mark.parametrize("path,split", PATHS)
@@ -33,7 +35,7 @@ def test_small_shapes(device, path, split):
     seed = 0
     for K in SMALL_K:
         for M in SMALL_M:
-            if path == nv.PATH_DOT and M > 8:
+            if path in VALU_PATHS and M > 8:
                 continue
             for N in SMALL_N:
                 seed += 1
@@ -73,8 +75,8 @@ def test_one_hot_rows_give_dequantised_weights(device, K):
     X = torch.zeros(M, K, dtype=torch.bfloat16)
     X[torch.arange(M), ks] = 1.0
     expect = Wd[ks.numpy(), :].astype(np.float32).astype(np.float64)
-    for path, split in _paths_for(M) + [(nv.PATH_DOT, 4)]:
-        if path == nv.PATH_DOT and M > 8:
+    for path, split in _paths_for(M) + [(nv.PATH_DOT, 4), (nv.PATH_STREAM, 16)]:
+        if path in VALU_PATHS and M > 8:
             Xs, ex = X[:8], expect[:8]
         else:
             Xs, ex = X, expect
