@@ -12,8 +12,9 @@ Protocol
     Cache) are rotated, so every step streams its weights from HBM.
   * The step is captured once per copy in a HIP graph; warmup replays, then exactly `steps`
     replays bracketed by torch.cuda.synchronize(), timed on the host clock.
-  * Per-kernel durations: HIP events around every GEMM launch, on the stream the kernels run on,
-    over `steps` eager steps; the dominant kernel (gate/up) gives the roofline object.
+  * Per-kernel durations: per GEMM, HIP graphs of back-to-back launches rotating over enough
+    cold copies (> 512 MB of weights), bracketed by HIP events on the stream the graphs run on;
+    the dominant kernel (gate/up) gives the roofline object.
   * The GPU output is checked against the oracle, and the oracle itself is timed on the host
     cores on the same layer (cpu_baseline).
   * "also": the verify shapes at M = 16 and M = 128, timed the same way (per-kernel events).
@@ -23,7 +24,6 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -35,32 +35,26 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) for NVFP4 skinny GEMM at M=1/16/128"
 EQUIV_MODEL_GB = 17.9     # the page's checkpoint size, for the tokens/s-equivalent figure
+CALIBRATION_BYTES = 256 << 20
+COLD_BYTES = 512 << 20      # rotated weight bytes per timed GEMM: twice the Infinity Cache
+LAUNCHES_PER_GRAPH = 32
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "skinny_gemm_nvfp4_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def load_traffic(kernel: str, workload: str):
-    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it was taken on the
-    current kernel sources; otherwise None."""
+def load_traffic(label: str):
+    """HBM bytes per launch of the GEMM `label` from the committed rocprofv3 PMC summary
+    (profiles/traffic.json), if it was taken on the current kernel sources; otherwise None."""
+    from skinny_gemm_nvfp4_amd.profile_summary import source_hash
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = data.get(f"{kernel}@{workload}")
+    entry = data.get(label)
     if not entry or entry.get("source_hash") != source_hash():
         return None
     return entry.get("bytes_per_launch")
@@ -69,9 +63,12 @@ def load_traffic(kernel: str, workload: str):
 class Layer:
     """Packed weights (C cold copies), activations and outputs of a list of GEMMs on the GPU."""
 
-    def __init__(self, gemms, copies, dev):
+    def __init__(self, gemms, copies, dev, tag, launches):
         import torch
         import skinny_gemm_nvfp4_amd as nv
+        self.tag = tag
+        self.launches = launches   # labels of the GEMM dispatches, in launch order
+        self.capturing = False
         self.names = [g.name for g in gemms]
         self.shapes = [g.shape for g in gemms]
         self.X = [g.X.to(dev) for g in gemms]
@@ -89,25 +86,65 @@ class Layer:
         import skinny_gemm_nvfp4_amd as nv
         Wq, Ws, g = self.packed[i][c]
         nv.gemm(self.X[i], Wq, Ws, g, out=self.Y[i])
+        if not self.capturing:
+            self.launches.append(self.label(i))
+
+    def label(self, i: int) -> str:
+        M, N, K = self.shapes[i]
+        return f"{self.tag}.{self.names[i]} M={M} N={N} K={K}"
+
+    def replayed(self) -> None:
+        """Record the dispatches of one graph replay of `step`."""
+        self.launches.extend(self.label(i) for i in range(len(self.names)))
 
     def step(self, c: int) -> None:
         for i in range(len(self.names)):
             self.run(c, i)
 
-    def kernel_times_us(self, reps: int):
-        """Average duration of every GEMM, from HIP events around each launch."""
+    def cold_copies(self, i: int) -> int:
+        """Copies of GEMM i's weights that together exceed twice the 256 MB Infinity Cache, so a
+        rotation over them streams from HBM; clones more copies when needed."""
+        from skinny_gemm_nvfp4_amd import roofline as rl
+        M, N, K = self.shapes[i]
+        need = max(self.copies, -(-COLD_BYTES // rl.weight_bytes(K, N)))
+        while len(self.packed[i]) < need:
+            self.packed[i].append(tuple(t.clone() for t in self.packed[i][0]))
+        return need
+
+    def kernel_times_us(self, launches: int):
+        """Average duration of one launch of every GEMM on its own.
+
+        Per GEMM, a HIP graph of LAUNCHES_PER_GRAPH back-to-back launches (rotating over cold
+        weight copies) is replayed until about `launches` launches ran; HIP events on the stream
+        the graphs run on bracket the replays. The figure is the kernel plus its share of the
+        dispatch gap, which is what a launch costs in a stream of GEMMs."""
         import torch
         stream = torch.cuda.current_stream()
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)] for _ in self.names]
-        for r in range(reps):
-            for i in range(len(self.names)):
-                ev[i][r][0].record(stream)
-                self.run(r % self.copies, i)
-                ev[i][r][1].record(stream)
-        torch.cuda.synchronize()
-        return [1e3 * sum(a.elapsed_time(b) for a, b in ev[i]) / reps
-                for i in range(len(self.names))]
+        out = []
+        for i in range(len(self.names)):
+            copies = self.cold_copies(i)
+            self.run(0, i)                     # eager first launch: one-time set-up
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            self.capturing = True
+            with torch.cuda.graph(graph):
+                for j in range(LAUNCHES_PER_GRAPH):
+                    self.run(j % copies, i)
+            self.capturing = False
+            replays = max(1, -(-launches // LAUNCHES_PER_GRAPH))
+            graph.replay()                     # warm
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(replays):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(1e3 * e0.elapsed_time(e1) / (replays * LAUNCHES_PER_GRAPH))
+            self.launches.extend([self.label(i)] * ((replays + 1) * LAUNCHES_PER_GRAPH))
+            del graph
+        return out
 
 
 def gemm_report(shape, us):
@@ -155,6 +192,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the M=16 / M=128 shapes")
+    ap.add_argument("--launch-log", default=None,
+                    help="write the label of every GEMM dispatch, in order, to this file (for "
+                         "matching a rocprofv3 kernel trace to the GEMMs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -168,14 +208,26 @@ def main() -> int:
 
     import skinny_gemm_nvfp4_amd as nv
     from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+    from skinny_gemm_nvfp4_amd import profile_summary as ps
 
     nv.load_library()
     dev = torch.device("cuda:0")
     C = max(1, args.cold_copies)
+    launches = []
+
+    # One plain device-to-device copy of known size: under rocprofv3 --pmc it calibrates
+    # FETCH_SIZE and WRITE_SIZE against bytes actually moved.
+    log(f"calibration copy of {CALIBRATION_BYTES} bytes")
+    src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
     log("generating and packing the M=1 dense layer (seeds 1-6)")
     wl = inputs.dense_layer_m1()
-    layer = Layer(wl.gemms, C, dev)
+    layer = Layer(wl.gemms, C, dev, "dense_layer_m1", launches)
     bytes_per_step = sum(rl.compulsory_bytes(*s) for s in layer.shapes)
 
     # Capture one step per cold copy in a HIP graph.
@@ -188,11 +240,13 @@ def main() -> int:
     torch.cuda.synchronize()
     eager_Y = [y.clone() for y in layer.Y]
     graphs = []
+    layer.capturing = True
     for c in range(C):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             layer.step(c)
         graphs.append(g)
+    layer.capturing = False
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} graph-replayed steps after {args.warmup} warmup")
@@ -204,6 +258,8 @@ def main() -> int:
         graphs[i % C].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    for i in range(args.warmup + args.steps):
+        layer.replayed()
     ms_per_step = 1e3 * (t1 - t0) / args.steps
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     for y, ye in zip(layer.Y, eager_Y):
@@ -216,7 +272,7 @@ def main() -> int:
     dom = max(range(len(layer.names)), key=lambda i: rl.compulsory_bytes(*layer.shapes[i]))
     dom_bytes = rl.compulsory_bytes(*layer.shapes[dom])
     achieved = dom_bytes / (kus[dom] * 1e-6) / 1e9
-    traffic = load_traffic(f"gemm_{layer.names[dom]}", "dense_layer_m1")
+    traffic = load_traffic(layer.label(dom))
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rl.HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / rl.HBM_PEAK_GBS, 4),
             "traffic": traffic, "kernel": f"nvfp4 GEMM {layer.names[dom]} M=1 "
@@ -243,8 +299,8 @@ def main() -> int:
                             ("batched_verify_m128", inputs.batched_verify_m128)):
             log(f"timing {wname}")
             w = make()
-            lay = Layer(w.gemms, C, dev)
-            us = lay.kernel_times_us(max(20, args.steps // 4))
+            lay = Layer(w.gemms, C, dev, wname, launches)
+            us = lay.kernel_times_us(max(64, args.steps))
             also[wname] = {n: gemm_report(s, t) for n, s, t in zip(lay.names, lay.shapes, us)}
             del lay
             torch.cuda.empty_cache()
@@ -267,8 +323,11 @@ def main() -> int:
         "cpu_baseline": cpu,
         "parity": parity,
         "also": also,
-        "source_hash": source_hash(),
+        "source_hash": ps.source_hash(),
     }
+    if args.launch_log:
+        with open(args.launch_log, "w") as f:
+            f.write("\n".join(launches) + "\n")
     print(json.dumps(line), flush=True)
     return 0
 

@@ -108,7 +108,9 @@ typedef enum {
     NVFP4_PATH_AUTO = 0,   /* what nvfp4_gemm does */
     NVFP4_PATH_DOT = 1,    /* VALU, tiled: E2M1->bf16 decode, v_dot2_f32_bf16, fp32 partial * s */
     NVFP4_PATH_MFMA = 2,   /* E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 tiles */
-    NVFP4_PATH_STREAM = 3  /* VALU, persistent: one workgroup per compute unit, X in LDS */
+    NVFP4_PATH_STREAM = 3, /* VALU, persistent: one workgroup per compute unit, X in LDS */
+    NVFP4_PATH_MFMA_STREAM = 4 /* matrix cores, persistent: one workgroup per compute unit and
+                                  16-row block of X */
 } nvfp4_path_t;
 
 /*
@@ -120,6 +122,8 @@ typedef enum {
  *   NVFP4_PATH_DOT, NVFP4_PATH_MFMA: waves of one workgroup that share the K loop: 1, 2, 4 or 8;
  *   NVFP4_PATH_STREAM: waves of the one workgroup per compute unit: 4, 8 or 16. If X does not
  *   fit in LDS (M * K too large) the call runs NVFP4_PATH_DOT with its own split instead.
+ *   NVFP4_PATH_MFMA_STREAM: waves of each persistent workgroup: 4 or 8. It needs K % 128 == 0;
+ *   for other K the call runs NVFP4_PATH_MFMA with its own split instead.
  * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
 nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,

@@ -23,6 +23,7 @@ PATH_AUTO = 0
 PATH_DOT = 1
 PATH_MFMA = 2
 PATH_STREAM = 3
+PATH_MFMA_STREAM = 4
 
 _lib = None
 

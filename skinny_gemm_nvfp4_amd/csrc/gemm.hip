@@ -5,14 +5,20 @@
 //     unit with an equal share of the columns, X staged in LDS. Decode (M = 1) and the smallest M.
 //   * gemv.h (NVFP4_PATH_DOT): tiled dot-product kernel, one workgroup per 4 C columns. Used
 //     when X does not fit in LDS for the persistent kernel.
-//   * mfma.h (NVFP4_PATH_MFMA): bf16 matrix-core kernel for M >= 16 (speculative verification).
+//   * verify_stream.h (NVFP4_PATH_MFMA_STREAM): persistent bf16 matrix-core kernel, one workgroup
+//     per compute unit and 16-row block of X (speculative verification), K % 128 == 0.
+//   * mfma.h (NVFP4_PATH_MFMA): tiled bf16 matrix-core kernel for the other K.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "gemv.h"
 #include "gemv_stream.h"
 #include "launch.h"
 #include "mfma.h"
+#include "verify_stream.h"
 
 namespace nvfp4 {
 
@@ -60,8 +66,6 @@ const int kDotColumns[8] = {4, 2, 2, 2, 1, 1, 1, 1};  // C of each MR
 const StreamFn kStream[3][8][3] = {NVFP4_STREAM_TABLE(true, false),
                                    NVFP4_STREAM_TABLE(false, false),
                                    NVFP4_STREAM_TABLE(false, true)};
-constexpr int kMaxDevices = 64;
-std::atomic<bool> g_stream_lds_ready[kMaxDevices][3][8][3];
 
 // ---- MFMA kernels: [MT - 1][split index], NT column tiles ----
 #define NVFP4_MFMA_SPLITS(T, NT, NARROW)                                                   \
@@ -79,6 +83,15 @@ std::atomic<bool> g_stream_lds_ready[kMaxDevices][3][8][3];
 const KernelFn kMfmaWide[8][4] = NVFP4_MFMA_TABLE(false);
 const KernelFn kMfmaNarrow[8][4] = NVFP4_MFMA_TABLE(true);
 const int kMfmaColumnTiles[8] = {2, 2, 1, 1, 1, 1, 1, 1};  // NT of each MT
+
+// ---- persistent matrix-core kernels: [TC index][wave index] ----
+// TC column tiles of 16 are processed together; the smallest TC >= the workgroup's tile count is
+// used, so that X is read once per workgroup.
+const int kVerifyTiles[6] = {1, 2, 3, 4, 6, 9};
+#define NVFP4_VERIFY_WAVES(TC) {&verify_stream_kernel<TC, 4>, &verify_stream_kernel<TC, 8>}
+const KernelFn kVerify[6][2] = {NVFP4_VERIFY_WAVES(1), NVFP4_VERIFY_WAVES(2),
+                                NVFP4_VERIFY_WAVES(3), NVFP4_VERIFY_WAVES(4),
+                                NVFP4_VERIFY_WAVES(6), NVFP4_VERIFY_WAVES(9)};
 
 int split_index(int split)
 {
@@ -122,6 +135,53 @@ int compute_units()
     return cus;
 }
 
+// Lets `fn` use up to `bytes` of LDS (above the 64 KB default), once per kernel and device.
+hipError_t allow_lds(const void *fn, int bytes)
+{
+    if (bytes <= kDefaultLds)
+        return hipSuccess;
+    static std::mutex mu;
+    static std::set<std::pair<int, const void *>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({dev, fn}))
+        return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e == hipSuccess)
+        done.insert({dev, fn});
+    return e;
+}
+
+// Workgroups, column-tile chunk and LDS bytes of the persistent matrix-core kernel; false if the
+// shape needs the tiled kernel (K % 128 != 0, or a workgroup's code bytes reach 2^31).
+struct VerifyPlan {
+    int grid, tc_index, lds;
+};
+
+bool verify_plan(int N, int K, int waves, VerifyPlan *P)
+{
+    if (K % kVerifyWindow != 0)
+        return false;
+    const int G = std::max(1, std::min(compute_units(), (N + 15) / 16));
+    const int cmax = (N + G - 1) / G;
+    if ((long long)cmax * (K / 2) >= (1LL << 31))
+        return false;
+    const int tiles = (cmax + 15) / 16;
+    int ti = 5;
+    for (int i = 0; i < 6; i++)
+        if (kVerifyTiles[i] >= tiles) {
+            ti = i;
+            break;
+        }
+    P->grid = G;
+    P->tc_index = ti;
+    P->lds = verify_lds_bytes(kVerifyTiles[ti], waves);
+    return P->lds <= kMaxLds;
+}
+
 // Workgroups and LDS layout of the persistent kernel; false if X does not fit in LDS.
 bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L)
 {
@@ -160,7 +220,22 @@ bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L)
 bool choose_config(int M, int N, int K, int *path, int *split)
 {
     if (*path == kPathAuto)
-        *path = (M <= 4) ? kPathStream : kPathMfma;
+        *path = (M <= 4) ? kPathStream : kPathMfmaStream;
+    if (*path == kPathMfmaStream) {
+        VerifyPlan P;
+        if (*split == 0) {
+            // Wide chunks keep more bytes in flight per wave; narrow ones need more waves.
+            if (!verify_plan(N, K, 8, &P))
+                P.tc_index = -1;
+            *split = (P.tc_index >= 4) ? 4 : 8;
+        }
+        if (*split != 4 && *split != 8)
+            return false;
+        if (verify_plan(N, K, *split, &P))
+            return true;
+        *path = kPathMfma;  // K % 128 != 0: tiled kernel
+        *split = 0;
+    }
     if (*path == kPathStream) {
         if (M > kDotMaxM)
             return false;
@@ -199,6 +274,19 @@ bool choose_config(int M, int N, int K, int *path, int *split)
 hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t stream)
 {
     (void)hipGetLastError();  // start from a clean error state
+    if (path == kPathMfmaStream) {
+        VerifyPlan P;
+        if (!verify_plan(a.N, a.K, split, &P))
+            return hipErrorInvalidValue;
+        const KernelFn fn = kVerify[P.tc_index][split == 4 ? 0 : 1];
+        const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), P.lds);
+        if (e != hipSuccess)
+            return e;
+        const unsigned mblocks = (unsigned)((a.M + 15) / 16);
+        hipLaunchKernelGGL(fn, dim3((unsigned)P.grid, mblocks), dim3(kWave * split), P.lds,
+                           stream, a);
+        return hipGetLastError();
+    }
     if (path == kPathStream) {
         StreamLayout L;
         int grid = 0;
@@ -208,23 +296,9 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
         const int wi = wave_index(split);
         const StreamFn fn = kStream[variant][a.M - 1][wi];
         const int lds = L.x_bytes + L.part_bytes;
-        if (lds > kDefaultLds) {
-            // Opt in to more than 64 KB of LDS, once per kernel and device.
-            int dev = 0;
-            (void)hipGetDevice(&dev);
-            std::atomic<bool> *ready =
-                (dev >= 0 && dev < kMaxDevices) ? &g_stream_lds_ready[dev][variant][a.M - 1][wi]
-                                                : nullptr;
-            if (!ready || !ready->load()) {
-                const hipError_t e = hipFuncSetAttribute(
-                    reinterpret_cast<const void *>(fn),
-                    hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-                if (e != hipSuccess)
-                    return e;
-                if (ready)
-                    ready->store(true);
-            }
-        }
+        const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), lds);
+        if (e != hipSuccess)
+            return e;
         hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * split), lds, stream, a, L);
         return hipGetLastError();
     }

@@ -15,7 +15,7 @@ struct GemmArgs {
     int M, N, K;
 };
 
-enum Path { kPathAuto = 0, kPathDot = 1, kPathMfma = 2, kPathStream = 3 };
+enum Path { kPathAuto = 0, kPathDot = 1, kPathMfma = 2, kPathStream = 3, kPathMfmaStream = 4 };
 
 // Largest M the dot-product kernel families are instantiated for.
 constexpr int kDotMaxM = 8;
@@ -24,7 +24,8 @@ constexpr int kDotMaxM = 8;
 constexpr int kMaxK = 1 << 22;
 
 // Resolves path/split (0 = automatic) for this shape. Returns false for an unsupported pair.
-// A persistent (stream) request whose X does not fit in LDS becomes the tiled dot-product path.
+// A persistent dot-product request whose X does not fit in LDS becomes the tiled dot-product
+// path; a persistent matrix-core request with K % 128 != 0 becomes the tiled matrix-core path.
 bool choose_config(int M, int N, int K, int *path, int *split);
 
 // Launch the GEMM with a resolved path and split. Returns the hipError_t of the launch.

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 PATHS = [(nv.PATH_STREAM, 4), (nv.PATH_STREAM, 8), (nv.PATH_STREAM, 16),
          (nv.PATH_DOT, 1), (nv.PATH_DOT, 2), (nv.PATH_DOT, 4), (nv.PATH_DOT, 8),
          (nv.PATH_MFMA, 1), (nv.PATH_MFMA, 2), (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
-         (nv.PATH_AUTO, 0)]
+         (nv.PATH_MFMA_STREAM, 4), (nv.PATH_MFMA_STREAM, 8), (nv.PATH_AUTO, 0)]
 VALU_PATHS = (nv.PATH_DOT, nv.PATH_STREAM)   # dot-product families: M <= 8
 SMALL_M = [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 130]
 SMALL_N = [1, 15, 16, 17, 65]
@@ -86,8 +86,9 @@ def test_one_hot_rows_give_dequantised_weights(device, K):
         assert diff.size == 0, f"path {path}: {len(diff)} mismatches, first {diff[:3].tolist()}"
 
 
-def test_nan_scale_propagates(device):
-    K, N, M = 64, 16, 2
+@pytest.mark.parametrize("K", [64, 256])
+def test_nan_scale_propagates(device, K):
+    N, M = 16, 2
     gen = inputs.generator(5)
     Wq, Ws = inputs.random_packed(gen, N, K, scale_bytes=[0x38])
     Ws[3, 1] = 0x7F
@@ -119,3 +120,17 @@ def test_deterministic(device):
         a = gpu_gemm(X, packed, device, path, split)
         b = gpu_gemm(X, packed, device, path, split)
         assert np.array_equal(a, b), f"path {path} split {split} not reproducible"
+
+
+@pytest.mark.parametrize("path,split", [(nv.PATH_MFMA_STREAM, 4), (nv.PATH_MFMA_STREAM, 8),
+                                        (nv.PATH_STREAM, 16)])
+def test_many_columns_per_workgroup(device, path, split):
+    """Enough columns that a persistent workgroup owns more column tiles than one pass takes
+    (several chunks per workgroup), with a ragged last tile and a ragged row block."""
+    M = 8 if path == nv.PATH_STREAM else 19
+    N, K = 256 * 16 * 11 + 5, 256
+    X, Wq, Ws, g = random_case(41, M, N, K, FINITE_SCALES)
+    Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
+    say(f"many-columns path={path} split={split} M={M} N={N} K={K}")
+    Y = gpu_gemm(X, to_device_packed(Wq, Ws, g, device), device, path, split)
+    check_close(Y, Yref, A, f"M={M} N={N} K={K}")
