@@ -20,7 +20,10 @@
 //     8 q + e at step d is byte 2 d + q / 2 of the window's 8 scale bytes of the column.
 //   * B = e2m1 * s decoded to bf16 (exact); the sum over k does not depend on the slot order, so
 //     this is the plain product.
-//   * Every load of the next window is in flight while the current one is multiplied.
+//   * Every load of the next window is in flight while the current one is multiplied. The weight
+//     loads use the normal cache policy: a wavefront reads 64 of the 128 bytes of a line and the
+//     other half belongs to another wavefront's window, which then hits in L2 instead of being
+//     fetched again.
 //   * The W partial tiles are summed through LDS in wavefront order and scaled by g once.
 //     Results are reproducible.
 // Requires K % 128 == 0 (the 8 scale bytes of a window are then one aligned 8-byte word).
@@ -57,9 +60,9 @@ struct VerifyWindow {
 #pragma unroll
         for (int t = 0; t < TC; t++) {
             c[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                rq, off_if(live, vq + (uint32_t)t * tq + (uint32_t)w * 64u), 0, kAuxStream);
+                rq, off_if(live, vq + (uint32_t)t * tq + (uint32_t)w * 64u), 0, kAuxNormal);
             s[t] = __builtin_amdgcn_raw_buffer_load_b64(
-                rs, off_if(live, vs + (uint32_t)t * ts + (uint32_t)w * 8u), 0, kAuxStream);
+                rs, off_if(live, vs + (uint32_t)t * ts + (uint32_t)w * 8u), 0, kAuxNormal);
         }
     }
 
