@@ -78,14 +78,18 @@ class Layer:
             W = g.W.to(dev)
             p = nv.pack(W)
             del W
-            self.packed.append([p] + [tuple(t.clone() for t in p) for _ in range(copies - 1)])
+            self.packed.append([p] + [self._clone(p) for _ in range(copies - 1)])
         torch.cuda.synchronize()
         self.copies = copies
 
+    @staticmethod
+    def _clone(p):
+        import skinny_gemm_nvfp4_amd as nv
+        return nv.Packed(p.Wq.clone(), p.Ws.clone(), p.g.clone(), p.N)
+
     def run(self, c: int, i: int) -> None:
         import skinny_gemm_nvfp4_amd as nv
-        Wq, Ws, g = self.packed[i][c]
-        nv.gemm(self.X[i], Wq, Ws, g, out=self.Y[i])
+        nv.gemm(self.X[i], *self.packed[i][c], out=self.Y[i])
         if not self.capturing:
             self.launches.append(self.label(i))
 
@@ -108,7 +112,7 @@ class Layer:
         M, N, K = self.shapes[i]
         need = max(self.copies, -(-COLD_BYTES // rl.weight_bytes(K, N)))
         while len(self.packed[i]) < need:
-            self.packed[i].append(tuple(t.clone() for t in self.packed[i][0]))
+            self.packed[i].append(self._clone(self.packed[i][0]))
         return need
 
     def kernel_times_us(self, launches: int):

@@ -22,13 +22,23 @@
  *   - tensor scale g: one fp32 per weight matrix.
  *   - dequantised weight: w(k,n) = e2m1(code(k,n)) * e4m3(Ws[n][k/16]) * g.
  *
- * Layout (all row-major, element (i,j) of an [R][C] array at offset i*C + j)
- *   W      fp32  [K][N]     input of nvfp4_pack
- *   Wq     uint8 [N][K/2]   byte (n, k/2) holds k even in bits 3..0 and k odd in bits 7..4
- *   Wscale uint8 [N][K/16]  E4M3 byte of block (n, k/16)
- *   gscale fp32  [1]        g, in device memory
- *   X      bf16  [M][K]     passed as uint16_t bit patterns
- *   Y      fp32  [M][N]     fully overwritten
+ * Layout (row-major: element (i,j) of an [R][C] array sits at offset i*C + j)
+ *   W      fp32  [K][N]             input of nvfp4_pack
+ *   Wq     uint8 [NG][CH][4][16]    codes, NG = ceil(N/4) groups of 4 columns, CH = ceil(K/32)
+ *                                   chunks of 32 k: byte (g, c, j, i) holds the codes of column
+ *                                   n = 4g + j at k = 32c + 2i (bits 3..0) and k = 32c + 2i + 1
+ *                                   (bits 7..4)
+ *   Wscale uint8 [NG][CH][4][2]     E4M3 scales: byte (g, c, j, b) is the scale of column 4g + j,
+ *                                   block k/16 = 2c + b
+ *   gscale fp32  [1]                g, in device memory
+ *   X      bf16  [M][K]             passed as uint16_t bit patterns
+ *   Y      fp32  [M][N]             fully overwritten
+ * Bytes of columns n >= N and of k >= K (the padding up to 4 columns and 32 k) are zero, as
+ * nvfp4_pack writes them; nvfp4_codes_bytes / nvfp4_scales_bytes give the array sizes.
+ * Why this order: one 32-k chunk of 4 adjacent columns is 64 contiguous bytes, so the 16 chunks
+ * of a 512-k window of a group are 1 KB in one piece (one 16-byte load per lane of a wavefront,
+ * whole 128-byte lines), and a 16-column x 128-k tile is four 256-byte pieces; both kinds of
+ * kernel read only whole cache lines. Scales follow the same order at 2 bytes per (column, chunk).
  *
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer owned by the caller; the library keeps none of them past
@@ -75,8 +85,8 @@ typedef enum {
  *
  *   K, N    sizes of W (K % 16 == 0)
  *   W       in:  fp32 [K][N], device
- *   Wq      out: uint8 [N][K/2], device
- *   Wscale  out: uint8 [N][K/16], device
+ *   Wq      out: uint8 [NG][CH][4][16] (nvfp4_codes_bytes(N, K) bytes), device; padding zeroed
+ *   Wscale  out: uint8 [NG][CH][4][2] (nvfp4_scales_bytes(N, K) bytes), device; padding zeroed
  *   gscale  out: fp32 [1], device; it also holds the running amax while the call executes
  *   stream  hipStream_t
  */
@@ -94,8 +104,8 @@ nvfp4_status_t nvfp4_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Ws
  *
  *   M, N, K  sizes (K % 16 == 0)
  *   X        in:  bf16 bits [M][K], device
- *   Wq       in:  uint8 [N][K/2], device (as written by nvfp4_pack)
- *   Wscale   in:  uint8 [N][K/16], device
+ *   Wq       in:  uint8 [NG][CH][4][16], device (as written by nvfp4_pack, padding zero)
+ *   Wscale   in:  uint8 [NG][CH][4][2], device
  *   gscale   in:  fp32 [1], device (read by the kernel; the host never reads it)
  *   Y        out: fp32 [M][N], device
  *   stream   hipStream_t
@@ -103,38 +113,42 @@ nvfp4_status_t nvfp4_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Ws
 nvfp4_status_t nvfp4_gemm(int M, int N, int K, const uint16_t *X, const uint8_t *Wq,
                           const uint8_t *Wscale, const float *gscale, float *Y, void *stream);
 
-/* Kernel families nvfp4_gemm chooses between (for nvfp4_gemm_path). */
+/* Kernel families nvfp4_gemm chooses between (for nvfp4_gemm_path). Both are persistent: one
+ * workgroup per compute unit (and per 16-row block of X for the matrix-core kernel), each with an
+ * equal share of the 4-column groups. */
 typedef enum {
-    NVFP4_PATH_AUTO = 0,   /* what nvfp4_gemm does */
-    NVFP4_PATH_DOT = 1,    /* VALU, tiled: E2M1->bf16 decode, v_dot2_f32_bf16, fp32 partial * s */
-    NVFP4_PATH_MFMA = 2,   /* E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 tiles */
-    NVFP4_PATH_STREAM = 3, /* VALU, persistent: one workgroup per compute unit, X in LDS */
-    NVFP4_PATH_MFMA_STREAM = 4 /* matrix cores, persistent: one workgroup per compute unit and
-                                  16-row block of X */
+    NVFP4_PATH_AUTO = 0,  /* what nvfp4_gemm does */
+    NVFP4_PATH_DOT = 1,   /* VALU: E2M1->bf16 decode, v_dot2_f32_bf16 against X staged in LDS,
+                             fp32 partial * s; M <= 8 */
+    NVFP4_PATH_MFMA = 2   /* matrix cores: E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 on
+                             16-row blocks of X; any M */
 } nvfp4_path_t;
 
 /*
  * nvfp4_gemm_path -- nvfp4_gemm with the kernel family forced, for testing and tuning.
  *
  * Same operation, arguments, rules and results as nvfp4_gemm. `path` is an nvfp4_path_t.
- * NVFP4_PATH_DOT and NVFP4_PATH_STREAM accept M <= 8 only (else NVFP4_ERROR_INVALID_VALUE).
- * `split` (0 picks it like nvfp4_gemm):
- *   NVFP4_PATH_DOT, NVFP4_PATH_MFMA: waves of one workgroup that share the K loop: 1, 2, 4 or 8;
- *   NVFP4_PATH_STREAM: waves of the one workgroup per compute unit: 4, 8 or 16. If X does not
- *   fit in LDS (M * K too large) the call runs NVFP4_PATH_DOT with its own split instead.
- *   NVFP4_PATH_MFMA_STREAM: waves of each persistent workgroup: 4 or 8. It needs K % 128 == 0;
- *   for other K the call runs NVFP4_PATH_MFMA with its own split instead.
+ * `split` is the number of wavefronts of each workgroup (0 picks it like nvfp4_gemm):
+ *   NVFP4_PATH_DOT: 4, 8 or 16; M <= 8, else NVFP4_ERROR_INVALID_VALUE. If X does not fit in
+ *     LDS (M * K too large) the call runs NVFP4_PATH_MFMA with its own split instead.
+ *   NVFP4_PATH_MFMA: 4 or 8.
  * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
 nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,
                                const uint8_t *Wq, const uint8_t *Wscale, const float *gscale,
                                float *Y, void *stream);
 
+/* Bytes of Wq for an N x K weight: 64 * ceil(N/4) * ceil(K/32); 0 if N < 1 or K < 1. */
+uint64_t nvfp4_codes_bytes(int N, int K);
+
+/* Bytes of Wscale for an N x K weight: 8 * ceil(N/4) * ceil(K/32); 0 if N < 1 or K < 1. */
+uint64_t nvfp4_scales_bytes(int N, int K);
+
 /* Static description of a status code; never NULL. */
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

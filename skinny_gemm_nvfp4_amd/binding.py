@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import NamedTuple, Optional
 
 import torch
 
@@ -22,8 +22,6 @@ ERROR_LAUNCH = 3
 PATH_AUTO = 0
 PATH_DOT = 1
 PATH_MFMA = 2
-PATH_STREAM = 3
-PATH_MFMA_STREAM = 4
 
 _lib = None
 
@@ -61,6 +59,10 @@ def load_library() -> ctypes.CDLL:
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_abi_version.argtypes = []
     L.nvfp4_abi_version.restype = ci
+    L.nvfp4_codes_bytes.argtypes = [ci, ci]
+    L.nvfp4_codes_bytes.restype = ctypes.c_uint64
+    L.nvfp4_scales_bytes.argtypes = [ci, ci]
+    L.nvfp4_scales_bytes.restype = ctypes.c_uint64
     _lib = L
     return L
 
@@ -90,6 +92,35 @@ def nvfp4_gemm_path(path: int, split: int, M: int, N: int, K: int, X: int, Wq: i
     return load_library().nvfp4_gemm_path(path, split, M, N, K, X, Wq, Wscale, gscale, Y, stream)
 
 
+def nvfp4_codes_bytes(N: int, K: int) -> int:
+    return load_library().nvfp4_codes_bytes(N, K)
+
+
+def nvfp4_scales_bytes(N: int, K: int) -> int:
+    return load_library().nvfp4_scales_bytes(N, K)
+
+
+# ---- packed layout (include/nvfp4.h): 4-column groups x 32-k chunks ----
+
+def codes_shape(N: int, K: int):
+    """Shape of Wq: [ceil(N/4)][ceil(K/32)][4][16] bytes."""
+    return (-(-N // 4), -(-K // 32), 4, 16)
+
+
+def scales_shape(N: int, K: int):
+    """Shape of Wscale: [ceil(N/4)][ceil(K/32)][4][2] bytes."""
+    return (-(-N // 4), -(-K // 32), 4, 2)
+
+
+class Packed(NamedTuple):
+    """NVFP4 weights as nvfp4_pack writes them: codes, block scales, tensor scale, and the true
+    column count N (the arrays are padded to a multiple of 4 columns)."""
+    Wq: torch.Tensor
+    Ws: torch.Tensor
+    g: torch.Tensor
+    N: int
+
+
 # ---- tensor-level helpers ----
 
 def _stream(stream) -> int:
@@ -109,33 +140,35 @@ def _check_device(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None
         raise ValueError(f"{name} must be contiguous")
 
 
-def pack(W: torch.Tensor, stream=None, out=None) -> Tuple[torch.Tensor, torch.Tensor,
-                                                           torch.Tensor]:
-    """Quantise fp32 W[K, N] (device) to (Wq uint8 [N, K/2], Ws uint8 [N, K/16], g fp32 [1])."""
+def pack(W: torch.Tensor, stream=None, out=None) -> Packed:
+    """Quantise fp32 W[K, N] (device) to Packed(Wq, Ws, g, N) in the layout of include/nvfp4.h."""
     K, N = W.shape
     _check_device(W, "W", torch.float32, (K, N))
     if out is None:
-        Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
-        Ws = torch.empty((N, K // 16), dtype=torch.uint8, device=W.device)
+        Wq = torch.empty(codes_shape(N, K), dtype=torch.uint8, device=W.device)
+        Ws = torch.empty(scales_shape(N, K), dtype=torch.uint8, device=W.device)
         g = torch.empty(1, dtype=torch.float32, device=W.device)
     else:
-        Wq, Ws, g = out
+        Wq, Ws, g = out[:3]
+        _check_device(Wq, "Wq", torch.uint8, codes_shape(N, K))
+        _check_device(Ws, "Ws", torch.uint8, scales_shape(N, K))
+        _check_device(g, "g", torch.float32, (1,))
     st = nvfp4_pack(K, N, W.data_ptr(), Wq.data_ptr(), Ws.data_ptr(), g.data_ptr(),
                     _stream(stream))
     if st != SUCCESS:
         raise NVFP4Error(st, "nvfp4_pack")
-    return Wq, Ws, g
+    return Packed(Wq, Ws, g, N)
 
 
-def gemm(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Tensor, stream=None,
-         out: Optional[torch.Tensor] = None, path: int = PATH_AUTO, split: int = 0
+def gemm(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Tensor, N: int,
+         stream=None, out: Optional[torch.Tensor] = None, path: int = PATH_AUTO, split: int = 0
          ) -> torch.Tensor:
-    """Y[M, N] = X[M, K] . dequant(Wq, Ws, g) in fp32. X is bf16 on the device."""
+    """Y[M, N] = X[M, K] . dequant(Wq, Ws, g) in fp32. X is bf16 on the device; Wq/Ws are in the
+    packed layout (Packed from pack(), or codes_shape/scales_shape arrays)."""
     M, K = X.shape
-    N = Wq.shape[0]
     _check_device(X, "X", torch.bfloat16, (M, K))
-    _check_device(Wq, "Wq", torch.uint8, (N, K // 2))
-    _check_device(Ws, "Ws", torch.uint8, (N, K // 16))
+    _check_device(Wq, "Wq", torch.uint8, codes_shape(N, K))
+    _check_device(Ws, "Ws", torch.uint8, scales_shape(N, K))
     _check_device(g, "g", torch.float32, (1,))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=X.device)

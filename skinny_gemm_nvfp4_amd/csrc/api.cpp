@@ -59,9 +59,9 @@ nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const u
         return NVFP4_ERROR_INVALID_VALUE;
     if (!X || !Wq || !Wscale || !gscale || !Y)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_MFMA_STREAM)
+    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_MFMA)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 16)
+    if (split != 0 && split != 4 && split != 8 && split != 16)
         return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
         !aligned(Y, 4))
@@ -101,6 +101,20 @@ const char *nvfp4_status_string(nvfp4_status_t status)
 int nvfp4_abi_version(void)
 {
     return NVFP4_ABI_VERSION;
+}
+
+uint64_t nvfp4_codes_bytes(int N, int K)
+{
+    if (N < 1 || K < 1)
+        return 0;
+    return nvfp4::codes_bytes(N, K);
+}
+
+uint64_t nvfp4_scales_bytes(int N, int K)
+{
+    if (N < 1 || K < 1)
+        return 0;
+    return nvfp4::scales_bytes(N, K);
 }
 
 }  // extern "C"

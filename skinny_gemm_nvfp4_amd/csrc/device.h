@@ -9,9 +9,7 @@
 //     RTX5090" model card, table "Recipe (NVIDIA ModelOpt)": NVFP4, group size 16).
 //   * e2m1 * s has at most 2 + 4 significant bits, so it is exact in fp32 and in bf16.
 //
-// Memory helpers: packed weights are read exactly once per call, so their loads carry the
-// non-temporal hint and do not displace the activations, which every workgroup re-reads, from
-// the caches.
+// Memory helpers: raw buffer descriptors, so that loads past a workgroup's range read zeros.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -115,83 +113,25 @@ __device__ __forceinline__ uint32_t off_if(bool valid, uint32_t off)
     return valid ? off : kOutOfRange;
 }
 
-// One chunk of one output column: 32 consecutive k, i.e. 16 code bytes and 2 scale bytes.
+// One chunk of one output column: 32 consecutive k, i.e. 16 code bytes and the aligned 4-byte
+// word that holds the chunk's 2 scale bytes (and those of the neighbouring column of the group).
 struct Chunk {
     uint32_t code[4];   // code[d] holds k = 8d .. 8d+7 of the chunk
-    uint32_t scale;     // byte 0: block of k 0..15, byte 1: block of k 16..31
+    uint32_t scale;     // >> (16 * (column & 1)): byte 0 = block of k 0..15, byte 1 = k 16..31
 };
 
-// Loads the chunk that starts at k = kc (a multiple of 32) of a row whose codes start at byte
-// qrow of rq and whose scales start at byte srow of rs. Blocks at or beyond K read as code 0
-// with scale byte 0, which add exactly zero.
-// Wide layout (K % 64 == 0): one 16-byte code load and the aligned 4-byte word that holds the
-// chunk's two scale bytes; rows are 4-byte aligned, so that word never leaves the row.
-// NARROW (any other K % 16 == 0): two 8-byte code loads and two 1-byte scale loads; code rows
-// are 8-byte aligned and the last chunk of a row may hold a single block.
-template <bool NARROW>
-__device__ __forceinline__ Chunk load_chunk(rsrc_t rq, rsrc_t rs, uint32_t qrow, uint32_t srow,
-                                            int kc, int K)
+// Sum of v over the 16 lanes that share lane & 3, in a fixed order (lane distance 4, 8, 16, 32),
+// so every lane gets the same bits.
+__device__ __forceinline__ float sum_lanes_stride4(float v)
 {
-    Chunk c;
-    if (!NARROW) {
-        const bool v = kc < K;  // K % 64 == 0: the chunk is either whole or absent
-        const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(
-            rq, off_if(v, qrow + (uint32_t)kc / 2), 0, kAuxStream);
-        c.code[0] = q[0];
-        c.code[1] = q[1];
-        c.code[2] = q[2];
-        c.code[3] = q[3];
-        // The 4-byte word holding this chunk's two scale bytes (and the neighbouring chunk's);
-        // scale_pair() picks the right half once the data is there. A 2-byte load would need a
-        // zero-extension right after it, which stalls on the load.
-        c.scale = __builtin_amdgcn_raw_buffer_load_b32(
-            rs, off_if(v, (srow + (uint32_t)kc / 16) & ~3u), 0, kAuxStream);
-    } else {
-        const bool v0 = kc < K, v1 = kc + 16 < K;
-        const u32x2_t q0 = __builtin_amdgcn_raw_buffer_load_b64(
-            rq, off_if(v0, qrow + (uint32_t)kc / 2), 0, kAuxStream);
-        const u32x2_t q1 = __builtin_amdgcn_raw_buffer_load_b64(
-            rq, off_if(v1, qrow + (uint32_t)kc / 2 + 8), 0, kAuxStream);
-        c.code[0] = q0[0];
-        c.code[1] = q0[1];
-        c.code[2] = q1[0];
-        c.code[3] = q1[1];
-        const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(
-            rs, off_if(v0, srow + (uint32_t)kc / 16), 0, kAuxStream);
-        const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(
-            rs, off_if(v1, srow + (uint32_t)kc / 16 + 1), 0, kAuxStream);
-        c.scale = b0 | (b1 << 8);
-    }
-    return c;
-}
-
-// The two scale bytes of a chunk loaded by load_chunk, in bits 0..15. In the wide layout the
-// byte offset srow + kc / 16 is even (K / 16 and kc / 16 are even and the descriptor base is
-// 4-byte aligned, see scale_rsrc), so the pair is the low or the high half of the loaded word.
-template <bool NARROW>
-__device__ __forceinline__ uint32_t scale_pair(uint32_t word, uint32_t srow, int kc)
-{
-    if (NARROW)
-        return word;
-    return word >> (((srow + (uint32_t)kc / 16) & 2u) * 8u);
-}
-
-// Descriptor over rows [first, first + rows) of the scale array Ws[.][K/16]. Its base is rounded
-// down to 4 bytes (Ws itself is 16-byte aligned, so the base stays inside Ws) and *bias is the
-// byte offset of the first row from that base; a row's scales start at *bias + row * (K / 16).
-__device__ __forceinline__ rsrc_t scale_rsrc(const uint8_t *Ws, size_t first, int rows, int K,
-                                             uint32_t *bias)
-{
-    const size_t start = first * (size_t)(K / 16);
-    *bias = (uint32_t)(start & 3u);
-    return make_rsrc(Ws + (start - *bias), (uint32_t)rows * (uint32_t)(K / 16) + *bias);
-}
-
-// Eight bf16 of X (16 bytes) at byte offset off of rx, or zeros if k is at or beyond K.
-// K % 16 == 0 and k % 8 == 0, so k < K implies k + 8 <= K.
-__device__ __forceinline__ u32x4_t load_x8(rsrc_t rx, uint32_t off, int k, int K)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(rx, off_if(k < K, off), 0, kAuxNormal);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    const uint32_t u = __float_as_uint(v);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const uint32_t u2 = __float_as_uint(v);
+    auto p2 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+    return __uint_as_float(p2[0]) + __uint_as_float(p2[1]);
 }
 
 // A value the compiler may keep in a scalar register (it is the same in every lane).

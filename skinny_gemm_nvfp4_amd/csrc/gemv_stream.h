@@ -5,24 +5,25 @@
 // reaches the HBM roof only if every compute unit keeps the same number of bytes in flight until
 // the very end, so the work is split evenly by construction instead of by tile count:
 //
-//   * One workgroup of W wavefronts per compute unit. Workgroup b owns the output columns
-//     [b N / G, (b + 1) N / G) of the G workgroups, so all hold the same number of weight bytes
-//     (to within one column).
-//   * Its columns are cut into groups of 4 and K into windows of 512; a unit is one (group,
-//     window) pair: quad q (16 lanes) of a wavefront reads 256 contiguous bytes of column 4 g + q,
-//     lane r the 32 k = 512 w + 32 r .. + 31 of it. The units, ordered group-major, are dealt to
-//     the W wavefronts in W contiguous runs of equal length (to within one unit).
+//   * One workgroup of W wavefronts per compute unit. Workgroup b owns the 4-column groups
+//     [b NG / G, (b + 1) NG / G) of the NG groups, so all hold the same number of weight bytes
+//     (to within one group).
+//   * A unit is one (group, 512-k window) pair: 16 chunks of 32 k x 4 columns, 1 KB of codes in
+//     one contiguous piece of the packed layout. Lane l of a wavefront reads its 16 bytes at
+//     16 l: column l % 4 of the group, chunk l / 4 of the window. The units of a workgroup,
+//     ordered group-major, are dealt to the W wavefronts in W contiguous runs of equal length
+//     (to within one unit).
 //   * X (all M rows, all of K) is staged once in LDS, so the weight loads are the only global
-//     traffic of the loop. Each 64-byte lane chunk sits in an 80-byte slot: eight consecutive
-//     lanes then read eight different bank groups, and the four 16-byte pieces of a chunk are
-//     immediate offsets of one address.
+//     traffic of the loop. Each 32-k chunk of X sits in an 80-byte slot; the 16 chunks a
+//     wavefront reads at once then fall into different bank groups, and each is broadcast to the
+//     4 lanes of its column quad.
 //   * A wavefront keeps D units in flight (a ring of D register sets filled through buffer loads
 //     that return zeros past the end), accumulates its run in registers, and when the group
-//     changes sums the 16 lanes of each quad and writes the column partial to an LDS slot. A
+//     changes sums the 16 lanes of each column and writes the column partial to an LDS slot. A
 //     group is split between at most L.slots consecutive wavefronts; the slots are added in
 //     wavefront order (= k order) at the end, times the tensor scale g. Results are reproducible.
-//   * FAST (K % 512 == 0, hence the wide layout) needs no per-lane K test: every load offset is a
-//     per-lane constant plus one wavefront-uniform term. Otherwise each lane checks its k range.
+//   * FAST (K % 512 == 0) needs no per-lane K test; otherwise a lane whose chunk is past the
+//     last one reads zeros instead of the next group's bytes.
 #pragma once
 
 #include "device.h"
@@ -50,39 +51,38 @@ __host__ __device__ inline int stream_owner(long long u, int W, long long units)
     return (int)(((u + 1) * W - 1) / units);
 }
 
-template <int MR, int W, int D, bool FAST, bool NARROW>
+template <int MR, int W, int D, bool FAST>
 __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, StreamLayout L)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     float *part = reinterpret_cast<float *>(lds + L.x_bytes);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
-    const int r = lane & 15;
-    const int q = lane >> 4;
+    const int col = lane & 3;   // column within the group
+    const int j = lane >> 2;    // chunk within the window
     const int K = a.K;
     const int N = a.N;
+    const int CH = num_chunks(K);
+    const int NG = num_groups(N);
     const int G = gridDim.x;
-    const int c0 = (int)(((long long)blockIdx.x * N) / G);
-    const int ncols = (int)(((long long)(blockIdx.x + 1) * N) / G) - c0;
-    const int ngroups = (ncols + 3) / 4;
+    const int g0 = (int)(((long long)blockIdx.x * NG) / G);
+    const int ngroups = (int)(((long long)(blockIdx.x + 1) * NG) / G) - g0;
+    const int c0 = kGroupCols * g0;
+    const int ncols = min(N - c0, kGroupCols * ngroups);
     const int nwin = L.nwin;
     const long long units = (long long)ngroups * nwin;
     const int u0 = (int)(((long long)wave * units) / W);
     const int u1 = (int)(((long long)(wave + 1) * units) / W);
 
-    const rsrc_t rq = make_rsrc(a.Wq + (size_t)c0 * (size_t)(K / 2),
-                                (uint32_t)ncols * (uint32_t)(K / 2));
-    uint32_t sbias;
-    const rsrc_t rs = scale_rsrc(a.Ws, (size_t)c0, ncols, K, &sbias);
-    const uint32_t qrow = (uint32_t)q * (uint32_t)(K / 2);           // this quad's column,
-    const uint32_t srow = sbias + (uint32_t)q * (uint32_t)(K / 16);  // relative to group 0
-    const uint32_t gq = 4u * (uint32_t)(K / 2);                       // bytes per group
-    const uint32_t gs = 4u * (uint32_t)(K / 16);
-    // FAST: the lane's offsets within a window are constants; the scale word holds lanes 2 p and
-    // 2 p + 1 (K % 64 == 0 makes srow a multiple of 4 and sbias zero).
-    const uint32_t vq = qrow + 16u * (uint32_t)r;
-    const uint32_t vs = srow + 4u * (uint32_t)(r >> 1);
-    const uint32_t sshift = 16u * (uint32_t)(r & 1);
+    const uint32_t gq = (uint32_t)CH * kChunkCodeBytes;    // code bytes per group
+    const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;   // scale bytes per group
+    const rsrc_t rq = make_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
+    const rsrc_t rs = make_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
+    // Within a unit: the lane's 16 code bytes, and the 4-byte word holding its 2 scale bytes
+    // (at 2 lane) together with those of lane ^ 1.
+    const uint32_t vq = 16u * (uint32_t)lane;
+    const uint32_t vs = 4u * (uint32_t)(lane >> 1);
+    const uint32_t sshift = 16u * (uint32_t)(lane & 1);
 
     // Prefetch cursor: unit up = (gp, wp).
     int up = u0;
@@ -90,21 +90,16 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     int wp = u0 - gp * nwin;
     auto load_next = [&]() -> Chunk {
         Chunk c;
-        const bool live = up < u1;
-        if (FAST) {
-            const uint32_t uq = live ? (uint32_t)gp * gq + (uint32_t)wp * 256u : kOutOfRange;
-            const uint32_t us = live ? (uint32_t)gp * gs + (uint32_t)wp * 32u : kOutOfRange;
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, vq + uq, 0, kAuxStream);
-            c.code[0] = v[0];
-            c.code[1] = v[1];
-            c.code[2] = v[2];
-            c.code[3] = v[3];
-            c.scale = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + us, 0, kAuxStream);
-        } else {
-            const int kc = live ? wp * kStreamWindow + 32 * r : K;  // K: zeros
-            c = load_chunk<NARROW>(rq, rs, qrow + (uint32_t)gp * gq, srow + (uint32_t)gp * gs,
-                                   kc, K);
-        }
+        const bool live = up < u1 && (FAST || kStreamWindow / kChunkK * wp + j < CH);
+        const uint32_t uq = (uint32_t)gp * gq + (uint32_t)wp * (16u * kChunkCodeBytes);
+        const uint32_t us = (uint32_t)gp * gs + (uint32_t)wp * (16u * kChunkScaleBytes);
+        const u32x4_t v =
+            __builtin_amdgcn_raw_buffer_load_b128(rq, off_if(live, vq + uq), 0, kAuxStream);
+        c.code[0] = v[0];
+        c.code[1] = v[1];
+        c.code[2] = v[2];
+        c.code[3] = v[3];
+        c.scale = __builtin_amdgcn_raw_buffer_load_b32(rs, off_if(live, vs + us), 0, kAuxStream);
         up++;
         if (++wp == nwin) {
             wp = 0;
@@ -170,19 +165,15 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     int gc = u0 / nwin;
     int wc = u0 - gc * nwin;
     int slot = (gc * nwin >= u0) ? 0 : wave - stream_owner((long long)gc * nwin, W, units);
-    const uint32_t xlane = (uint32_t)r * kStreamSlot;
+    const uint32_t xlane = (uint32_t)j * kStreamSlot;
 
     auto flush = [&]() {
 #pragma unroll
         for (int m = 0; m < MR; m++) {
-            float v = acc[m];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 8);
+            const float v = sum_lanes_stride4(acc[m]);
             acc[m] = 0.0f;
-            if (r == 0)
-                part[((gc * L.slots + slot) * MR + m) * 4 + q] = v;
+            if (j == 0)
+                part[((gc * L.slots + slot) * MR + m) * 4 + col] = v;
         }
     };
 
@@ -193,10 +184,7 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
             if (u + s < u1) {
                 const Chunk &c = ring[s];
-                const uint32_t sc =
-                    FAST ? (c.scale >> sshift)
-                         : scale_pair<NARROW>(c.scale, srow + (uint32_t)gc * gs,
-                                              wc * kStreamWindow + 32 * r);
+                const uint32_t sc = c.scale >> sshift;
                 const float s0 = e4m3_to_f32<0>(sc);
                 const float s1 = e4m3_to_f32<1>(sc);
                 bf16x2_t w[16];

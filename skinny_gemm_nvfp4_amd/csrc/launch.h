@@ -1,4 +1,5 @@
-// launch.h -- internal interface between the C ABI (api.cpp) and the kernel launchers.
+// launch.h -- internal interface between the C ABI (api.cpp) and the kernel launchers, and the
+// packed-weight layout shared by the packer and the GEMM kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,30 +9,61 @@ namespace nvfp4 {
 
 struct GemmArgs {
     const uint16_t *X;       // bf16 bits [M][K]
-    const uint8_t *Wq;       // [N][K/2]
-    const uint8_t *Ws;       // [N][K/16]
+    const uint8_t *Wq;       // [NG][CH][4][16]
+    const uint8_t *Ws;       // [NG][CH][4][2]
     const float *gscale;     // [1]
     float *Y;                // [M][N]
     int M, N, K;
 };
 
-enum Path { kPathAuto = 0, kPathDot = 1, kPathMfma = 2, kPathStream = 3, kPathMfmaStream = 4 };
+// Packed layout: 4-column groups, 32-k chunks. One chunk of one group is 4 x 16 code bytes
+// (column-major inside the chunk: column j's 32 codes are bytes 16 j .. 16 j + 15) and 4 x 2
+// scale bytes. Groups are contiguous runs of CH chunks.
+constexpr int kGroupCols = 4;
+constexpr int kChunkK = 32;
+constexpr int kChunkCodeBytes = kGroupCols * 16;   // 64
+constexpr int kChunkScaleBytes = kGroupCols * 2;   // 8
 
-// Largest M the dot-product kernel families are instantiated for.
+__host__ __device__ inline int num_groups(int N) { return (N + kGroupCols - 1) / kGroupCols; }
+__host__ __device__ inline int num_chunks(int K) { return (K + kChunkK - 1) / kChunkK; }
+
+// Byte offset of the 16 code bytes of (column n, chunk c) and of the scale pair of the same.
+__host__ __device__ inline size_t code_offset(int n, int c, int CH)
+{
+    return (((size_t)(n / kGroupCols) * (size_t)CH + (size_t)c) * kGroupCols + (size_t)(n % 4)) *
+           16u;
+}
+__host__ __device__ inline size_t scale_offset(int n, int c, int CH)
+{
+    return (((size_t)(n / kGroupCols) * (size_t)CH + (size_t)c) * kGroupCols + (size_t)(n % 4)) *
+           2u;
+}
+
+inline uint64_t codes_bytes(int N, int K)
+{
+    return (uint64_t)num_groups(N) * (uint64_t)num_chunks(K) * kChunkCodeBytes;
+}
+inline uint64_t scales_bytes(int N, int K)
+{
+    return (uint64_t)num_groups(N) * (uint64_t)num_chunks(K) * kChunkScaleBytes;
+}
+
+enum Path { kPathAuto = 0, kPathDot = 1, kPathMfma = 2 };
+
+// Largest M the dot-product kernel is instantiated for.
 constexpr int kDotMaxM = 8;
 
 // Largest K: keeps every per-workgroup byte range of the buffer loads below 2^31.
 constexpr int kMaxK = 1 << 22;
 
 // Resolves path/split (0 = automatic) for this shape. Returns false for an unsupported pair.
-// A persistent dot-product request whose X does not fit in LDS becomes the tiled dot-product
-// path; a persistent matrix-core request with K % 128 != 0 becomes the tiled matrix-core path.
+// A dot-product request whose X does not fit in LDS becomes the matrix-core path.
 bool choose_config(int M, int N, int K, int *path, int *split);
 
 // Launch the GEMM with a resolved path and split. Returns the hipError_t of the launch.
 hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t stream);
 
-// Launch the three-kernel pack sequence (amax, tensor scale, quantise) on the stream.
+// Launch the pack sequence (clear, amax, tensor scale, quantise) on the stream.
 hipError_t launch_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Ws, float *gscale,
                        hipStream_t stream);
 

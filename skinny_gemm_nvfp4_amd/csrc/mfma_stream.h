@@ -1,0 +1,210 @@
+// mfma_stream.h -- persistent NVFP4 x bf16 matrix-core kernel, one 16-row block of X per workgroup.
+//
+// Speculative verification of one request runs the target's projections on 1 + 15 drafted
+// tokens at once ("SparkInfer" README, speculative decoding sections), so X has 16 rows: one
+// v_mfma_f32_16x16x32_bf16 row tile. The kernel is bound by the weight stream, like decode. More
+// rows run as more 16-row blocks (blockIdx.y).
+//
+// Work split
+//   * One workgroup of W wavefronts per compute unit and row block; workgroup b owns the 4-column
+//     groups [b NG / G, (b + 1) NG / G) (equal weight bytes per compute unit). Four consecutive
+//     groups form a tile of 16 columns; the tiles are taken TC at a time.
+//   * K is cut into windows of 128 (4 chunks of 32); wavefront w owns the windows w, w + W, ...
+//     and, for those windows, every tile of the chunk.
+//   * Lane l = 16 q + r holds column r of the tile: it loads the 16 code bytes of chunk q of the
+//     window of that column (group r / 4, column r % 4 of the group). The 64 lanes together read
+//     4 pieces of 256 contiguous bytes of the packed layout, i.e. whole cache lines. MFMA k-slot
+//     8 q + e of step d (d = 0..3) is k = 128 w + 32 q + 8 d + e, so dword d of the lane's codes
+//     is its B fragment of step d, with the scale of block 2 (4 w + q) + d / 2.
+//   * X: the wavefront reads the 16 rows x 128 k of its window with contiguous 16-byte loads
+//     (four 1 KB pieces), stores them in its own LDS buffer (rows padded to 272 bytes) and reads
+//     its A fragments there: lane (r, q) takes row r at k = 32 q + 8 d. The loads of the next
+//     window (X first, then weights) are in flight while the current one is multiplied.
+//   * B = e2m1 * s decoded to bf16 (exact); the sum over k does not depend on the slot order, so
+//     this is the plain product.
+//   * The W partial tiles are summed through LDS in wavefront order and scaled by g once.
+//     Results are reproducible.
+//   * FAST (K % 128 == 0) needs no per-lane K test; otherwise lanes past the last chunk read zeros.
+#pragma once
+
+#include "device.h"
+#include "launch.h"
+
+namespace nvfp4 {
+
+constexpr int kMfmaWindow = 128;
+constexpr int kXRowBytes = 272;                   // 256 bytes of a 128-k row + 16 of padding
+constexpr int kXBufBytes = 16 * kXRowBytes;       // one window of 16 rows
+
+// LDS bytes of mfma_stream_kernel<TC, W>: two X buffers per wavefront, reused at the end for one
+// 16 x 16 fp32 partial per wavefront and tile.
+constexpr int mfma_stream_lds_bytes(int tc, int w)
+{
+    return (2 * kXBufBytes * w > w * tc * 4 * kWave * 4) ? 2 * kXBufBytes * w
+                                                         : w * tc * 4 * kWave * 4;
+}
+
+template <int TC>
+struct MfmaWindow {
+    u32x4_t x[4];      // X pieces in load order: row 4 p + l / 16, k = 8 (l % 16)
+    u32x4_t c[TC];     // the lane's 16 code bytes of each tile
+    uint32_t s[TC];    // the word holding the lane's 2 scale bytes of each tile
+
+    // lq/ls: the lane's code/scale offset within a tile-window at window 0; tq/ts: bytes per
+    // tile; wq/ws: bytes per window; xo: the lane's X offset at window 0.
+    template <bool FAST>
+    __device__ __forceinline__ void load(rsrc_t rq, rsrc_t rs, rsrc_t rx, uint32_t lq,
+                                         uint32_t ls, uint32_t tq, uint32_t ts, uint32_t xo,
+                                         int xk, int w, bool live, int tc0, int ngroups,
+                                         int gr, int q, int CH, int K)
+    {
+#pragma unroll
+        for (int p = 0; p < 4; p++)
+            x[p] = __builtin_amdgcn_raw_buffer_load_b128(
+                rx,
+                off_if(live && kMfmaWindow * w + xk < K,
+                       xo + (uint32_t)p * 4u * (uint32_t)K * 2u + (uint32_t)w * (kMfmaWindow * 2)),
+                0, kAuxNormal);
+        const bool kv = live && (FAST || 4 * w + q < CH);
+#pragma unroll
+        for (int t = 0; t < TC; t++) {
+            const bool v = kv && 4 * (tc0 + t) + gr < ngroups;
+            c[t] = __builtin_amdgcn_raw_buffer_load_b128(
+                rq, off_if(v, lq + (uint32_t)(tc0 + t) * tq + (uint32_t)w * (4u * kChunkCodeBytes)),
+                0, kAuxNormal);
+            s[t] = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, off_if(v, ls + (uint32_t)(tc0 + t) * ts + (uint32_t)w * (4u * kChunkScaleBytes)),
+                0, kAuxNormal);
+        }
+    }
+
+    // X pieces into the wavefront's LDS buffer.
+    __device__ __forceinline__ void stage(uint8_t *buf, int lane) const
+    {
+#pragma unroll
+        for (int p = 0; p < 4; p++)
+            *reinterpret_cast<u32x4_t *>(buf + (4 * p + (lane >> 4)) * kXRowBytes +
+                                         16 * (lane & 15)) = x[p];
+    }
+
+    __device__ __forceinline__ void mul(f32x4_t (&acc)[TC], const uint8_t *buf, int r, int q,
+                                        int nt, uint32_t sshift) const
+    {
+        u32x4_t a[4];
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+            a[d] = *reinterpret_cast<const u32x4_t *>(buf + r * kXRowBytes + 64 * q + 16 * d);
+#pragma unroll
+        for (int t = 0; t < TC; t++) {
+            if (t < nt) {
+                const uint32_t sw = s[t] >> sshift;
+                const float s_lo = e4m3_to_f32<0>(sw);   // k 32 q .. + 15 of the window
+                const float s_hi = e4m3_to_f32<1>(sw);   // k 32 q + 16 .. + 31
+#pragma unroll
+                for (int d = 0; d < 4; d++)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(a[d]), decode8_scaled(c[t][d], d < 2 ? s_lo : s_hi), acc[t], 0,
+                        0, 0);
+            }
+        }
+    }
+};
+
+template <int TC, int W, bool FAST>
+__global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int r = lane & 15;
+    const int q = lane >> 4;
+    const int K = a.K;
+    const int N = a.N;
+    const int CH = num_chunks(K);
+    const int NG = num_groups(N);
+    const int G = gridDim.x;
+    const int g0 = (int)(((long long)blockIdx.x * NG) / G);
+    const int ngroups = (int)(((long long)(blockIdx.x + 1) * NG) / G) - g0;
+    const int c0 = kGroupCols * g0;
+    const int ncols = min(N - c0, kGroupCols * ngroups);
+    const int T = (ngroups + 3) / 4;   // tiles of 16 columns
+    const int m0 = blockIdx.y * 16;
+    const int mrows = min(16, a.M - m0);
+    const int nwin = (CH + 3) / 4;
+
+    const uint32_t gq = (uint32_t)CH * kChunkCodeBytes;
+    const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;
+    const rsrc_t rq = make_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
+    const rsrc_t rs = make_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
+    const rsrc_t rx = make_rsrc(a.X + (size_t)m0 * (size_t)K, (uint32_t)mrows * (uint32_t)K * 2u);
+    const int gr = r >> 2;   // group of the lane's column within the tile
+    const uint32_t lq = (uint32_t)gr * gq + (uint32_t)q * kChunkCodeBytes + (uint32_t)(r & 3) * 16u;
+    const uint32_t ls = (uint32_t)gr * gs + (uint32_t)q * kChunkScaleBytes +
+                        (uint32_t)(r & 2) * 2u;   // word of columns (r & 2), (r & 2) + 1
+    const uint32_t sshift = 16u * (uint32_t)(r & 1);
+    const uint32_t tq = 4u * gq;
+    const uint32_t ts = 4u * gs;
+    const int xk = 8 * r;    // k of the lane's X piece within the window
+    const uint32_t xo = ((uint32_t)(lane >> 4) * (uint32_t)K + (uint32_t)xk) * 2u;
+    uint8_t *xbuf0 = lds + wave * 2 * kXBufBytes;
+    uint8_t *xbuf1 = xbuf0 + kXBufBytes;
+    const float g = *a.gscale;
+
+    for (int tc0 = 0; tc0 < T; tc0 += TC) {
+        const int nt = min(TC, T - tc0);
+        f32x4_t acc[TC];
+#pragma unroll
+        for (int t = 0; t < TC; t++)
+            acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+        MfmaWindow<TC> wa, wb;
+        int w = wave;
+        wa.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w, w < nwin, tc0, ngroups, gr,
+                               q, CH, K);
+        wa.stage(xbuf0, lane);
+        while (w < nwin) {
+            wb.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w + W, w + W < nwin, tc0,
+                                   ngroups, gr, q, CH, K);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
+            wa.mul(acc, xbuf0, r, q, nt, sshift);
+            __builtin_amdgcn_sched_barrier(0);
+            wb.stage(xbuf1, lane);
+            w += W;
+            if (w >= nwin)
+                break;
+            wa.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w + W, w + W < nwin, tc0,
+                                   ngroups, gr, q, CH, K);
+            __builtin_amdgcn_sched_barrier(0);
+            wb.mul(acc, xbuf1, r, q, nt, sshift);
+            __builtin_amdgcn_sched_barrier(0);
+            wa.stage(xbuf0, lane);
+            w += W;
+        }
+
+        // acc[t][e] is the partial Y[m0 + 4 q + e][c0 + 16 (tc0 + t) + r] of this wavefront.
+        __syncthreads();  // every wavefront is done with its X buffers, which red reuses
+        float *red = reinterpret_cast<float *>(lds);   // [W][TC][4][64]
+#pragma unroll
+        for (int t = 0; t < TC; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                red[((wave * TC + t) * 4 + e) * kWave + lane] = acc[t][e];
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nt * 4 * kWave; idx += kWave * W) {
+            const int t = idx / (4 * kWave);
+            const int e = (idx / kWave) % 4;
+            const int ln = idx % kWave;
+            const int row = 4 * (ln >> 4) + e;
+            const int colx = 16 * (tc0 + t) + (ln & 15);
+            if (row < mrows && colx < ncols) {
+                float sum = red[(t * 4 + e) * kWave + ln];
+                for (int v = 1; v < W; v++)
+                    sum += red[((v * TC + t) * 4 + e) * kWave + ln];
+                a.Y[(size_t)(m0 + row) * N + c0 + colx] = sum * g;
+            }
+        }
+        __syncthreads();  // red and the X buffers are reused by the next chunk
+    }
+}
+
+}  // namespace nvfp4

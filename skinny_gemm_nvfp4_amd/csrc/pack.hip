@@ -11,8 +11,10 @@
 //                          non-negative floats the bit order is the numeric order) into *gscale,
 //                          which pack_clear_kernel zeroed first.
 //   2. pack_scale_kernel : *gscale = amax / 2688 (one thread; correctly rounded division).
-//   3. pack_quant_kernel : one thread per (block b, column n); consecutive lanes take consecutive
-//                          n, so the 16 reads of a block are coalesced across the wavefront.
+//   3. pack_quant_kernel : one thread per (block b, column n) of the padded layout (columns up
+//                          to a multiple of 4, blocks up to a multiple of 2); consecutive lanes
+//                          take consecutive n, so the 16 reads of a block are coalesced across
+//                          the wavefront. Padding positions are written as zero bytes.
 #include "device.h"
 #include "launch.h"
 
@@ -82,17 +84,19 @@ __global__ __launch_bounds__(256) void pack_quant_kernel(int K, int N, const flo
                                                          uint8_t *Wq, uint8_t *Ws,
                                                          const float *gscale)
 {
-    const size_t nblocks = (size_t)(K / 16);
+    const int CH = num_chunks(K);
+    const int NP = kGroupCols * num_groups(N);
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= nblocks * (size_t)N)
+    if (idx >= (size_t)(2 * CH) * (size_t)NP)
         return;
-    const int n = (int)(idx % (size_t)N);
-    const size_t b = idx / (size_t)N;
+    const int n = (int)(idx % (size_t)NP);
+    const int b = (int)(idx / (size_t)NP);
+    uint8_t *codes_out = Wq + code_offset(n, b / 2, CH) + 8 * (b & 1);
+    uint8_t *scale_out = Ws + scale_offset(n, b / 2, CH) + (b & 1);
     const float g = *gscale;
-    uint8_t *codes_out = Wq + (size_t)n * (size_t)(K / 2) + 8 * b;
-    uint8_t *scale_out = Ws + (size_t)n * nblocks + b;
 
-    if (g == 0.0f) {  // all-zero or underflowing tensor: every byte 0
+    // Padding (n >= N or k >= K), or an all-zero or underflowing tensor: every byte 0.
+    if (n >= N || 16 * b >= K || g == 0.0f) {
         *reinterpret_cast<uint2 *>(codes_out) = make_uint2(0u, 0u);
         *scale_out = 0;
         return;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(256) void pack_quant_kernel(int K, int N, const flo
     float bmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        w[i] = W[(16 * b + i) * (size_t)N + n];
+        w[i] = W[(16 * (size_t)b + i) * (size_t)N + n];
         const float a = fabsf(w[i]);
         if (a > bmax)
             bmax = a;
@@ -135,7 +139,7 @@ hipError_t launch_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Ws, f
     hipLaunchKernelGGL(pack_amax_kernel, dim3(amax_blocks), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(W), count4, slot);
     hipLaunchKernelGGL(pack_scale_kernel, dim3(1), dim3(1), 0, stream, gscale);
-    const size_t threads = (size_t)(K / 16) * (size_t)N;
+    const size_t threads = (size_t)(2 * num_chunks(K)) * (size_t)(kGroupCols * num_groups(N));
     const size_t qblocks = (threads + 255) / 256;
     hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)qblocks), dim3(256), 0, stream, K, N, W,
                        Wq, Ws, gscale);

@@ -41,7 +41,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"nvfp4_pack", "nvfp4_gemm", "nvfp4_gemm_path", "nvfp4_status_string",
-                          "nvfp4_abi_version"}
+                          "nvfp4_abi_version", "nvfp4_codes_bytes", "nvfp4_scales_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
@@ -51,7 +51,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert nv.abi_version() == 1
+    assert nv.abi_version() == 2
     for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH):
         assert nv.status_string(st)
     assert nv.status_string(99) == "unknown status"
@@ -83,18 +83,15 @@ def test_gemm_rejects_misaligned_pointers(lib):
 
 def test_gemm_path_rejects_bad_options(lib):
     ptrs = [A16, A16B, A16C, A16D, A16E]
-    assert nv.nvfp4_gemm_path(5, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_gemm_path(3, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
     assert nv.nvfp4_gemm_path(-1, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
-    for split in (3, 32, -1):
+    for split in (1, 2, 3, 32, -1):
         assert nv.nvfp4_gemm_path(0, split, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
-    # the dot-product families cover M <= 8 only
+    # the dot-product kernel covers M <= 8 only
     assert nv.nvfp4_gemm_path(nv.PATH_DOT, 0, 9, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
-    assert nv.nvfp4_gemm_path(nv.PATH_STREAM, 0, 9, 16, 256, *ptrs, None) == \
+    # the matrix-core kernel runs 4 or 8 waves per workgroup
+    assert nv.nvfp4_gemm_path(nv.PATH_MFMA, 16, 16, 16, 256, *ptrs, None) == \
         nv.ERROR_INVALID_VALUE
-    # the persistent matrix-core kernel runs 4 or 8 waves per workgroup
-    for split in (1, 2, 16):
-        assert nv.nvfp4_gemm_path(nv.PATH_MFMA_STREAM, split, 16, 16, 256, *ptrs, None) == \
-            nv.ERROR_INVALID_VALUE
 
 
 def test_gemm_rejects_overflowing_sizes(lib):
@@ -122,10 +119,21 @@ def test_pack_rejects_bad_arguments(lib):
 def test_tensor_helpers_require_device_tensors(lib):
     import torch
     with pytest.raises(ValueError):
-        nv.gemm(torch.zeros(1, 32, dtype=torch.bfloat16), torch.zeros(4, 16, dtype=torch.uint8),
-                torch.zeros(4, 2, dtype=torch.uint8), torch.ones(1))
+        nv.gemm(torch.zeros(1, 32, dtype=torch.bfloat16), torch.zeros(1, 1, 4, 16, dtype=torch.uint8),
+                torch.zeros(1, 1, 4, 2, dtype=torch.uint8), torch.ones(1), 4)
     with pytest.raises(ValueError):
         nv.pack(torch.zeros(32, 4))
+
+
+def test_packed_sizes(lib):
+    """Bytes of the packed arrays: 64 resp. 8 per (4-column group, 32-k chunk), padded up."""
+    for N, K in [(1, 16), (4, 32), (5, 48), (7168, 5120), (5120, 17408), (151936, 5120)]:
+        groups, chunks = -(-N // 4), -(-K // 32)
+        assert nv.nvfp4_codes_bytes(N, K) == 64 * groups * chunks
+        assert nv.nvfp4_scales_bytes(N, K) == 8 * groups * chunks
+        assert nv.codes_shape(N, K) == (groups, chunks, 4, 16)
+        assert nv.scales_shape(N, K) == (groups, chunks, 4, 2)
+    assert nv.nvfp4_codes_bytes(0, 32) == 0 and nv.nvfp4_scales_bytes(4, 0) == 0
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

@@ -15,11 +15,9 @@ from parity import (FINITE_SCALES, check_close, gpu_gemm, random_case, say, to_d
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [(nv.PATH_STREAM, 4), (nv.PATH_STREAM, 8), (nv.PATH_STREAM, 16),
-         (nv.PATH_DOT, 1), (nv.PATH_DOT, 2), (nv.PATH_DOT, 4), (nv.PATH_DOT, 8),
-         (nv.PATH_MFMA, 1), (nv.PATH_MFMA, 2), (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
-         (nv.PATH_MFMA_STREAM, 4), (nv.PATH_MFMA_STREAM, 8), (nv.PATH_AUTO, 0)]
-VALU_PATHS = (nv.PATH_DOT, nv.PATH_STREAM)   # dot-product families: M <= 8
+PATHS = [(nv.PATH_DOT, 4), (nv.PATH_DOT, 8), (nv.PATH_DOT, 16),
+         (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8), (nv.PATH_AUTO, 0)]
+VALU_PATHS = (nv.PATH_DOT,)   # the dot-product kernel: M <= 8
 SMALL_M = [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 130]
 SMALL_N = [1, 15, 16, 17, 65]
 SMALL_K = [16, 48, 256, 272, 528, 1024]
@@ -75,7 +73,7 @@ def test_one_hot_rows_give_dequantised_weights(device, K):
     X = torch.zeros(M, K, dtype=torch.bfloat16)
     X[torch.arange(M), ks] = 1.0
     expect = Wd[ks.numpy(), :].astype(np.float32).astype(np.float64)
-    for path, split in _paths_for(M) + [(nv.PATH_DOT, 4), (nv.PATH_STREAM, 16)]:
+    for path, split in _paths_for(M):
         if path in VALU_PATHS and M > 8:
             Xs, ex = X[:8], expect[:8]
         else:
@@ -122,12 +120,12 @@ def test_deterministic(device):
         assert np.array_equal(a, b), f"path {path} split {split} not reproducible"
 
 
-@pytest.mark.parametrize("path,split", [(nv.PATH_MFMA_STREAM, 4), (nv.PATH_MFMA_STREAM, 8),
-                                        (nv.PATH_STREAM, 16)])
+@pytest.mark.parametrize("path,split", [(nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
+                                        (nv.PATH_DOT, 16)])
 def test_many_columns_per_workgroup(device, path, split):
     """Enough columns that a persistent workgroup owns more column tiles than one pass takes
     (several chunks per workgroup), with a ragged last tile and a ragged row block."""
-    M = 8 if path == nv.PATH_STREAM else 19
+    M = 8 if path == nv.PATH_DOT else 19
     N, K = 256 * 16 * 11 + 5, 256
     X, Wq, Ws, g = random_case(41, M, N, K, FINITE_SCALES)
     Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
