@@ -120,8 +120,10 @@ typedef enum {
     NVFP4_PATH_AUTO = 0,  /* what nvfp4_gemm does */
     NVFP4_PATH_DOT = 1,   /* VALU: E2M1->bf16 decode, v_dot2_f32_bf16 against X staged in LDS,
                              fp32 partial * s; M <= 8 */
-    NVFP4_PATH_MFMA = 2   /* matrix cores: E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 on
-                             16-row blocks of X; any M */
+    NVFP4_PATH_MFMA = 2,  /* matrix cores: E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 on
+                             one 16-row block of X per workgroup; any M */
+    NVFP4_PATH_BATCH = 3  /* matrix cores, every weight decoded once for up to 128 rows of X
+                             (X shared through LDS); any M, meant for 16 < M <= 128 */
 } nvfp4_path_t;
 
 /*
@@ -132,6 +134,7 @@ typedef enum {
  *   NVFP4_PATH_DOT: 4, 8 or 16; M <= 8, else NVFP4_ERROR_INVALID_VALUE. If X does not fit in
  *     LDS (M * K too large) the call runs NVFP4_PATH_MFMA with its own split instead.
  *   NVFP4_PATH_MFMA: 4 or 8.
+ *   NVFP4_PATH_BATCH: 4 (the only size; 0 picks it too).
  * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
 nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,

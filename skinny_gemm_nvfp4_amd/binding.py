@@ -22,6 +22,7 @@ ERROR_LAUNCH = 3
 PATH_AUTO = 0
 PATH_DOT = 1
 PATH_MFMA = 2
+PATH_BATCH = 3
 
 _lib = None
 

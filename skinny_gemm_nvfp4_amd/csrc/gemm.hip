@@ -5,7 +5,9 @@
 //   * gemv_stream.h (NVFP4_PATH_DOT): dot products against X staged in LDS. Decode (M = 1) and
 //     the smallest M.
 //   * mfma_stream.h (NVFP4_PATH_MFMA): bf16 matrix cores on 16-row blocks of X (speculative
-//     verification), and every shape whose X does not fit in LDS.
+//     verification of one request), and every shape whose X does not fit in LDS.
+//   * mfma_batch.h (NVFP4_PATH_BATCH): bf16 matrix cores, each weight decoded once for up to 128
+//     rows of X (verification of several requests together).
 #include <algorithm>
 #include <atomic>
 #include <mutex>
@@ -14,6 +16,7 @@
 
 #include "gemv_stream.h"
 #include "launch.h"
+#include "mfma_batch.h"
 #include "mfma_stream.h"
 
 namespace nvfp4 {
@@ -57,6 +60,17 @@ const int kMfmaTiles[6] = {1, 2, 3, 4, 6, 9};
             NVFP4_MFMA_WAVES(4, FAST), NVFP4_MFMA_WAVES(6, FAST), NVFP4_MFMA_WAVES(9, FAST) \
     }
 const KernelFn kMfma[2][6][2] = {NVFP4_MFMA_TABLE(false), NVFP4_MFMA_TABLE(true)};
+
+// ---- batch kernels: 4 tile lanes (one wavefront per SIMD), TCW = 1..3 tiles each per pass,
+// loads 2 windows ahead ----
+constexpr int kBatchRing = 3;
+const KernelFn kBatch[3] = {&mfma_batch_kernel<1, 4, kBatchRing>,
+                            &mfma_batch_kernel<2, 4, kBatchRing>,
+                            &mfma_batch_kernel<3, 4, kBatchRing>};
+const int kBatchLds[3] = {mfma_batch_lds_bytes(1, 4, kBatchRing),
+                          mfma_batch_lds_bytes(2, 4, kBatchRing),
+                          mfma_batch_lds_bytes(3, 4, kBatchRing)};
+constexpr int kBatchWaves = 4;
 
 int wave_index(int waves)
 {
@@ -187,12 +201,37 @@ int mfma_default_waves(int N, int K)
     return kMfmaTiles[P.tc_index] >= 6 ? 4 : 8;
 }
 
+// Batch kernel for this shape, its LDS bytes and grid; false if a workgroup's bytes overflow.
+// Only on request (NVFP4_PATH_BATCH): its loads still run about one window ahead, so
+// nvfp4_gemm keeps the 16-row kernel for every M.
+bool batch_plan(int N, int K, KernelFn *fn, int *lds, int *grid)
+{
+    const int G = group_grid(N);
+    if (!bytes_fit(N, K, G))
+        return false;
+    const int gmax = (num_groups(N) + G - 1) / G;
+    const int tiles = (gmax + 3) / 4;
+    const int i = std::min(3, (tiles + kBatchWaves - 1) / kBatchWaves) - 1;
+    *fn = kBatch[i];
+    *lds = kBatchLds[i];
+    *grid = G;
+    return *lds <= kMaxLds;
+}
+
 }  // namespace
 
 bool choose_config(int M, int N, int K, int *path, int *split)
 {
     if (*path == kPathAuto)
         *path = (M <= 4) ? kPathDot : kPathMfma;
+    if (*path == kPathBatch) {
+        if (*split != 0 && *split != kBatchWaves)
+            return false;
+        *split = kBatchWaves;
+        KernelFn fn;
+        int lds, grid;
+        return batch_plan(N, K, &fn, &lds, &grid);
+    }
     if (*path == kPathDot) {
         if (M > kDotMaxM)
             return false;
@@ -232,6 +271,19 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
         if (e != hipSuccess)
             return e;
         hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * split), lds, stream, a, L);
+        return hipGetLastError();
+    }
+    if (path == kPathBatch) {
+        KernelFn fn;
+        int lds, grid;
+        if (!batch_plan(a.N, a.K, &fn, &lds, &grid))
+            return hipErrorInvalidValue;
+        const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), lds);
+        if (e != hipSuccess)
+            return e;
+        const unsigned slabs = (unsigned)((a.M + 16 * kBatchMaxBlocks - 1) / (16 * kBatchMaxBlocks));
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid, slabs), dim3(kWave * kBatchWaves), lds,
+                           stream, a);
         return hipGetLastError();
     }
     if (path != kPathMfma)

@@ -83,7 +83,7 @@ def test_gemm_rejects_misaligned_pointers(lib):
 
 def test_gemm_path_rejects_bad_options(lib):
     ptrs = [A16, A16B, A16C, A16D, A16E]
-    assert nv.nvfp4_gemm_path(3, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_gemm_path(4, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
     assert nv.nvfp4_gemm_path(-1, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
     for split in (1, 2, 3, 32, -1):
         assert nv.nvfp4_gemm_path(0, split, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
@@ -91,6 +91,9 @@ def test_gemm_path_rejects_bad_options(lib):
     assert nv.nvfp4_gemm_path(nv.PATH_DOT, 0, 9, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
     # the matrix-core kernel runs 4 or 8 waves per workgroup
     assert nv.nvfp4_gemm_path(nv.PATH_MFMA, 16, 16, 16, 256, *ptrs, None) == \
+        nv.ERROR_INVALID_VALUE
+    # the batch kernel runs 4 waves per workgroup
+    assert nv.nvfp4_gemm_path(nv.PATH_BATCH, 8, 128, 16, 256, *ptrs, None) == \
         nv.ERROR_INVALID_VALUE
 
 
