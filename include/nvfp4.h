@@ -113,28 +113,31 @@ nvfp4_status_t nvfp4_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Ws
 nvfp4_status_t nvfp4_gemm(int M, int N, int K, const uint16_t *X, const uint8_t *Wq,
                           const uint8_t *Wscale, const float *gscale, float *Y, void *stream);
 
-/* Kernel families nvfp4_gemm chooses between (for nvfp4_gemm_path). Both are persistent: one
- * workgroup per compute unit (and per 16-row block of X for the matrix-core kernel), each with an
- * equal share of the 4-column groups. */
+/* Kernel families nvfp4_gemm chooses between (for nvfp4_gemm_path). All are persistent: one
+ * workgroup per compute unit (and per 16-row block of X for NVFP4_PATH_MFMA), each with an equal
+ * share of the 4-column groups. nvfp4_gemm takes DOT for M <= 4, MFMA for M <= 16 and BATCH
+ * above. */
 typedef enum {
     NVFP4_PATH_AUTO = 0,  /* what nvfp4_gemm does */
     NVFP4_PATH_DOT = 1,   /* VALU: E2M1->bf16 decode, v_dot2_f32_bf16 against X staged in LDS,
                              fp32 partial * s; M <= 8 */
     NVFP4_PATH_MFMA = 2,  /* matrix cores: E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 on
                              one 16-row block of X per workgroup; any M */
-    NVFP4_PATH_BATCH = 3  /* matrix cores, every weight decoded once for up to 128 rows of X
-                             (X shared through LDS); any M, meant for 16 < M <= 128 */
+    NVFP4_PATH_BATCH = 3  /* matrix cores, every weight decoded once per 128-row slab of X:
+                             loader wavefronts stage X and the weights in LDS, four consumer
+                             wavefronts decode and multiply; any M, meant for M > 16 */
 } nvfp4_path_t;
 
 /*
  * nvfp4_gemm_path -- nvfp4_gemm with the kernel family forced, for testing and tuning.
  *
  * Same operation, arguments, rules and results as nvfp4_gemm. `path` is an nvfp4_path_t.
- * `split` is the number of wavefronts of each workgroup (0 picks it like nvfp4_gemm):
- *   NVFP4_PATH_DOT: 4, 8 or 16; M <= 8, else NVFP4_ERROR_INVALID_VALUE. If X does not fit in
- *     LDS (M * K too large) the call runs NVFP4_PATH_MFMA with its own split instead.
- *   NVFP4_PATH_MFMA: 4 or 8.
- *   NVFP4_PATH_BATCH: 4 (the only size; 0 picks it too).
+ * `split` tunes the kernel (0 picks it like nvfp4_gemm):
+ *   NVFP4_PATH_DOT: wavefronts per workgroup, 4, 8 or 16; M <= 8, else NVFP4_ERROR_INVALID_VALUE.
+ *     If X does not fit in LDS (M * K too large) the call runs NVFP4_PATH_MFMA with its own split.
+ *   NVFP4_PATH_MFMA: wavefronts per workgroup, 4 or 8.
+ *   NVFP4_PATH_BATCH: 1, 2 or 4, the number of consumer wavefronts that share the K steps of one
+ *     column tile (4 / split tiles are processed side by side).
  * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
 nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,

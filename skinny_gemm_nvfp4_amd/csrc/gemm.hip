@@ -61,16 +61,35 @@ const int kMfmaTiles[6] = {1, 2, 3, 4, 6, 9};
     }
 const KernelFn kMfma[2][6][2] = {NVFP4_MFMA_TABLE(false), NVFP4_MFMA_TABLE(true)};
 
-// ---- batch kernels: 4 tile lanes (one wavefront per SIMD), TCW = 1..3 tiles each per pass,
-// loads 2 windows ahead ----
-constexpr int kBatchRing = 3;
-const KernelFn kBatch[3] = {&mfma_batch_kernel<1, 4, kBatchRing>,
-                            &mfma_batch_kernel<2, 4, kBatchRing>,
-                            &mfma_batch_kernel<3, 4, kBatchRing>};
-const int kBatchLds[3] = {mfma_batch_lds_bytes(1, 4, kBatchRing),
-                          mfma_batch_lds_bytes(2, 4, kBatchRing),
-                          mfma_batch_lds_bytes(3, 4, kBatchRing)};
-constexpr int kBatchWaves = 4;
+// ---- batch kernels: [TCW - 1][MB index: 1, 2, 4, 8 row blocks][KS index: 1, 2, 4] ----
+#define NVFP4_BATCH_KS(TCW, MB)                                                            \
+    {                                                                                      \
+        &mfma_batch_kernel<TCW, MB, 1>, &mfma_batch_kernel<TCW, MB, 2>,                    \
+            &mfma_batch_kernel<TCW, MB, 4>                                                 \
+    }
+#define NVFP4_BATCH_MB(TCW)                                                                \
+    {                                                                                      \
+        NVFP4_BATCH_KS(TCW, 1), NVFP4_BATCH_KS(TCW, 2), NVFP4_BATCH_KS(TCW, 4),           \
+            NVFP4_BATCH_KS(TCW, 8)                                                         \
+    }
+const KernelFn kBatch[3][4][3] = {NVFP4_BATCH_MB(1), NVFP4_BATCH_MB(2), NVFP4_BATCH_MB(3)};
+
+template <int TCW, int MB, int KS>
+constexpr int batch_lds()
+{
+    return BatchShape<TCW, MB, KS>::LDS;
+}
+#define NVFP4_BATCH_LDS_KS(TCW, MB)                                                        \
+    {                                                                                      \
+        batch_lds<TCW, MB, 1>(), batch_lds<TCW, MB, 2>(), batch_lds<TCW, MB, 4>()          \
+    }
+#define NVFP4_BATCH_LDS_MB(TCW)                                                            \
+    {                                                                                      \
+        NVFP4_BATCH_LDS_KS(TCW, 1), NVFP4_BATCH_LDS_KS(TCW, 2), NVFP4_BATCH_LDS_KS(TCW, 4), \
+            NVFP4_BATCH_LDS_KS(TCW, 8)                                                     \
+    }
+constexpr int kBatchLds[3][4][3] = {NVFP4_BATCH_LDS_MB(1), NVFP4_BATCH_LDS_MB(2),
+                                    NVFP4_BATCH_LDS_MB(3)};
 
 int wave_index(int waves)
 {
@@ -201,36 +220,104 @@ int mfma_default_waves(int N, int K)
     return kMfmaTiles[P.tc_index] >= 6 ? 4 : 8;
 }
 
-// Batch kernel for this shape, its LDS bytes and grid; false if a workgroup's bytes overflow.
-// Only on request (NVFP4_PATH_BATCH): its loads still run about one window ahead, so
-// nvfp4_gemm keeps the 16-row kernel for every M.
-bool batch_plan(int N, int K, KernelFn *fn, int *lds, int *grid)
+// Batch kernel for one slab of `rows` <= 128 rows: row blocks MB (1, 2, 4 or 8), tiles per
+// consumer TCW and step split KS (ks_req unless 0), from a cycle estimate per compute unit. A
+// window costs the slowest of: the busiest consumer's MFMAs (16 cycles each) or decode (about 80
+// VALU cycles per tile and step); the X bytes from L2 (64 bytes per cycle); the LDS traffic (128
+// bytes per cycle); the weight bytes at the compute unit's share of HBM (13 bytes per cycle); and
+// the load latency spread over the windows in flight (about 4000 cycles / 4). Every pass also
+// pays one latency to fill the pipeline.
+struct BatchPlan {
+    int tcw, mbi, ksi, mb, grid, lds;
+};
+
+constexpr double kLoadLatency = 4000.0;
+
+bool batch_plan(int rows, int N, int K, int ks_req, BatchPlan *P)
 {
     const int G = group_grid(N);
-    if (!bytes_fit(N, K, G))
+    // The Y descriptor covers rows * N floats with 32-bit offsets.
+    if (!bytes_fit(N, K, G) || (long long)rows * N * 4 >= (1LL << 31))
         return false;
     const int gmax = (num_groups(N) + G - 1) / G;
-    const int tiles = (gmax + 3) / 4;
-    const int i = std::min(3, (tiles + kBatchWaves - 1) / kBatchWaves) - 1;
-    *fn = kBatch[i];
-    *lds = kBatchLds[i];
-    *grid = G;
-    return *lds <= kMaxLds;
+    const int T = (gmax + 3) / 4;
+    const int nwin = (K + kBatchWindow - 1) / kBatchWindow;
+    const int mbi = rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 64 ? 2 : 3;
+    const int MB = 1 << mbi;
+    double best = 0.0;
+    bool found = false;
+    for (int ksi = 0; ksi < 3; ksi++) {
+        const int KS = 1 << ksi;
+        if (ks_req != 0 && KS != ks_req)
+            continue;
+        const int TS = kBatchConsumers / KS;
+        const int NSTEP = 4 / KS;
+        for (int tcw = 1; tcw <= 3; tcw++) {
+            if (kBatchLds[tcw - 1][mbi][ksi] > kMaxLds)
+                continue;
+            const int PT = TS * tcw;
+            double cost = 0.0;
+            for (int t0 = 0; t0 < T; t0 += PT) {
+                const int pt = std::min(PT, T - t0);              // tiles of this pass
+                const int live = std::min(tcw, (pt + TS - 1) / TS);
+                const double mfma = 16.0 * live * MB * NSTEP;
+                const double valu = 80.0 * live * NSTEP;
+                const double x_l2 = 16.0 * MB * kBatchRowBytes / 64.0;
+                const double lds = (16.0 * MB * kBatchRowBytes * (1 + kBatchConsumers / KS) +
+                                    2.0 * pt * (kBatchTileBytes + kWave * 4)) /
+                                   128.0;
+                const double hbm = pt * (kBatchTileBytes + kWave * 4) / 13.0;
+                const double lat = kLoadLatency / (kBatchWRing - 1);
+                const double win = std::max(std::max(std::max(mfma, valu), std::max(x_l2, lds)),
+                                            std::max(hbm, lat));
+                // (plus a tenth of the consumer's own work, which breaks ties toward spreading
+                // it over more consumers)
+                cost += nwin * (win + 0.1 * std::max(mfma, valu)) + kLoadLatency;
+            }
+            if (!found || cost < best - 1e-9) {
+                best = cost;
+                found = true;
+                P->tcw = tcw;
+                P->ksi = ksi;
+            }
+        }
+    }
+    if (!found)
+        return false;
+    P->mbi = mbi;
+    P->mb = MB;
+    P->grid = G;
+    P->lds = kBatchLds[P->tcw - 1][mbi][P->ksi];
+    return true;
+}
+
+// Tiles of 16 columns per workgroup when every compute unit takes an equal share of the groups.
+int tiles_per_workgroup(int N)
+{
+    const int G = group_grid(N);
+    return ((num_groups(N) + G - 1) / G + 3) / 4;
 }
 
 }  // namespace
 
 bool choose_config(int M, int N, int K, int *path, int *split)
 {
+    // Automatic choice (measured on the layer shapes): the dot-product kernel for the smallest M;
+    // the 16-row matrix-core kernel up to M = 16 and, up to M = 48, for narrow shapes (a few
+    // tiles per compute unit), whose weights it reads once per row block; above that the batch
+    // kernel, which decodes each weight once per 128 rows.
     if (*path == kPathAuto)
-        *path = (M <= 4) ? kPathDot : kPathMfma;
+        *path = (M <= 4)                                           ? kPathDot
+                : (M <= 16 || (M <= 48 && tiles_per_workgroup(N) < 6)) ? kPathMfma
+                                                                       : kPathBatch;
     if (*path == kPathBatch) {
-        if (*split != 0 && *split != kBatchWaves)
+        if (*split != 0 && *split != 1 && *split != 2 && *split != 4)
             return false;
-        *split = kBatchWaves;
-        KernelFn fn;
-        int lds, grid;
-        return batch_plan(N, K, &fn, &lds, &grid);
+        BatchPlan P;
+        if (!batch_plan(std::min(M, 16 * kBatchMaxBlocks), N, K, *split, &P))
+            return false;
+        *split = 1 << P.ksi;
+        return true;
     }
     if (*path == kPathDot) {
         if (M > kDotMaxM)
@@ -274,17 +361,28 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
         return hipGetLastError();
     }
     if (path == kPathBatch) {
-        KernelFn fn;
-        int lds, grid;
-        if (!batch_plan(a.N, a.K, &fn, &lds, &grid))
-            return hipErrorInvalidValue;
-        const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), lds);
-        if (e != hipSuccess)
-            return e;
-        const unsigned slabs = (unsigned)((a.M + 16 * kBatchMaxBlocks - 1) / (16 * kBatchMaxBlocks));
-        hipLaunchKernelGGL(fn, dim3((unsigned)grid, slabs), dim3(kWave * kBatchWaves), lds,
-                           stream, a);
-        return hipGetLastError();
+        // Slabs of 128 rows, one launch each (the last one may be smaller).
+        constexpr int kSlab = 16 * kBatchMaxBlocks;
+        for (int m0 = 0; m0 < a.M; m0 += kSlab) {
+            const int rows = std::min(kSlab, a.M - m0);
+            BatchPlan P;
+            if (!batch_plan(rows, a.N, a.K, split, &P))
+                return hipErrorInvalidValue;
+            const KernelFn fn = kBatch[P.tcw - 1][P.mbi][P.ksi];
+            const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), P.lds);
+            if (e != hipSuccess)
+                return e;
+            GemmArgs b = a;
+            b.X = a.X + (size_t)m0 * (size_t)a.K;
+            b.Y = a.Y + (size_t)m0 * (size_t)a.N;
+            b.M = rows;
+            hipLaunchKernelGGL(fn, dim3((unsigned)P.grid), dim3(kWave * kBatchWaves), P.lds,
+                               stream, b);
+            const hipError_t le = hipGetLastError();
+            if (le != hipSuccess)
+                return le;
+        }
+        return hipSuccess;
     }
     if (path != kPathMfma)
         return hipErrorInvalidValue;

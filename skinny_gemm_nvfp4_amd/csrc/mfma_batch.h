@@ -1,102 +1,202 @@
 // mfma_batch.h -- persistent NVFP4 x bf16 matrix-core kernel for up to 128 rows of X at once.
 //
 // Eight requests verifying 16 tokens each put 128 rows through every projection ("SparkInfer"
-// README, speculative decoding sections); at that size the bf16 MFMA work, not the weight stream,
-// bounds the kernel. Every weight is therefore decoded once per workgroup and multiplied against
-// all row blocks of X while it sits in registers.
+// README, speculative decoding sections). At that size the bf16 MFMA work, not the weight stream,
+// bounds the kernel, so every weight is decoded once per workgroup and multiplied against all
+// row blocks of X while it sits in registers.
 //
-// Work split
-//   * One workgroup per compute unit and slab of up to 128 rows (blockIdx.y); workgroup b owns
-//     the 4-column groups [b NG / G, (b + 1) NG / G), i.e. T tiles of 16 columns (4 groups each).
-//   * TW wavefronts, one per SIMD: wavefront w takes the tiles t = w + TW j (at most TCW of them
-//     per pass), for every 128-k window.
-//   * Every global load writes LDS directly (buffer_load ... lds), so nothing waits in registers:
-//       - X: all rows of a window go to one slot of a ring of P windows shared by the workgroup.
-//         Rows are 256 bytes; the 16-byte piece kp of row m sits at slot kp ^ (m & 7), so the
-//         A-fragment reads (lane (r, q): row 16 rb + r, k = 32 q + 8 d) hit distinct banks.
-//       - Weights: a ring of P windows per wavefront: the codes of tile j land lane-major (lane
-//         l = 16 q + r: 16 bytes of column r, chunk q of the window, whole cache lines across
-//         the wavefront), then the words holding the lanes' scale pairs.
-//     Loads retire in issue order, so X and weights travel in one stream, P - 1 windows ahead:
-//     every iteration issues the same number of loads (ranges past the end read zeros), window
-//     it has landed at the fixed wait vmcnt((P - 2) * loads per iteration), and one barrier per
-//     iteration both publishes X and frees the ring slots of the previous window.
-//   * The decoded B fragments of a tile are reused for all row blocks (MB <= 8
-//     v_mfma_f32_16x16x32_bf16 per fragment); Y = acc * g. Results are reproducible.
+// Work split (one workgroup of 8 wavefronts per compute unit; workgroup b owns the 4-column groups
+// [b NG / G, (b + 1) NG / G), i.e. T tiles of 16 columns, for all of K and one slab of at most
+// 16 MB rows of X; the tiles are taken PT = 4 TCW / KS at a time)
+//   * K is cut into windows of 128 (4 chunks of 32). Every window passes through LDS once, in two
+//     buffers, with one barrier per window:
+//       - wavefronts 4 and 5 load X: rows 8 MB p .. 8 MB p + 8 MB - 1 of the window, as 16-byte
+//         pieces, 1 to 3 windows ahead (fewer for more rows). Rows are 256 bytes in LDS; piece
+//         kp of row m sits at slot kp ^ (m & 15), so the 16 rows of an A-fragment read hit 16
+//         different slots.
+//       - wavefronts 6 and 7 load the weights of the pass's tiles, kBatchWRing - 1 windows ahead:
+//         lane l = 16 q + r of a tile takes the 16 code bytes of column r, chunk q (the 64 lanes
+//         read four 256-byte pieces, i.e. whole cache lines) and the word that holds that
+//         column's 2 scale bytes.
+//     Each loader issues one kind of load, so the in-order completion of loads never makes one
+//     stream wait for the other.
+//   * Wavefronts 0..3 are the consumers (one per SIMD) and issue no global loads. Consumer
+//     c = TS ks + ts takes tiles ts, ts + TS, ... of the pass (TS = 4 / KS) and, of each window,
+//     the MFMA steps d = ks, ks + KS, ... Step d of lane (r, q) covers k = 32 q + 8 d .. + 7 of
+//     the window: code dword d is its B fragment, scale byte d / 2 the block scale, and row
+//     16 b + r of X at those k its A fragment of row block b (v_mfma_f32_16x16x32_bf16). Narrow
+//     shapes (few tiles per workgroup) take KS = 2 or 4 so that all four matrix cores work.
+//   * B = e2m1 * s decoded to bf16 (exact). The KS partial sums of a tile are added through LDS
+//     in ks order, then Y = sum * g. Results are reproducible.
 #pragma once
 
 #include "device.h"
 #include "launch.h"
-#include "mfma_stream.h"
 
 namespace nvfp4 {
 
-constexpr int kBatchMaxBlocks = 8;                          // 16-row blocks: M <= 128
-constexpr int kBatchRowBytes = 256;                         // one 128-k row of bf16
-constexpr int kBatchXWinBytes = 16 * kBatchMaxBlocks * kBatchRowBytes;   // 32 KB per window
-constexpr int kBatchTileBytes = kWave * 16 + kWave * 4;     // codes + scale words of a tile
+constexpr int kBatchWindow = 128;
+constexpr int kBatchMaxBlocks = 8;       // 16-row blocks: at most 128 rows per slab
+constexpr int kBatchRowBytes = 256;      // one 128-k row of bf16 in LDS
+constexpr int kBatchConsumers = 4;
+constexpr int kBatchWaves = 8;
+constexpr int kBatchTileBytes = kWave * 16;   // codes of one tile and window
+constexpr int kBatchWRing = 5;           // weight windows held by a weight loader
 
-// Loads per wavefront and iteration: X (1 KB each, the window split over TW wavefronts), then
-// codes and scale words of TCW tiles.
-constexpr int batch_x_loads(int tw)
+template <int TCW, int MB, int KS>
+struct BatchShape {
+    static constexpr int TS = kBatchConsumers / KS;   // tile lanes
+    static constexpr int PT = TS * TCW;               // tiles per pass
+    static constexpr int NWP = (PT + 1) / 2;          // tiles per weight loader
+    static constexpr int NXP = 2 * MB;                // X pieces per lane of an X loader
+    static constexpr int XRING = MB >= 8 ? 2 : MB >= 4 ? 3 : 4;   // X windows per X loader
+    static constexpr int NSTEP = 4 / KS;              // MFMA steps per window and consumer
+    static constexpr int XBUF = 16 * MB * kBatchRowBytes;
+    static constexpr int WBUF = PT * (kBatchTileBytes + kWave * 4);
+    static constexpr int MAIN = 2 * XBUF + 2 * WBUF;
+    static constexpr int RED = (KS - 1) * TS * TCW * MB * kWave * 16;
+    static constexpr int LDS = MAIN > RED ? MAIN : RED;
+};
+
+// Byte position / 4 of code dword d inside a tile's 16 bytes in LDS: the order is d = 0, 2, 1, 3,
+// so that the dwords of steps ks and ks + 2 (KS = 2) are adjacent.
+__host__ __device__ constexpr int batch_dword_pos(int d)
 {
-    return (kBatchXWinBytes / 1024) / tw;
-}
-constexpr int batch_loads(int tcw, int tw)
-{
-    return batch_x_loads(tw) + 2 * tcw;
+    return d == 0 ? 0 : d == 1 ? 2 : d == 2 ? 1 : 3;
 }
 
-// LDS bytes of mfma_batch_kernel<TCW, TW, P>: the X ring, then the weight rings.
-constexpr int mfma_batch_lds_bytes(int tcw, int tw, int p)
+// Barrier for LDS hand-over. It waits for the wavefront's own LDS traffic only, not for its
+// global loads in flight (a fenced __syncthreads would wait for those too).
+__device__ __forceinline__ void batch_barrier()
 {
-    return p * kBatchXWinBytes + tw * p * tcw * kBatchTileBytes;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-// One window: decode the TCW tiles' B fragments step by step and multiply them against the MB
-// row blocks of X in LDS. FULL: all 8 row blocks and all TCW tiles are live, so the A fragments
-// of a step are read together and no guard sits between the MFMAs.
-template <bool FULL, int TCW>
-__device__ __forceinline__ void mul_window(f32x4_t (&acc)[kBatchMaxBlocks][TCW],
-                                           const uint8_t *xb, const u32x4_t (&c)[TCW],
-                                           const uint32_t (&s)[TCW], int MB, int nt, int r, int q,
-                                           uint32_t sshift)
+// The A fragments of step d for all MB row blocks.
+template <int MB>
+__device__ __forceinline__ void batch_read_a(u32x4_t (&av)[MB], const uint8_t *xb, int r, int q,
+                                             int d)
 {
+    const int piece = 4 * q + d;
 #pragma unroll
-    for (int d = 0; d < 4; d++) {
-        bf16x8_t bfrag[TCW];
-#pragma unroll
-        for (int j = 0; j < TCW; j++) {
-            const uint32_t sw = s[j] >> sshift;
-            const float sc = (d < 2) ? e4m3_to_f32<0>(sw) : e4m3_to_f32<1>(sw);
-            bfrag[j] = decode8_scaled(c[j][d], sc);
-        }
-        const int piece = 4 * q + d;
-        u32x4_t av[kBatchMaxBlocks];
-#pragma unroll
-        for (int b = 0; b < kBatchMaxBlocks; b++) {
-            const int row = 16 * b + r;
-            if (FULL || b < MB)
-                av[b] = *reinterpret_cast<const u32x4_t *>(xb + row * kBatchRowBytes +
-                                                           16 * (piece ^ (row & 7)));
-        }
-#pragma unroll
-        for (int b = 0; b < kBatchMaxBlocks; b++)
-#pragma unroll
-            for (int j = 0; j < TCW; j++)
-                if (FULL || (b < MB && j < nt))
-                    acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(av[b]), bfrag[j], acc[b][j], 0, 0, 0);
+    for (int b = 0; b < MB; b++) {
+        const int row = 16 * b + r;
+        av[b] = *reinterpret_cast<const u32x4_t *>(xb + row * kBatchRowBytes +
+                                                   16 * (piece ^ (row & 15)));
     }
 }
 
-template <int TCW, int TW, int P>
-__global__ __launch_bounds__(kWave *TW) void mfma_batch_kernel(GemmArgs a)
+// One window of one consumer with NT live tiles: NSTEP steps of decode + MB x NT MFMAs; the A
+// fragments of the next step are read while the current one multiplies.
+template <int TCW, int MB, int KS, int NT>
+__device__ __forceinline__ void batch_window(f32x4_t (&acc)[MB][TCW], const uint8_t *xb,
+                                             const uint8_t *wb, int ts, int ks, int lane, int r,
+                                             int q, uint32_t sshift)
 {
-    constexpr int XL = batch_x_loads(TW);        // X loads per wavefront per iteration
-    constexpr int LOADS = batch_loads(TCW, TW);  // all loads per wavefront per iteration
-    static_assert(P >= 2 && (P - 2) * LOADS <= 63, "vmcnt counts at most 63 loads");
-    static_assert(XL * TW * 1024 == kBatchXWinBytes, "X loads must tile the window");
+    using S = BatchShape<TCW, MB, KS>;
+    uint32_t code[NT][S::NSTEP];
+    uint32_t sw[NT];
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+        const uint8_t *tb = wb + (ts + S::TS * j) * kBatchTileBytes + lane * 16;
+        if (KS == 1) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(tb);
+#pragma unroll
+            for (int d = 0; d < S::NSTEP; d++)
+                code[j][d] = v[batch_dword_pos(d)];
+        } else if (KS == 2) {
+            const u32x2_t v = *reinterpret_cast<const u32x2_t *>(tb + 8 * ks);
+            code[j][0] = v[0];
+            code[j][S::NSTEP - 1] = v[1];
+        } else {
+            code[j][0] = *reinterpret_cast<const uint32_t *>(
+                tb + 4 * (ks == 0 ? 0 : ks == 1 ? 2 : ks == 2 ? 1 : 3));
+        }
+        sw[j] = *reinterpret_cast<const uint32_t *>(wb + S::PT * kBatchTileBytes +
+                                                    (ts + S::TS * j) * (kWave * 4) + lane * 4) >>
+                sshift;
+    }
+    u32x4_t av[2][MB];
+    batch_read_a<MB>(av[0], xb, r, q, ks);
+#pragma unroll
+    for (int i = 0; i < S::NSTEP; i++) {
+        const int d = ks + KS * i;
+        if (i + 1 < S::NSTEP)
+            batch_read_a<MB>(av[(i + 1) & 1], xb, r, q, d + KS);
+        bf16x8_t bfrag[NT];
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            // Steps 0 and 1 lie in the chunk's first block of 16 k, steps 2 and 3 in the second.
+            const float sc = (d < 2) ? e4m3_to_f32<0>(sw[j]) : e4m3_to_f32<1>(sw[j]);
+            bfrag[j] = decode8_scaled(code[j][i], sc);
+        }
+#pragma unroll
+        for (int b = 0; b < MB; b++)
+#pragma unroll
+            for (int j = 0; j < NT; j++)
+                acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i & 1][b]),
+                                                                    bfrag[j], acc[b][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// All windows of one pass for a consumer with NT live tiles (NT = 0: barriers only).
+template <int TCW, int MB, int KS, int NT>
+__device__ __forceinline__ void batch_consume(f32x4_t (&acc)[MB][TCW], const uint8_t *lds,
+                                              int nwin, int ts, int ks, int lane, int r, int q,
+                                              uint32_t sshift)
+{
+    using S = BatchShape<TCW, MB, KS>;
+    for (int it = 0; it < nwin; it++) {
+        batch_barrier();   // window it is in buffer it & 1
+        const int buf = it & 1;
+        if constexpr (NT > 0)
+            batch_window<TCW, MB, KS, NT>(acc, lds + buf * S::XBUF,
+                                          lds + 2 * S::XBUF + buf * S::WBUF, ts, ks, lane, r, q,
+                                          sshift);
+    }
+}
+
+// Loader pipeline shared by both kinds of loader: D - 1 windows in flight; window it is stored to
+// buffer it & 1 and published by the barrier of window it.
+template <int D, typename Win, typename Load, typename Store>
+__device__ __forceinline__ void batch_produce(int nwin, Load &load, Store &store)
+{
+    Win ring[D];
+#pragma unroll
+    for (int u = 0; u < D - 1; u++)
+        load(u, ring[u]);
+    for (int it0 = 0; it0 < nwin; it0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; u++) {
+            const int it = it0 + u;
+            if (it < nwin) {
+                load(it + D - 1, ring[(u + D - 1) % D]);
+                __builtin_amdgcn_sched_barrier(0);
+                store(it & 1, ring[u]);
+                batch_barrier();   // window it published
+            }
+        }
+    }
+}
+
+template <int NWP>
+struct BatchWWin {
+    u32x4_t c[NWP];
+    uint32_t s[NWP];
+};
+
+template <int NXP>
+struct BatchXWin {
+    u32x4_t x[NXP];
+};
+
+template <int TCW, int MB, int KS>
+__global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs a)
+{
+    using S = BatchShape<TCW, MB, KS>;
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
@@ -104,9 +204,7 @@ __global__ __launch_bounds__(kWave *TW) void mfma_batch_kernel(GemmArgs a)
     const int q = lane >> 4;
     const int K = a.K;
     const int N = a.N;
-    const int m0 = blockIdx.y * 16 * kBatchMaxBlocks;   // row slab of this workgroup
-    const int M = min(16 * kBatchMaxBlocks, a.M - m0);  // rows of the slab
-    const int MB = (M + 15) / 16;
+    const int M = a.M;   // rows of this slab: 16 (MB - 1) < M <= 16 MB
     const int CH = num_chunks(K);
     const int NG = num_groups(N);
     const int G = gridDim.x;
@@ -115,116 +213,180 @@ __global__ __launch_bounds__(kWave *TW) void mfma_batch_kernel(GemmArgs a)
     const int c0 = kGroupCols * g0;
     const int ncols = min(N - c0, kGroupCols * ngroups);
     const int T = (ngroups + 3) / 4;
-    const int nwin = (CH + 3) / 4;
+    const int nwin = (K + kBatchWindow - 1) / kBatchWindow;
 
-    const uint32_t gq = (uint32_t)CH * kChunkCodeBytes;
-    const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;
-    const rsrc_t rq = make_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
-    const rsrc_t rs = make_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
-    const rsrc_t rx = make_rsrc(a.X + (size_t)m0 * (size_t)K, (uint32_t)M * (uint32_t)K * 2u);
-    const int gr = r >> 2;
-    const uint32_t lq = (uint32_t)gr * gq + (uint32_t)q * kChunkCodeBytes + (uint32_t)(r & 3) * 16u;
-    const uint32_t ls = (uint32_t)gr * gs + (uint32_t)q * kChunkScaleBytes + (uint32_t)(r & 2) * 2u;
-    const uint32_t sshift = 16u * (uint32_t)(r & 1);
-    const float g = *a.gscale;
-    uint8_t *const ring = lds + P * kBatchXWinBytes + wave * (P * TCW * kBatchTileBytes);
-
-    for (int tc0 = 0; tc0 < T; tc0 += TW * TCW) {
-        // Tiles of this wavefront in this pass: tc0 + wave + TW j, j < nt.
-        const int nt = max(0, min(TCW, (T - tc0 - wave + TW - 1) / TW));
-
-        // X of window w into ring slot w % P: load p of this wavefront fills the 1 KB block
-        // p * TW + wave of the slot, i.e. 4 rows.
-        auto issue_x = [&](int w) {
-            uint8_t *slotp = lds + (w % P) * kBatchXWinBytes;
+    // Each role runs its own loop over the passes (tiles tc0 .. tc0 + PT - 1), so that what it
+    // precomputes stays inside its branch; all roles meet the same barriers in the same order.
+    if (wave >= kBatchConsumers + 2) {
+        // ---------------- weight loader: pass tiles p = wl, wl + 2, ... ----------------
+        const int wl = wave - (kBatchConsumers + 2);
+        const uint32_t gq = (uint32_t)CH * kChunkCodeBytes;
+        const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;
+        const rsrc_t rq = make_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
+        const rsrc_t rs = make_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
+        const int gr = r >> 2;
+        const uint32_t lq =
+            (uint32_t)gr * gq + (uint32_t)q * kChunkCodeBytes + (uint32_t)(r & 3) * 16u;
+        const uint32_t ls =
+            (uint32_t)gr * gs + (uint32_t)q * kChunkScaleBytes + (uint32_t)(r & 2) * 2u;
+        for (int tc0 = 0; tc0 < T; tc0 += S::PT) {
+            // Window-0 offsets; a missing tile gets kOutOfRange, which stays out of range after
+            // a window offset is added (every buffer here is far below 2^31 bytes).
+            uint32_t coff[S::NWP], soff[S::NWP];
 #pragma unroll
-            for (int p = 0; p < XL; p++) {
-                const int blk = p * TW + wave;
-                const int row = blk * 4 + (lane >> 4);
-                const int kp = (lane & 15) ^ (row & 7);
-                const int k = kMfmaWindow * w + 8 * kp;
-                const bool v = w < nwin && row < M && k < K;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rx, (__attribute__((address_space(3))) void *)(slotp + blk * 1024), 16,
-                    off_if(v, ((uint32_t)row * (uint32_t)K + (uint32_t)k) * 2u), 0, 0,
-                    kAuxNormal);
+            for (int i = 0; i < S::NWP; i++) {
+                const int p = wl + 2 * i;
+                const int t = tc0 + p;
+                const bool v = p < S::PT && 4 * t + gr < ngroups;
+                coff[i] = off_if(v, lq + (uint32_t)t * (4u * gq));
+                soff[i] = off_if(v, ls + (uint32_t)t * (4u * gs));
             }
-        };
-        // Weights of window w into this wavefront's ring slot w % P.
-        auto issue_w = [&](int w) {
-            const bool kv = w < nwin && 4 * w + q < CH;
-            uint8_t *slotp = ring + (w % P) * (TCW * kBatchTileBytes);
+            auto load = [&](int w, BatchWWin<S::NWP> &dst) {
+                const bool kv = w < nwin && 4 * w + q < CH;
+                const uint32_t cw = (uint32_t)w * (4u * kChunkCodeBytes);
+                const uint32_t sw = (uint32_t)w * (4u * kChunkScaleBytes);
 #pragma unroll
-            for (int j = 0; j < TCW; j++) {
-                const int t = tc0 + wave + TW * j;
-                const bool v = kv && j < nt && 4 * t + gr < ngroups;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rq, (__attribute__((address_space(3))) void *)(slotp + j * (kWave * 16)), 16,
-                    off_if(v, lq + (uint32_t)t * (4u * gq) + (uint32_t)w * (4u * kChunkCodeBytes)),
-                    0, 0, kAuxNormal);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs,
-                    (__attribute__((address_space(3))) void *)(slotp + TCW * (kWave * 16) +
-                                                               j * (kWave * 4)),
-                    4, off_if(v, ls + (uint32_t)t * (4u * gs) + (uint32_t)w * (4u * kChunkScaleBytes)),
-                    0, 0, kAuxNormal);
-            }
-        };
-
-        f32x4_t acc[kBatchMaxBlocks][TCW];
+                for (int i = 0; i < S::NWP; i++) {
+                    dst.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off_if(kv, coff[i] + cw),
+                                                                     0, kAuxNormal);
+                    dst.s[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_if(kv, soff[i] + sw),
+                                                                    0, kAuxNormal);
+                }
+            };
+            auto store = [&](int buf, const BatchWWin<S::NWP> &src) {
+                uint8_t *wb = lds + 2 * S::XBUF + buf * S::WBUF;
 #pragma unroll
-        for (int b = 0; b < kBatchMaxBlocks; b++)
+                for (int i = 0; i < S::NWP; i++) {
+                    const int p = wl + 2 * i;
+                    if (p < S::PT) {
+                        u32x4_t v;
 #pragma unroll
-            for (int t = 0; t < TCW; t++)
-                acc[b][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-        __syncthreads();   // the previous pass is done with every buffer
-#pragma unroll
-        for (int w = 0; w < P - 1; w++) {
-            issue_x(w);
-            issue_w(w);
-        }
-        for (int it = 0; it < nwin; it++) {
-            // Window it has landed once only the P - 2 later windows' loads are pending; the
-            // barrier then publishes its X and tells that every wavefront is done with window
-            // it - 1, whose slots the loads of window it + P - 1 reuse. A plain s_barrier: a
-            // fenced one would also wait for the loads still in flight.
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((P - 2) * LOADS) : "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            issue_x(it + P - 1);
-            issue_w(it + P - 1);
-            const uint8_t *slotp = ring + (it % P) * (TCW * kBatchTileBytes);
-            u32x4_t c[TCW];
-            uint32_t s[TCW];
-#pragma unroll
-            for (int j = 0; j < TCW; j++) {
-                c[j] = *reinterpret_cast<const u32x4_t *>(slotp + j * (kWave * 16) + lane * 16);
-                s[j] = *reinterpret_cast<const uint32_t *>(slotp + TCW * (kWave * 16) +
-                                                           j * (kWave * 4) + lane * 4);
-            }
-            const uint8_t *xb = lds + (it % P) * kBatchXWinBytes;
-            if (MB == kBatchMaxBlocks && nt == TCW)
-                mul_window<true>(acc, xb, c, s, MB, nt, r, q, sshift);
-            else
-                mul_window<false>(acc, xb, c, s, MB, nt, r, q, sshift);
-        }
-        // Drain: the loads issued past the last window must land before LDS is reused.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-#pragma unroll
-        for (int j = 0; j < TCW; j++) {
-            const int colx = 16 * (tc0 + wave + TW * j) + r;
-            if (j < nt && colx < ncols) {
-#pragma unroll
-                for (int b = 0; b < kBatchMaxBlocks; b++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int row = 16 * b + 4 * q + e;
-                        if (row < M)
-                            a.Y[(size_t)(m0 + row) * N + c0 + colx] = acc[b][j][e] * g;
+                        for (int d = 0; d < 4; d++)
+                            v[batch_dword_pos(d)] = src.c[i][d];
+                        *reinterpret_cast<u32x4_t *>(wb + p * kBatchTileBytes + lane * 16) = v;
+                        *reinterpret_cast<uint32_t *>(wb + S::PT * kBatchTileBytes +
+                                                      p * (kWave * 4) + lane * 4) = src.s[i];
                     }
+                }
+            };
+            batch_produce<kBatchWRing, BatchWWin<S::NWP>>(nwin, load, store);
+            batch_barrier();   // the consumers are done with both buffers
+            if (KS > 1) {
+                batch_barrier();   // partial sums written
+                batch_barrier();   // partial sums read
             }
+        }
+    } else if (wave >= kBatchConsumers) {
+        // ---------------- X loader: rows 8 MB xl .. 8 MB xl + 8 MB - 1 ----------------
+        const int xl = wave - kBatchConsumers;
+        // Rows past M lie beyond the descriptor and read zeros; k past K is cut per lane.
+        const rsrc_t rx = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * 2u);
+        const int kp = lane & 15;
+        const int row0 = 8 * MB * xl + (lane >> 4);   // row of piece i: row0 + 4 i
+        const uint32_t xbase = ((uint32_t)row0 * (uint32_t)K + 8u * (uint32_t)kp) * 2u;
+        const uint32_t xstep = 8u * (uint32_t)K;      // 4 rows
+        uint32_t slot4[4];                           // LDS slot of piece i depends on i % 4
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            slot4[c] = (uint32_t)row0 * kBatchRowBytes +
+                       16u * (uint32_t)(kp ^ ((row0 + 4 * c) & 15));
+        for (int tc0 = 0; tc0 < T; tc0 += S::PT) {
+            auto load = [&](int w, BatchXWin<S::NXP> &dst) {
+                const bool v = w < nwin && kBatchWindow * w + 8 * kp < K;
+                const uint32_t cur = xbase + (uint32_t)w * (kBatchWindow * 2);
+#pragma unroll
+                for (int i = 0; i < S::NXP; i++)
+                    dst.x[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rx, off_if(v, cur + (uint32_t)i * xstep), 0, kAuxNormal);
+            };
+            auto store = [&](int buf, const BatchXWin<S::NXP> &src) {
+                uint8_t *xb = lds + buf * S::XBUF;
+#pragma unroll
+                for (int i = 0; i < S::NXP; i++)
+                    *reinterpret_cast<u32x4_t *>(xb + slot4[i & 3] + 4 * i * kBatchRowBytes) =
+                        src.x[i];
+            };
+            batch_produce<S::XRING, BatchXWin<S::NXP>>(nwin, load, store);
+            batch_barrier();
+            if (KS > 1) {
+                batch_barrier();
+                batch_barrier();
+            }
+        }
+    } else {
+        // ---------------- consumer ----------------
+        const int ts = wave % S::TS;
+        const int ks = wave / S::TS;
+        const uint32_t sshift = 16u * (uint32_t)(r & 1);
+        const rsrc_t ry = make_rsrc(a.Y, (uint32_t)M * (uint32_t)N * 4u);
+        for (int tc0 = 0; tc0 < T; tc0 += S::PT) {
+            const int nt = max(0, min(TCW, (T - tc0 - ts + S::TS - 1) / S::TS));
+            f32x4_t acc[MB][TCW];
+#pragma unroll
+            for (int b = 0; b < MB; b++)
+#pragma unroll
+                for (int j = 0; j < TCW; j++)
+                    acc[b][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if (nt >= TCW)
+                batch_consume<TCW, MB, KS, TCW>(acc, lds, nwin, ts, ks, lane, r, q, sshift);
+            else if (TCW > 1 && nt == TCW - 1)
+                batch_consume<TCW, MB, KS, (TCW > 1 ? TCW - 1 : 0)>(acc, lds, nwin, ts, ks, lane,
+                                                                    r, q, sshift);
+            else if (TCW > 2 && nt == TCW - 2)
+                batch_consume<TCW, MB, KS, (TCW > 2 ? TCW - 2 : 0)>(acc, lds, nwin, ts, ks, lane,
+                                                                    r, q, sshift);
+            else
+                batch_consume<TCW, MB, KS, 0>(acc, lds, nwin, ts, ks, lane, r, q, sshift);
+            batch_barrier();   // every wavefront is done with the buffers, which red reuses
+
+            // acc[b][j][e] is the partial Y[16 b + 4 q + e][column 16 (tc0 + ts + TS j) + r] over
+            // the steps of this consumer.
+            float *red = reinterpret_cast<float *>(lds);   // [KS - 1][TS][TCW][MB][4][64]
+            auto red_at = [&](int k2, int j, int b, int e) -> float & {
+                return red[((((k2 - 1) * S::TS + ts) * TCW + j) * MB + b) * (4 * kWave) +
+                           e * kWave + lane];
+            };
+            if (KS > 1) {
+                if (ks > 0) {
+#pragma unroll
+                    for (int j = 0; j < TCW; j++)
+                        if (j < nt)
+#pragma unroll
+                            for (int b = 0; b < MB; b++)
+#pragma unroll
+                                for (int e = 0; e < 4; e++)
+                                    red_at(ks, j, b, e) = acc[b][j][e];
+                }
+                batch_barrier();   // partial sums written
+            }
+            if (ks == 0) {
+                // Rows >= M lie beyond the descriptor (the whole offset is in the VGPR, which
+                // the range check covers), so their stores are dropped; so are columns past the
+                // workgroup's share.
+                const float g = *a.gscale;
+#pragma unroll
+                for (int j = 0; j < TCW; j++) {
+                    const int colx = 16 * (tc0 + ts + S::TS * j) + r;
+                    if (j < nt) {
+                        const bool cv = colx < ncols;
+                        const uint32_t vo =
+                            ((uint32_t)(4 * q) * (uint32_t)N + (uint32_t)(c0 + colx)) * 4u;
+#pragma unroll
+                        for (int b = 0; b < MB; b++)
+#pragma unroll
+                            for (int e = 0; e < 4; e++) {
+                                float v = acc[b][j][e];
+                                for (int k2 = 1; k2 < KS; k2++)
+                                    v += red_at(k2, j, b, e);
+                                const uint32_t ro = (uint32_t)(16 * b + e) * (uint32_t)N * 4u;
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    __float_as_uint(v * g), ry, off_if(cv, vo + ro), 0, 0);
+                            }
+                    }
+                }
+            }
+            if (KS > 1)
+                batch_barrier();   // partial sums read before the next pass refills the buffers
         }
     }
 }

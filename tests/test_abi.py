@@ -92,9 +92,16 @@ def test_gemm_path_rejects_bad_options(lib):
     # the matrix-core kernel runs 4 or 8 waves per workgroup
     assert nv.nvfp4_gemm_path(nv.PATH_MFMA, 16, 16, 16, 256, *ptrs, None) == \
         nv.ERROR_INVALID_VALUE
-    # the batch kernel runs 4 waves per workgroup
-    assert nv.nvfp4_gemm_path(nv.PATH_BATCH, 8, 128, 16, 256, *ptrs, None) == \
-        nv.ERROR_INVALID_VALUE
+    # the batch kernel's split is the step split 1, 2 or 4
+    for split in (8, 16):
+        assert nv.nvfp4_gemm_path(nv.PATH_BATCH, split, 128, 16, 256, *ptrs, None) == \
+            nv.ERROR_INVALID_VALUE
+    # the wave counts of the other kernels are 4, 8 or 16
+    for split in (1, 2):
+        assert nv.nvfp4_gemm_path(nv.PATH_MFMA, split, 16, 16, 256, *ptrs, None) == \
+            nv.ERROR_INVALID_VALUE
+        assert nv.nvfp4_gemm_path(nv.PATH_DOT, split, 1, 16, 256, *ptrs, None) == \
+            nv.ERROR_INVALID_VALUE
 
 
 def test_gemm_rejects_overflowing_sizes(lib):

@@ -16,7 +16,8 @@ from parity import (FINITE_SCALES, check_close, gpu_gemm, random_case, say, to_d
 pytestmark = pytest.mark.gpu
 
 PATHS = [(nv.PATH_DOT, 4), (nv.PATH_DOT, 8), (nv.PATH_DOT, 16),
-         (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8), (nv.PATH_BATCH, 4), (nv.PATH_AUTO, 0)]
+         (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
+         (nv.PATH_BATCH, 1), (nv.PATH_BATCH, 2), (nv.PATH_BATCH, 4), (nv.PATH_AUTO, 0)]
 VALU_PATHS = (nv.PATH_DOT,)   # the dot-product kernel: M <= 8
 SMALL_M = [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 130]
 SMALL_N = [1, 15, 16, 17, 65]
@@ -121,7 +122,8 @@ def test_deterministic(device):
 
 
 @pytest.mark.parametrize("path,split", [(nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
-                                        (nv.PATH_BATCH, 4), (nv.PATH_DOT, 16)])
+                                        (nv.PATH_BATCH, 1), (nv.PATH_BATCH, 4),
+                                        (nv.PATH_DOT, 16)])
 def test_many_columns_per_workgroup(device, path, split):
     """Enough columns that a persistent workgroup owns more column tiles than one pass takes
     (several chunks per workgroup), with a ragged last tile and a ragged row block."""
