@@ -88,56 +88,92 @@ __device__ __forceinline__ void batch_read_a(u32x4_t (&av)[MB], const uint8_t *x
     }
 }
 
-// One window of one consumer with NT live tiles: NSTEP steps of decode + MB x NT MFMAs; the A
-// fragments of the next step are read while the current one multiplies.
+// B fragments of step d (code dword i of each live tile) decoded to bf16 with their block scale.
+template <int NT>
+__device__ __forceinline__ void batch_decode(bf16x8_t (&bf)[NT], const uint32_t (&code)[NT],
+                                             const uint32_t (&sw)[NT], int d)
+{
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+        // Steps 0 and 1 lie in the chunk's first block of 16 k, steps 2 and 3 in the second.
+        const float sc = (d < 2) ? e4m3_to_f32<0>(sw[j]) : e4m3_to_f32<1>(sw[j]);
+        bf[j] = decode8_scaled(code[j], sc);
+    }
+}
+
+// One window of one consumer with NT live tiles: NSTEP steps of MB x NT MFMAs. The A fragments
+// and the decoded B fragments of step i + 1 are prepared while step i multiplies: the
+// scheduling groups interleave one MFMA with a few VALU instructions of the next decode (the
+// matrix core runs an MFMA for 16 cycles, during which the wavefront can issue VALU work).
 template <int TCW, int MB, int KS, int NT>
 __device__ __forceinline__ void batch_window(f32x4_t (&acc)[MB][TCW], const uint8_t *xb,
                                              const uint8_t *wb, int ts, int ks, int lane, int r,
                                              int q, uint32_t sshift)
 {
     using S = BatchShape<TCW, MB, KS>;
-    uint32_t code[NT][S::NSTEP];
+    // Code dword of step i of live tile j (read from LDS one step ahead) and its scale word.
+    auto code_at = [&](int i, int j) -> uint32_t {
+        const int d = ks + KS * i;
+        return *reinterpret_cast<const uint32_t *>(wb + (ts + S::TS * j) * kBatchTileBytes +
+                                                   lane * 16 + 4 * batch_dword_pos(d));
+    };
+    uint32_t code[2][NT];
     uint32_t sw[NT];
 #pragma unroll
     for (int j = 0; j < NT; j++) {
-        const uint8_t *tb = wb + (ts + S::TS * j) * kBatchTileBytes + lane * 16;
-        if (KS == 1) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(tb);
-#pragma unroll
-            for (int d = 0; d < S::NSTEP; d++)
-                code[j][d] = v[batch_dword_pos(d)];
-        } else if (KS == 2) {
-            const u32x2_t v = *reinterpret_cast<const u32x2_t *>(tb + 8 * ks);
-            code[j][0] = v[0];
-            code[j][S::NSTEP - 1] = v[1];
-        } else {
-            code[j][0] = *reinterpret_cast<const uint32_t *>(
-                tb + 4 * (ks == 0 ? 0 : ks == 1 ? 2 : ks == 2 ? 1 : 3));
-        }
+        code[0][j] = code_at(0, j);
         sw[j] = *reinterpret_cast<const uint32_t *>(wb + S::PT * kBatchTileBytes +
                                                     (ts + S::TS * j) * (kWave * 4) + lane * 4) >>
                 sshift;
     }
-    u32x4_t av[2][MB];
-    batch_read_a<MB>(av[0], xb, r, q, ks);
+    // av[b] is refilled with step i + 1's fragment right after its last MFMA of step i.
+    u32x4_t av[MB];
+    bf16x8_t bf[2][NT];
+    batch_read_a<MB>(av, xb, r, q, ks);
+    batch_decode<NT>(bf[0], code[0], sw, ks);
+    if (S::NSTEP > 1) {
+#pragma unroll
+        for (int j = 0; j < NT; j++)
+            code[1][j] = code_at(1, j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kValuPerMfma = (20 + MB - 1) / MB;   // decode of one tile: about 20 VALU
 #pragma unroll
     for (int i = 0; i < S::NSTEP; i++) {
         const int d = ks + KS * i;
-        if (i + 1 < S::NSTEP)
-            batch_read_a<MB>(av[(i + 1) & 1], xb, r, q, d + KS);
-        bf16x8_t bfrag[NT];
+        const bool more = i + 1 < S::NSTEP;
+        if (more) {
+            batch_decode<NT>(bf[(i + 1) & 1], code[(i + 1) & 1], sw, d + KS);
+            if (i + 2 < S::NSTEP) {
 #pragma unroll
-        for (int j = 0; j < NT; j++) {
-            // Steps 0 and 1 lie in the chunk's first block of 16 k, steps 2 and 3 in the second.
-            const float sc = (d < 2) ? e4m3_to_f32<0>(sw[j]) : e4m3_to_f32<1>(sw[j]);
-            bfrag[j] = decode8_scaled(code[j][i], sc);
+                for (int j = 0; j < NT; j++)
+                    code[i & 1][j] = code_at(i + 2, j);
+            }
         }
+        const int piece = 4 * q + d + KS;
 #pragma unroll
-        for (int b = 0; b < MB; b++)
+        for (int b = 0; b < MB; b++) {
 #pragma unroll
             for (int j = 0; j < NT; j++)
-                acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i & 1][b]),
-                                                                    bfrag[j], acc[b][j], 0, 0, 0);
+                acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(av[b]), bf[i & 1][j], acc[b][j], 0, 0, 0);
+            if (more) {
+                const int row = 16 * b + r;
+                av[b] = *reinterpret_cast<const u32x4_t *>(xb + row * kBatchRowBytes +
+                                                           16 * (piece ^ (row & 15)));
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int b = 0; b < MB; b++) {
+#pragma unroll
+                for (int j = 0; j < NT; j++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // next decode
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next A of block b
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
