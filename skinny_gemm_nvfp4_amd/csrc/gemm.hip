@@ -91,6 +91,25 @@ constexpr int batch_lds()
 constexpr int kBatchLds[3][4][3] = {NVFP4_BATCH_LDS_MB(1), NVFP4_BATCH_LDS_MB(2),
                                     NVFP4_BATCH_LDS_MB(3)};
 
+// ---- batch kernels with remainder tiles (KS = 1): [(TCW, NR) index][MB index] ----
+constexpr int kBatchNrCombos = 3;
+constexpr int kBatchNrTcw[kBatchNrCombos] = {1, 1, 2};
+constexpr int kBatchNrNr[kBatchNrCombos] = {1, 2, 1};
+#define NVFP4_BATCH_NR_MB(TCW, NR)                                                         \
+    {                                                                                      \
+        &mfma_batch_kernel<TCW, 1, 1, NR>, &mfma_batch_kernel<TCW, 2, 1, NR>,              \
+            &mfma_batch_kernel<TCW, 4, 1, NR>, &mfma_batch_kernel<TCW, 8, 1, NR>           \
+    }
+const KernelFn kBatchNr[kBatchNrCombos][4] = {NVFP4_BATCH_NR_MB(1, 1), NVFP4_BATCH_NR_MB(1, 2),
+                                              NVFP4_BATCH_NR_MB(2, 1)};
+#define NVFP4_BATCH_NR_LDS(TCW, NR)                                                        \
+    {                                                                                      \
+        BatchShape<TCW, 1, 1, NR>::LDS, BatchShape<TCW, 2, 1, NR>::LDS,                    \
+            BatchShape<TCW, 4, 1, NR>::LDS, BatchShape<TCW, 8, 1, NR>::LDS                 \
+    }
+constexpr int kBatchNrLds[kBatchNrCombos][4] = {NVFP4_BATCH_NR_LDS(1, 1), NVFP4_BATCH_NR_LDS(1, 2),
+                                                NVFP4_BATCH_NR_LDS(2, 1)};
+
 int wave_index(int waves)
 {
     switch (waves) {
@@ -227,11 +246,29 @@ int mfma_default_waves(int N, int K)
 // bytes per cycle); the weight bytes at the compute unit's share of HBM (13 bytes per cycle); and
 // the load latency spread over the windows in flight (about 4000 cycles / 4). Every pass also
 // pays one latency to fill the pipeline.
+constexpr double kLoadLatency = 4000.0;
+
 struct BatchPlan {
     int tcw, mbi, ksi, mb, grid, lds;
+    int nr;    // remainder tiles per pass (KS = 1 only), 0 for none
+    int nri;   // index into kBatchNr when nr > 0
 };
 
-constexpr double kLoadLatency = 4000.0;
+// Cycle estimate of one pass window (see batch_plan) for `units` tile-steps per consumer.
+double batch_window_cost(int units, int MB, int KS, int pt)
+{
+    const double mfma = 16.0 * units * MB;
+    const double valu = 80.0 * units;
+    const double x_l2 = 16.0 * MB * kBatchRowBytes / 64.0;
+    const double lds = (16.0 * MB * kBatchRowBytes * (1 + kBatchConsumers / KS) +
+                        2.0 * pt * (kBatchTileBytes + kWave * 4)) /
+                       128.0;
+    const double hbm = pt * (kBatchTileBytes + kWave * 4) / 13.0;
+    const double lat = kLoadLatency / (kBatchWRing - 1);
+    // (plus a tenth of the consumer's own work, which breaks ties toward spreading it)
+    return std::max(std::max(std::max(mfma, valu), std::max(x_l2, lds)), std::max(hbm, lat)) +
+           0.1 * std::max(mfma, valu);
+}
 
 bool batch_plan(int rows, int N, int K, int ks_req, BatchPlan *P)
 {
@@ -260,25 +297,36 @@ bool batch_plan(int rows, int N, int K, int ks_req, BatchPlan *P)
             for (int t0 = 0; t0 < T; t0 += PT) {
                 const int pt = std::min(PT, T - t0);              // tiles of this pass
                 const int live = std::min(tcw, (pt + TS - 1) / TS);
-                const double mfma = 16.0 * live * MB * NSTEP;
-                const double valu = 80.0 * live * NSTEP;
-                const double x_l2 = 16.0 * MB * kBatchRowBytes / 64.0;
-                const double lds = (16.0 * MB * kBatchRowBytes * (1 + kBatchConsumers / KS) +
-                                    2.0 * pt * (kBatchTileBytes + kWave * 4)) /
-                                   128.0;
-                const double hbm = pt * (kBatchTileBytes + kWave * 4) / 13.0;
-                const double lat = kLoadLatency / (kBatchWRing - 1);
-                const double win = std::max(std::max(std::max(mfma, valu), std::max(x_l2, lds)),
-                                            std::max(hbm, lat));
-                // (plus a tenth of the consumer's own work, which breaks ties toward spreading
-                // it over more consumers)
-                cost += nwin * (win + 0.1 * std::max(mfma, valu)) + kLoadLatency;
+                cost += nwin * batch_window_cost(live * NSTEP, MB, KS, pt) + kLoadLatency;
             }
             if (!found || cost < best - 1e-9) {
                 best = cost;
                 found = true;
                 P->tcw = tcw;
                 P->ksi = ksi;
+                P->nr = 0;
+                P->nri = 0;
+            }
+        }
+    }
+    // Remainder variants (KS = 1): passes of 4 TCW + NR tiles, every consumer 4 TCW + NR steps.
+    if (ks_req == 0 || ks_req == 1) {
+        for (int ci = 0; ci < kBatchNrCombos; ci++) {
+            const int tcw = kBatchNrTcw[ci], nr = kBatchNrNr[ci];
+            if (kBatchNrLds[ci][mbi] > kMaxLds)
+                continue;
+            const int PT = kBatchConsumers * tcw + nr;
+            double cost = 0.0;
+            for (int t0 = 0; t0 < T; t0 += PT)
+                cost += nwin * batch_window_cost(4 * tcw + nr, MB, 1, std::min(PT, T - t0)) +
+                        kLoadLatency;
+            if (!found || cost < best - 1e-9) {
+                best = cost;
+                found = true;
+                P->tcw = tcw;
+                P->ksi = 0;
+                P->nr = nr;
+                P->nri = ci;
             }
         }
     }
@@ -287,7 +335,7 @@ bool batch_plan(int rows, int N, int K, int ks_req, BatchPlan *P)
     P->mbi = mbi;
     P->mb = MB;
     P->grid = G;
-    P->lds = kBatchLds[P->tcw - 1][mbi][P->ksi];
+    P->lds = P->nr > 0 ? kBatchNrLds[P->nri][mbi] : kBatchLds[P->tcw - 1][mbi][P->ksi];
     return true;
 }
 
@@ -368,7 +416,7 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
             BatchPlan P;
             if (!batch_plan(rows, a.N, a.K, split, &P))
                 return hipErrorInvalidValue;
-            const KernelFn fn = kBatch[P.tcw - 1][P.mbi][P.ksi];
+            const KernelFn fn = P.nr > 0 ? kBatchNr[P.nri][P.mbi] : kBatch[P.tcw - 1][P.mbi][P.ksi];
             const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), P.lds);
             if (e != hipSuccess)
                 return e;

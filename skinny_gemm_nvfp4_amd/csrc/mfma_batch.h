@@ -26,8 +26,12 @@
 //     the window: code dword d is its B fragment, scale byte d / 2 the block scale, and row
 //     16 b + r of X at those k its A fragment of row block b (v_mfma_f32_16x16x32_bf16). Narrow
 //     shapes (few tiles per workgroup) take KS = 2 or 4 so that all four matrix cores work.
-//   * B = e2m1 * s decoded to bf16 (exact). The KS partial sums of a tile are added through LDS
-//     in ks order, then Y = sum * g. Results are reproducible.
+//   * With KS = 1 a pass may end in NR remainder tiles (4 TCW + NR tiles): consumer c multiplies
+//     MFMA step c of each remainder tile, so every consumer does the same work per window (a
+//     workgroup of 9 tiles runs as 4 x 2 + 1 instead of 3, 2, 2, 2).
+//   * B = e2m1 * s decoded to bf16 (exact). The KS partial sums of a tile (or the 4 of a
+//     remainder tile) are added through LDS in a fixed order, then Y = sum * g. Results are
+//     reproducible.
 #pragma once
 
 #include "device.h"
@@ -43,10 +47,14 @@ constexpr int kBatchWaves = 8;
 constexpr int kBatchTileBytes = kWave * 16;   // codes of one tile and window
 constexpr int kBatchWRing = 5;           // weight windows held by a weight loader
 
-template <int TCW, int MB, int KS>
+// NR > 0 (KS = 1 only): NR remainder tiles per pass after the TS TCW full ones; consumer c takes
+// MFMA step c of each of them, so that a pass of 4 TCW + NR tiles is balanced over the consumers.
+template <int TCW, int MB, int KS, int NR = 0>
 struct BatchShape {
+    static_assert(NR == 0 || KS == 1, "remainder tiles need KS = 1");
     static constexpr int TS = kBatchConsumers / KS;   // tile lanes
-    static constexpr int PT = TS * TCW;               // tiles per pass
+    static constexpr int PT = TS * TCW + NR;          // tiles per pass
+    static constexpr int NACC = TCW + NR;             // accumulator tiles per consumer
     static constexpr int NWP = (PT + 1) / 2;          // tiles per weight loader
     static constexpr int NXP = 2 * MB;                // X pieces per lane of an X loader
     static constexpr int XRING = MB >= 8 ? 2 : MB >= 4 ? 3 : 4;   // X windows per X loader
@@ -54,7 +62,9 @@ struct BatchShape {
     static constexpr int XBUF = 16 * MB * kBatchRowBytes;
     static constexpr int WBUF = PT * (kBatchTileBytes + kWave * 4);
     static constexpr int MAIN = 2 * XBUF + 2 * WBUF;
-    static constexpr int RED = (KS - 1) * TS * TCW * MB * kWave * 16;
+    static constexpr int RED_KS = (KS - 1) * TS * TCW * MB * kWave * 16;
+    static constexpr int RED_NR = kBatchConsumers * NR * MB * kWave * 16;
+    static constexpr int RED = RED_KS > RED_NR ? RED_KS : RED_NR;
     static constexpr int LDS = MAIN > RED ? MAIN : RED;
 };
 
@@ -105,12 +115,12 @@ __device__ __forceinline__ void batch_decode(bf16x8_t (&bf)[NT], const uint32_t 
 // and the decoded B fragments of step i + 1 are prepared while step i multiplies: the
 // scheduling groups interleave one MFMA with a few VALU instructions of the next decode (the
 // matrix core runs an MFMA for 16 cycles, during which the wavefront can issue VALU work).
-template <int TCW, int MB, int KS, int NT>
-__device__ __forceinline__ void batch_window(f32x4_t (&acc)[MB][TCW], const uint8_t *xb,
+template <int TCW, int MB, int KS, int NT, int NR>
+__device__ __forceinline__ void batch_window(f32x4_t (&acc)[MB][TCW + NR], const uint8_t *xb,
                                              const uint8_t *wb, int ts, int ks, int lane, int r,
                                              int q, uint32_t sshift)
 {
-    using S = BatchShape<TCW, MB, KS>;
+    using S = BatchShape<TCW, MB, KS, NR>;
     // Code dword of step i of live tile j (read from LDS one step ahead) and its scale word.
     auto code_at = [&](int i, int j) -> uint32_t {
         const int d = ks + KS * i;
@@ -126,8 +136,24 @@ __device__ __forceinline__ void batch_window(f32x4_t (&acc)[MB][TCW], const uint
                                                     (ts + S::TS * j) * (kWave * 4) + lane * 4) >>
                 sshift;
     }
+    // Remainder tiles: this consumer (ts, with TS = 4) multiplies their step ts only.
+    bf16x8_t bfr[NR > 0 ? NR : 1];
+    if constexpr (NR > 0) {
+#pragma unroll
+        for (int rr = 0; rr < NR; rr++) {
+            const int p = S::TS * TCW + rr;
+            const uint32_t c = *reinterpret_cast<const uint32_t *>(
+                wb + p * kBatchTileBytes + lane * 16 +
+                4 * (ts == 0 ? 0 : ts == 1 ? 2 : ts == 2 ? 1 : 3));
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(
+                                   wb + S::PT * kBatchTileBytes + p * (kWave * 4) + lane * 4) >>
+                               sshift;
+            bfr[rr] = decode8_scaled(c, ts < 2 ? e4m3_to_f32<0>(w) : e4m3_to_f32<1>(w));
+        }
+    }
     // av[b] is refilled with step i + 1's fragment right after its last MFMA of step i.
     u32x4_t av[MB];
+    u32x4_t ar[NR > 0 ? MB : 1];   // A fragments of step ts for the remainder tiles
     bf16x8_t bf[2][NT];
     batch_read_a<MB>(av, xb, r, q, ks);
     batch_decode<NT>(bf[0], code[0], sw, ks);
@@ -151,6 +177,10 @@ __device__ __forceinline__ void batch_window(f32x4_t (&acc)[MB][TCW], const uint
             }
         }
         const int piece = 4 * q + d + KS;
+        if constexpr (NR > 0) {
+            if (i == S::NSTEP - 1)
+                batch_read_a<MB>(ar, xb, r, q, ts);   // step ts, for the remainder tiles
+        }
 #pragma unroll
         for (int b = 0; b < MB; b++) {
 #pragma unroll
@@ -176,20 +206,29 @@ __device__ __forceinline__ void batch_window(f32x4_t (&acc)[MB][TCW], const uint
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (NR > 0) {
+        // Remainder tiles: MFMA step ts of each, with the fragments read during the last step.
+#pragma unroll
+        for (int b = 0; b < MB; b++)
+#pragma unroll
+            for (int rr = 0; rr < NR; rr++)
+                acc[b][TCW + rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(ar[b]), bfr[rr], acc[b][TCW + rr], 0, 0, 0);
+    }
 }
 
 // All windows of one pass for a consumer with NT live tiles (NT = 0: barriers only).
-template <int TCW, int MB, int KS, int NT>
-__device__ __forceinline__ void batch_consume(f32x4_t (&acc)[MB][TCW], const uint8_t *lds,
+template <int TCW, int MB, int KS, int NT, int NR>
+__device__ __forceinline__ void batch_consume(f32x4_t (&acc)[MB][TCW + NR], const uint8_t *lds,
                                               int nwin, int ts, int ks, int lane, int r, int q,
                                               uint32_t sshift)
 {
-    using S = BatchShape<TCW, MB, KS>;
+    using S = BatchShape<TCW, MB, KS, NR>;
     for (int it = 0; it < nwin; it++) {
         batch_barrier();   // window it is in buffer it & 1
         const int buf = it & 1;
         if constexpr (NT > 0)
-            batch_window<TCW, MB, KS, NT>(acc, lds + buf * S::XBUF,
+            batch_window<TCW, MB, KS, NT, NR>(acc, lds + buf * S::XBUF,
                                           lds + 2 * S::XBUF + buf * S::WBUF, ts, ks, lane, r, q,
                                           sshift);
     }
@@ -229,10 +268,11 @@ struct BatchXWin {
     u32x4_t x[NXP];
 };
 
-template <int TCW, int MB, int KS>
+template <int TCW, int MB, int KS, int NR = 0>
 __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs a)
 {
-    using S = BatchShape<TCW, MB, KS>;
+    using S = BatchShape<TCW, MB, KS, NR>;
+    constexpr int kExtraBarriers = (KS > 1 || NR > 0) ? 2 : 0;   // partial sums via LDS
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
@@ -307,10 +347,8 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
             };
             batch_produce<kBatchWRing, BatchWWin<S::NWP>>(nwin, load, store);
             batch_barrier();   // the consumers are done with both buffers
-            if (KS > 1) {
-                batch_barrier();   // partial sums written
-                batch_barrier();   // partial sums read
-            }
+            for (int e = 0; e < kExtraBarriers; e++)
+                batch_barrier();   // partial sums written, then read
         }
     } else if (wave >= kBatchConsumers) {
         // ---------------- X loader: rows 8 MB xl .. 8 MB xl + 8 MB - 1 ----------------
@@ -344,10 +382,8 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
             };
             batch_produce<S::XRING, BatchXWin<S::NXP>>(nwin, load, store);
             batch_barrier();
-            if (KS > 1) {
+            for (int e = 0; e < kExtraBarriers; e++)
                 batch_barrier();
-                batch_barrier();
-            }
         }
     } else {
         // ---------------- consumer ----------------
@@ -357,22 +393,22 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
         const rsrc_t ry = make_rsrc(a.Y, (uint32_t)M * (uint32_t)N * 4u);
         for (int tc0 = 0; tc0 < T; tc0 += S::PT) {
             const int nt = max(0, min(TCW, (T - tc0 - ts + S::TS - 1) / S::TS));
-            f32x4_t acc[MB][TCW];
+            f32x4_t acc[MB][S::NACC];
 #pragma unroll
             for (int b = 0; b < MB; b++)
 #pragma unroll
-                for (int j = 0; j < TCW; j++)
+                for (int j = 0; j < S::NACC; j++)
                     acc[b][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            if (nt >= TCW)
-                batch_consume<TCW, MB, KS, TCW>(acc, lds, nwin, ts, ks, lane, r, q, sshift);
+            if (NR > 0 || nt >= TCW)   // with remainder tiles every slot runs (dead ones on zeros)
+                batch_consume<TCW, MB, KS, TCW, NR>(acc, lds, nwin, ts, ks, lane, r, q, sshift);
             else if (TCW > 1 && nt == TCW - 1)
-                batch_consume<TCW, MB, KS, (TCW > 1 ? TCW - 1 : 0)>(acc, lds, nwin, ts, ks, lane,
-                                                                    r, q, sshift);
+                batch_consume<TCW, MB, KS, (TCW > 1 ? TCW - 1 : 0), NR>(acc, lds, nwin, ts, ks,
+                                                                        lane, r, q, sshift);
             else if (TCW > 2 && nt == TCW - 2)
-                batch_consume<TCW, MB, KS, (TCW > 2 ? TCW - 2 : 0)>(acc, lds, nwin, ts, ks, lane,
-                                                                    r, q, sshift);
+                batch_consume<TCW, MB, KS, (TCW > 2 ? TCW - 2 : 0), NR>(acc, lds, nwin, ts, ks,
+                                                                        lane, r, q, sshift);
             else
-                batch_consume<TCW, MB, KS, 0>(acc, lds, nwin, ts, ks, lane, r, q, sshift);
+                batch_consume<TCW, MB, KS, 0, NR>(acc, lds, nwin, ts, ks, lane, r, q, sshift);
             batch_barrier();   // every wavefront is done with the buffers, which red reuses
 
             // acc[b][j][e] is the partial Y[16 b + 4 q + e][column 16 (tc0 + ts + TS j) + r] over
@@ -423,6 +459,40 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
             }
             if (KS > 1)
                 batch_barrier();   // partial sums read before the next pass refills the buffers
+            if constexpr (NR > 0) {
+                // Remainder tiles: every consumer's partial (its own MFMA step) into LDS, then
+                // consumer rr adds the four of tile rr in consumer order.
+                float *rred = reinterpret_cast<float *>(lds);   // [4][NR][MB][4][64]
+#pragma unroll
+                for (int rr = 0; rr < NR; rr++)
+#pragma unroll
+                    for (int b = 0; b < MB; b++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            rred[(((ts * NR + rr) * MB + b) * 4 + e) * kWave + lane] =
+                                acc[b][TCW + rr][e];
+                batch_barrier();   // partial sums written
+                if (ts < NR) {
+                    const float g = *a.gscale;
+                    const int colx = 16 * (tc0 + S::TS * TCW + ts) + r;
+                    const bool cv = colx < ncols;
+                    const uint32_t vo =
+                        ((uint32_t)(4 * q) * (uint32_t)N + (uint32_t)(c0 + colx)) * 4u;
+#pragma unroll
+                    for (int b = 0; b < MB; b++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            float v = 0.0f;
+#pragma unroll
+                            for (int c = 0; c < kBatchConsumers; c++)
+                                v += rred[(((c * NR + ts) * MB + b) * 4 + e) * kWave + lane];
+                            const uint32_t ro = (uint32_t)(16 * b + e) * (uint32_t)N * 4u;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * g), ry,
+                                                                  off_if(cv, vo + ro), 0, 0);
+                        }
+                }
+                batch_barrier();   // partial sums read before the next pass refills the buffers
+            }
         }
     }
 }

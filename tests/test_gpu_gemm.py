@@ -134,3 +134,17 @@ def test_many_columns_per_workgroup(device, path, split):
     say(f"many-columns path={path} split={split} M={M} N={N} K={K}")
     Y = gpu_gemm(X, to_device_packed(Wq, Ws, g, device), device, path, split)
     check_close(Y, Yref, A, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,split", [(16, 34813, 0), (100, 34813, 0), (128, 34813, 1),
+                                       (33, 18431, 0), (128, 22521, 1), (16, 22521, 1)])
+def test_batch_remainder_tiles(device, M, N, split):
+    """Column shares of 5, 6 and 9 tiles of 16 per compute unit (256 CUs), where the batch kernel
+    splits the last 1 or 2 tiles of a pass by MFMA step across its four consumers and adds their
+    partial sums in LDS; ragged N, ragged last window (K = 272) and ragged row blocks."""
+    K = 272
+    X, Wq, Ws, g = random_case(500 + M + N, M, N, K, FINITE_SCALES)
+    Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
+    say(f"remainder path=batch split={split} M={M} N={N} K={K}")
+    Y = gpu_gemm(X, to_device_packed(Wq, Ws, g, device), device, nv.PATH_BATCH, split)
+    check_close(Y, Yref, A, f"M={M} N={N} K={K}")
