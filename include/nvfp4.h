@@ -42,7 +42,14 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer owned by the caller; the library keeps none of them past
- *     the call and allocates no device memory.
+ *     the call.
+ *   - Device memory of the library's own: only the split-K workspace of the batch kernel (K cut
+ *     across workgroups for narrow shapes at M > 16): one buffer per device, allocated by the
+ *     first call that needs it, grown when a call needs more, never freed before the process ends
+ *     (a captured graph may still use it). A call that would have to allocate while its stream is
+ *     being captured runs without split K instead; run one such call eagerly first.
+ *     Because the workspace is shared, calls that may split K (M > 16, or NVFP4_PATH_BATCH_SPLITK)
+ *     must not run concurrently on different streams of the same device.
  *   - Sizes: 1 <= M, 1 <= N, 16 <= K <= 4194304 (2^22), K % 16 == 0, and every array must have
  *     fewer than 2^62 bytes. Anything else returns NVFP4_ERROR_INVALID_VALUE.
  *   - Alignment: X, Wq, Wscale and W must be 16-byte aligned, Y and gscale 4-byte aligned;
@@ -53,8 +60,11 @@
  *   - Calls are stream-ordered on `stream` (a hipStream_t; NULL is the null stream) and never
  *     synchronise. A failed kernel launch returns NVFP4_ERROR_LAUNCH; faults during execution
  *     surface at the caller's next synchronisation, as for any HIP kernel.
- *   - Results are deterministic: the same inputs give the same bits on every call.
- *   - Calls are re-entrant and thread-safe; the library has no mutable global state.
+ *   - Results are deterministic: the same inputs give the same bits on every call. (The one
+ *     exception: a call that runs without split K for want of a workspace under capture, as
+ *     above, may differ from the split-K result in the last bits.)
+ *   - Calls are re-entrant and thread-safe on the host. The only mutable global state is the
+ *     workspace table, behind a mutex.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -123,9 +133,13 @@ typedef enum {
                              fp32 partial * s; M <= 8 */
     NVFP4_PATH_MFMA = 2,  /* matrix cores: E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 on
                              one 16-row block of X per workgroup; any M */
-    NVFP4_PATH_BATCH = 3  /* matrix cores, every weight decoded once per 128-row slab of X:
+    NVFP4_PATH_BATCH = 3, /* matrix cores, every weight decoded once per 128-row slab of X:
                              loader wavefronts stage X and the weights in LDS, four consumer
-                             wavefronts decode and multiply; any M, meant for M > 16 */
+                             wavefronts decode and multiply; any M, meant for M > 16. It may cut
+                             K across workgroups (see below) */
+    NVFP4_PATH_BATCH_SPLITK = 4 /* NVFP4_PATH_BATCH with K cut into `split` slices across
+                             workgroups: partial sums go to a workspace, a second kernel adds
+                             them in slice order and applies g */
 } nvfp4_path_t;
 
 /*
@@ -138,6 +152,7 @@ typedef enum {
  *   NVFP4_PATH_MFMA: wavefronts per workgroup, 4 or 8.
  *   NVFP4_PATH_BATCH: 1, 2 or 4, the number of consumer wavefronts that share the K steps of one
  *     column tile (4 / split tiles are processed side by side).
+ *   NVFP4_PATH_BATCH_SPLITK: 2, 4 or 8 K slices (at most one per 128 k).
  * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
 nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,

@@ -23,6 +23,7 @@ PATH_AUTO = 0
 PATH_DOT = 1
 PATH_MFMA = 2
 PATH_BATCH = 3
+PATH_BATCH_SPLITK = 4
 
 _lib = None
 

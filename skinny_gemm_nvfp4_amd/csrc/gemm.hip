@@ -10,6 +10,7 @@
 //     rows of X (verification of several requests together).
 #include <algorithm>
 #include <atomic>
+#include <map>
 #include <mutex>
 #include <set>
 #include <utility>
@@ -250,13 +251,17 @@ constexpr double kLoadLatency = 4000.0;
 
 struct BatchPlan {
     int tcw, mbi, ksi, mb, grid, lds;
-    int nr;    // remainder tiles per pass (KS = 1 only), 0 for none
-    int nri;   // index into kBatchNr when nr > 0
+    int nr;       // remainder tiles per pass (KS = 1 only), 0 for none
+    int nri;      // index into kBatchNr when nr > 0
+    int nslice;   // K slices across workgroups (split K), 1 for none
 };
 
 // Cycle estimate of one pass window (see batch_plan) for `units` tile-steps per consumer.
 double batch_window_cost(int units, int MB, int KS, int pt)
 {
+    // X arrives from L2 about 1400 cycles after it is requested, XRING - 1 windows ahead.
+    const int xring = MB >= 8 ? 2 : MB >= 4 ? 3 : 4;
+    const double x_lat = 1400.0 / (xring - 1);
     const double mfma = 16.0 * units * MB;
     const double valu = 80.0 * units;
     const double x_l2 = 16.0 * MB * kBatchRowBytes / 64.0;
@@ -266,67 +271,79 @@ double batch_window_cost(int units, int MB, int KS, int pt)
     const double hbm = pt * (kBatchTileBytes + kWave * 4) / 13.0;
     const double lat = kLoadLatency / (kBatchWRing - 1);
     // (plus a tenth of the consumer's own work, which breaks ties toward spreading it)
-    return std::max(std::max(std::max(mfma, valu), std::max(x_l2, lds)), std::max(hbm, lat)) +
+    return std::max(std::max(std::max(mfma, valu), std::max(x_l2, lds)),
+                    std::max(std::max(hbm, lat), x_lat)) +
            0.1 * std::max(mfma, valu);
 }
 
-bool batch_plan(int rows, int N, int K, int ks_req, BatchPlan *P)
+bool batch_plan(int rows, int N, int K, int ks_req, int s_req, BatchPlan *P)
 {
-    const int G = group_grid(N);
     // The Y descriptor covers rows * N floats with 32-bit offsets.
-    if (!bytes_fit(N, K, G) || (long long)rows * N * 4 >= (1LL << 31))
+    if ((long long)rows * N * 4 >= (1LL << 31))
         return false;
-    const int gmax = (num_groups(N) + G - 1) / G;
-    const int T = (gmax + 3) / 4;
     const int nwin = (K + kBatchWindow - 1) / kBatchWindow;
     const int mbi = rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 64 ? 2 : 3;
     const int MB = 1 << mbi;
+    const int cus = compute_units();
     double best = 0.0;
     bool found = false;
-    for (int ksi = 0; ksi < 3; ksi++) {
-        const int KS = 1 << ksi;
-        if (ks_req != 0 && KS != ks_req)
+    for (int si = 0; si < 4; si++) {
+        const int S = 1 << si;   // K slices
+        if ((s_req != 0 && S != s_req) || S > nwin)
             continue;
-        const int TS = kBatchConsumers / KS;
-        const int NSTEP = 4 / KS;
-        for (int tcw = 1; tcw <= 3; tcw++) {
-            if (kBatchLds[tcw - 1][mbi][ksi] > kMaxLds)
-                continue;
-            const int PT = TS * tcw;
-            double cost = 0.0;
-            for (int t0 = 0; t0 < T; t0 += PT) {
-                const int pt = std::min(PT, T - t0);              // tiles of this pass
-                const int live = std::min(tcw, (pt + TS - 1) / TS);
-                cost += nwin * batch_window_cost(live * NSTEP, MB, KS, pt) + kLoadLatency;
-            }
+        const int G = std::max(1, std::min(num_groups(N), cus / S));
+        if (!bytes_fit(N, K, G))
+            continue;
+        const int T = ((num_groups(N) + G - 1) / G + 3) / 4;
+        const int nw = (nwin + S - 1) / S;   // windows of the longest slice
+        // Split K adds the S partial slices' round trip and a second launch.
+        const double reduce =
+            S > 1 ? (S + 1.0) * rows * N * 4.0 / 2400.0 + kLoadLatency : 0.0;
+        auto consider = [&](double cost, int tcw, int ksi, int nr, int nri) {
+            cost += reduce;
             if (!found || cost < best - 1e-9) {
                 best = cost;
                 found = true;
                 P->tcw = tcw;
                 P->ksi = ksi;
-                P->nr = 0;
-                P->nri = 0;
+                P->nr = nr;
+                P->nri = nri;
+                P->nslice = S;
+                P->grid = G;
+            }
+        };
+        for (int ksi = 0; ksi < 3; ksi++) {
+            const int KS = 1 << ksi;
+            if (ks_req != 0 && KS != ks_req)
+                continue;
+            const int TS = kBatchConsumers / KS;
+            const int NSTEP = 4 / KS;
+            for (int tcw = 1; tcw <= 3; tcw++) {
+                if (kBatchLds[tcw - 1][mbi][ksi] > kMaxLds)
+                    continue;
+                const int PT = TS * tcw;
+                double cost = 0.0;
+                for (int t0 = 0; t0 < T; t0 += PT) {
+                    const int pt = std::min(PT, T - t0);   // tiles of this pass
+                    const int live = std::min(tcw, (pt + TS - 1) / TS);
+                    cost += nw * batch_window_cost(live * NSTEP, MB, KS, pt) + kLoadLatency;
+                }
+                consider(cost, tcw, ksi, 0, 0);
             }
         }
-    }
-    // Remainder variants (KS = 1): passes of 4 TCW + NR tiles, every consumer 4 TCW + NR steps.
-    if (ks_req == 0 || ks_req == 1) {
-        for (int ci = 0; ci < kBatchNrCombos; ci++) {
-            const int tcw = kBatchNrTcw[ci], nr = kBatchNrNr[ci];
-            if (kBatchNrLds[ci][mbi] > kMaxLds)
-                continue;
-            const int PT = kBatchConsumers * tcw + nr;
-            double cost = 0.0;
-            for (int t0 = 0; t0 < T; t0 += PT)
-                cost += nwin * batch_window_cost(4 * tcw + nr, MB, 1, std::min(PT, T - t0)) +
-                        kLoadLatency;
-            if (!found || cost < best - 1e-9) {
-                best = cost;
-                found = true;
-                P->tcw = tcw;
-                P->ksi = 0;
-                P->nr = nr;
-                P->nri = ci;
+        // Remainder variants (KS = 1): passes of 4 TCW + NR tiles, every consumer 4 TCW + NR
+        // steps.
+        if (ks_req == 0 || ks_req == 1) {
+            for (int ci = 0; ci < kBatchNrCombos; ci++) {
+                const int tcw = kBatchNrTcw[ci], nr = kBatchNrNr[ci];
+                if (kBatchNrLds[ci][mbi] > kMaxLds)
+                    continue;
+                const int PT = kBatchConsumers * tcw + nr;
+                double cost = 0.0;
+                for (int t0 = 0; t0 < T; t0 += PT)
+                    cost += nw * batch_window_cost(4 * tcw + nr, MB, 1, std::min(PT, T - t0)) +
+                            kLoadLatency;
+                consider(cost, tcw, 0, nr, ci);
             }
         }
     }
@@ -334,9 +351,36 @@ bool batch_plan(int rows, int N, int K, int ks_req, BatchPlan *P)
         return false;
     P->mbi = mbi;
     P->mb = MB;
-    P->grid = G;
     P->lds = P->nr > 0 ? kBatchNrLds[P->nri][mbi] : kBatchLds[P->tcw - 1][mbi][P->ksi];
     return true;
+}
+
+// Split-K workspace: one per device, grown (never shrunk or freed: a captured graph may still
+// hold an older one) on first need. Returns null when it would have to grow while the stream is
+// being captured, or when the allocation fails; the caller then runs without split K.
+float *batch_workspace(size_t bytes, hipStream_t stream)
+{
+    static std::mutex mu;
+    static std::map<int, std::pair<void *, size_t>> ws;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    auto &e = ws[dev];
+    if (e.first != nullptr && e.second >= bytes)
+        return static_cast<float *>(e.first);
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    e = {p, bytes};
+    return static_cast<float *>(p);
 }
 
 // Tiles of 16 columns per workgroup when every compute unit takes an equal share of the groups.
@@ -352,20 +396,27 @@ bool choose_config(int M, int N, int K, int *path, int *split)
 {
     // Automatic choice (measured on the layer shapes): the dot-product kernel for the smallest M;
     // the 16-row matrix-core kernel up to M = 16 and, up to M = 48, for narrow shapes (a few
-    // tiles per compute unit), whose weights it reads once per row block; above that the batch
-    // kernel, which decodes each weight once per 128 rows.
-    if (*path == kPathAuto)
-        *path = (M <= 4)                                           ? kPathDot
-                : (M <= 16 || (M <= 48 && tiles_per_workgroup(N) < 6)) ? kPathMfma
-                                                                       : kPathBatch;
+    // tiles per compute unit) of moderate K, whose weights it reads once per row block; above
+    // that the batch kernel, which decodes each weight once per 128 rows (and cuts K across
+    // workgroups for narrow shapes).
+    if (*path == kPathAuto) {
+        const bool narrow = tiles_per_workgroup(N) < 6 && K <= 8192;
+        *path = (M <= 4) ? kPathDot : (M <= 16 || (M <= 48 && narrow)) ? kPathMfma : kPathBatch;
+    }
     if (*path == kPathBatch) {
         if (*split != 0 && *split != 1 && *split != 2 && *split != 4)
             return false;
         BatchPlan P;
-        if (!batch_plan(std::min(M, 16 * kBatchMaxBlocks), N, K, *split, &P))
+        if (!batch_plan(std::min(M, 16 * kBatchMaxBlocks), N, K, *split, 0, &P))
             return false;
         *split = 1 << P.ksi;
         return true;
+    }
+    if (*path == kPathBatchSplit) {
+        if (*split != 2 && *split != 4 && *split != 8)
+            return false;
+        BatchPlan P;
+        return batch_plan(std::min(M, 16 * kBatchMaxBlocks), N, K, 0, *split, &P);
     }
     if (*path == kPathDot) {
         if (M > kDotMaxM)
@@ -408,27 +459,48 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
         hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * split), lds, stream, a, L);
         return hipGetLastError();
     }
-    if (path == kPathBatch) {
+    if (path == kPathBatch || path == kPathBatchSplit) {
+        const int ks_req = path == kPathBatch ? split : 0;
+        const int s_req = path == kPathBatch ? 0 : split;
         // Slabs of 128 rows, one launch each (the last one may be smaller).
         constexpr int kSlab = 16 * kBatchMaxBlocks;
         for (int m0 = 0; m0 < a.M; m0 += kSlab) {
             const int rows = std::min(kSlab, a.M - m0);
             BatchPlan P;
-            if (!batch_plan(rows, a.N, a.K, split, &P))
+            if (!batch_plan(rows, a.N, a.K, ks_req, s_req, &P))
                 return hipErrorInvalidValue;
-            const KernelFn fn = P.nr > 0 ? kBatchNr[P.nri][P.mbi] : kBatch[P.tcw - 1][P.mbi][P.ksi];
-            const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), P.lds);
-            if (e != hipSuccess)
-                return e;
             GemmArgs b = a;
             b.X = a.X + (size_t)m0 * (size_t)a.K;
             b.Y = a.Y + (size_t)m0 * (size_t)a.N;
             b.M = rows;
-            hipLaunchKernelGGL(fn, dim3((unsigned)P.grid), dim3(kWave * kBatchWaves), P.lds,
-                               stream, b);
-            const hipError_t le = hipGetLastError();
+            float *ws = nullptr;
+            const size_t stride = batch_slice_stride(rows, a.N);
+            if (P.nslice > 1) {
+                ws = batch_workspace((size_t)P.nslice * stride * sizeof(float), stream);
+                if (ws == nullptr && !batch_plan(rows, a.N, a.K, ks_req, 1, &P))
+                    return hipErrorInvalidValue;   // no workspace: run unsplit
+            }
+            const KernelFn fn = P.nr > 0 ? kBatchNr[P.nri][P.mbi] : kBatch[P.tcw - 1][P.mbi][P.ksi];
+            const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), P.lds);
+            if (e != hipSuccess)
+                return e;
+            GemmArgs kb = b;
+            if (P.nslice > 1)
+                kb.Y = ws;   // unscaled partial sums, slice by slice
+            hipLaunchKernelGGL(fn, dim3((unsigned)P.grid, (unsigned)P.nslice),
+                               dim3(kWave * kBatchWaves), P.lds, stream, kb);
+            hipError_t le = hipGetLastError();
             if (le != hipSuccess)
                 return le;
+            if (P.nslice > 1) {
+                const long long count = (long long)rows * a.N;
+                const unsigned blocks = (unsigned)((count + 4 * 256 - 1) / (4 * 256));
+                hipLaunchKernelGGL(batch_reduce_kernel, dim3(blocks), dim3(256), 0, stream, ws,
+                                   P.nslice, count, (long long)stride, a.gscale, b.Y);
+                le = hipGetLastError();
+                if (le != hipSuccess)
+                    return le;
+            }
         }
         return hipSuccess;
     }

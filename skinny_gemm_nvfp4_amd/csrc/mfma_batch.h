@@ -29,6 +29,10 @@
 //   * With KS = 1 a pass may end in NR remainder tiles (4 TCW + NR tiles): consumer c multiplies
 //     MFMA step c of each remainder tile, so every consumer does the same work per window (a
 //     workgroup of 9 tiles runs as 4 x 2 + 1 instead of 3, 2, 2, 2).
+//   * Split K (gridDim.y = S > 1): workgroup (b, s) takes windows [s nwin / S, (s + 1) nwin / S)
+//     and writes its unscaled partial sums to slice s of a workspace (a.Y, S x M x N floats);
+//     batch_reduce_kernel adds the S slices in order and applies g. Narrow shapes (a few tiles
+//     per compute unit) then read 1 / S of X per compute unit.
 //   * B = e2m1 * s decoded to bf16 (exact). The KS partial sums of a tile (or the 4 of a
 //     remainder tile) are added through LDS in a fixed order, then Y = sum * g. Results are
 //     reproducible.
@@ -67,6 +71,12 @@ struct BatchShape {
     static constexpr int RED = RED_KS > RED_NR ? RED_KS : RED_NR;
     static constexpr int LDS = MAIN > RED ? MAIN : RED;
 };
+
+// Floats between the split-K slices of the workspace: M * N rounded up to 4 (16-byte slices).
+__host__ __device__ inline size_t batch_slice_stride(int M, int N)
+{
+    return ((size_t)M * (size_t)N + 3) & ~(size_t)3;
+}
 
 // Byte position / 4 of code dword d inside a tile's 16 bytes in LDS: the order is d = 0, 2, 1, 3,
 // so that the dwords of steps ks and ks + 2 (KS = 2) are adjacent.
@@ -289,7 +299,10 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
     const int c0 = kGroupCols * g0;
     const int ncols = min(N - c0, kGroupCols * ngroups);
     const int T = (ngroups + 3) / 4;
-    const int nwin = (K + kBatchWindow - 1) / kBatchWindow;
+    const int nwin_all = (K + kBatchWindow - 1) / kBatchWindow;
+    const int nslice = gridDim.y;   // K slices
+    const int w0 = (int)(((long long)blockIdx.y * nwin_all) / nslice);
+    const int nwin = (int)(((long long)(blockIdx.y + 1) * nwin_all) / nslice) - w0;
 
     // Each role runs its own loop over the passes (tiles tc0 .. tc0 + PT - 1), so that what it
     // precomputes stays inside its branch; all roles meet the same barriers in the same order.
@@ -317,8 +330,9 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
                 coff[i] = off_if(v, lq + (uint32_t)t * (4u * gq));
                 soff[i] = off_if(v, ls + (uint32_t)t * (4u * gs));
             }
-            auto load = [&](int w, BatchWWin<S::NWP> &dst) {
-                const bool kv = w < nwin && 4 * w + q < CH;
+            auto load = [&](int wl, BatchWWin<S::NWP> &dst) {
+                const int w = w0 + wl;   // window of K
+                const bool kv = wl < nwin && 4 * w + q < CH;
                 const uint32_t cw = (uint32_t)w * (4u * kChunkCodeBytes);
                 const uint32_t sw = (uint32_t)w * (4u * kChunkScaleBytes);
 #pragma unroll
@@ -365,8 +379,9 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
             slot4[c] = (uint32_t)row0 * kBatchRowBytes +
                        16u * (uint32_t)(kp ^ ((row0 + 4 * c) & 15));
         for (int tc0 = 0; tc0 < T; tc0 += S::PT) {
-            auto load = [&](int w, BatchXWin<S::NXP> &dst) {
-                const bool v = w < nwin && kBatchWindow * w + 8 * kp < K;
+            auto load = [&](int wl, BatchXWin<S::NXP> &dst) {
+                const int w = w0 + wl;   // window of K
+                const bool v = wl < nwin && kBatchWindow * w + 8 * kp < K;
                 const uint32_t cur = xbase + (uint32_t)w * (kBatchWindow * 2);
 #pragma unroll
                 for (int i = 0; i < S::NXP; i++)
@@ -390,7 +405,10 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
         const int ts = wave % S::TS;
         const int ks = wave / S::TS;
         const uint32_t sshift = 16u * (uint32_t)(r & 1);
-        const rsrc_t ry = make_rsrc(a.Y, (uint32_t)M * (uint32_t)N * 4u);
+        // Split K: slice blockIdx.y of the workspace, unscaled; otherwise Y, times g.
+        const rsrc_t ry = make_rsrc(a.Y + (size_t)blockIdx.y * batch_slice_stride(M, N),
+                                    (uint32_t)M * (uint32_t)N * 4u);
+        const float g = nslice > 1 ? 1.0f : *a.gscale;
         for (int tc0 = 0; tc0 < T; tc0 += S::PT) {
             const int nt = max(0, min(TCW, (T - tc0 - ts + S::TS - 1) / S::TS));
             f32x4_t acc[MB][S::NACC];
@@ -435,7 +453,6 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
                 // Rows >= M lie beyond the descriptor (the whole offset is in the VGPR, which
                 // the range check covers), so their stores are dropped; so are columns past the
                 // workgroup's share.
-                const float g = *a.gscale;
 #pragma unroll
                 for (int j = 0; j < TCW; j++) {
                     const int colx = 16 * (tc0 + ts + S::TS * j) + r;
@@ -473,7 +490,6 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
                                 acc[b][TCW + rr][e];
                 batch_barrier();   // partial sums written
                 if (ts < NR) {
-                    const float g = *a.gscale;
                     const int colx = 16 * (tc0 + S::TS * TCW + ts) + r;
                     const bool cv = colx < ncols;
                     const uint32_t vo =
@@ -493,6 +509,33 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
                 }
                 batch_barrier();   // partial sums read before the next pass refills the buffers
             }
+        }
+    }
+}
+
+// Y = g * (P[0] + P[1] + ... + P[S - 1]) over count = M * N floats, slices in order (split K);
+// slice s starts at P + s * stride (batch_slice_stride). Thread t takes elements 4 t .. 4 t + 3.
+__global__ __launch_bounds__(256) void batch_reduce_kernel(const float *P, int S, long long count,
+                                                          long long stride, const float *gscale,
+                                                          float *Y)
+{
+    const long long e0 = 4 * ((long long)blockIdx.x * blockDim.x + threadIdx.x);
+    if (e0 >= count)
+        return;
+    const float g = *gscale;
+    if (e0 + 3 < count) {
+        f32x4_t v = *reinterpret_cast<const f32x4_t *>(P + e0);
+        for (int s = 1; s < S; s++)
+            v += *reinterpret_cast<const f32x4_t *>(P + s * stride + e0);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            Y[e0 + i] = v[i] * g;
+    } else {
+        for (long long e = e0; e < count; e++) {
+            float v = P[e];
+            for (int s = 1; s < S; s++)
+                v += P[s * stride + e];
+            Y[e] = v * g;
         }
     }
 }

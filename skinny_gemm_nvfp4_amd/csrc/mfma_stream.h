@@ -110,7 +110,7 @@ struct MfmaWindow {
     }
 };
 
-template <int TC, int W, bool FAST>
+template <int TC, int W, bool FAST, int D = 2>
 __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -146,9 +146,10 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const uint32_t ts = 4u * gs;
     const int xk = 8 * r;    // k of the lane's X piece within the window
     const uint32_t xo = ((uint32_t)(lane >> 4) * (uint32_t)K + (uint32_t)xk) * 2u;
-    uint8_t *xbuf0 = lds + wave * 2 * kXBufBytes;
-    uint8_t *xbuf1 = xbuf0 + kXBufBytes;
+    uint8_t *xbuf[2] = {lds + wave * 2 * kXBufBytes, lds + wave * 2 * kXBufBytes + kXBufBytes};
     const float g = *a.gscale;
+    // This wavefront's windows: wave, wave + W, ...; window i of the wavefront is wave + i W.
+    const int nmine = (nwin - wave + W - 1) / W;
 
     for (int tc0 = 0; tc0 < T; tc0 += TC) {
         const int nt = min(TC, T - tc0);
@@ -157,28 +158,31 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
         for (int t = 0; t < TC; t++)
             acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-        MfmaWindow<TC> wa, wb;
-        int w = wave;
-        wa.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w, w < nwin, tc0, ngroups, gr,
-                               q, CH, K);
-        wa.stage(xbuf0, lane);
-        while (w < nwin) {
-            wb.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w + W, w + W < nwin, tc0,
-                                   ngroups, gr, q, CH, K);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-            wa.mul(acc, xbuf0, r, q, nt, sshift);
-            __builtin_amdgcn_sched_barrier(0);
-            wb.stage(xbuf1, lane);
-            w += W;
-            if (w >= nwin)
-                break;
-            wa.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w + W, w + W < nwin, tc0,
-                                   ngroups, gr, q, CH, K);
-            __builtin_amdgcn_sched_barrier(0);
-            wb.mul(acc, xbuf1, r, q, nt, sshift);
-            __builtin_amdgcn_sched_barrier(0);
-            wa.stage(xbuf0, lane);
-            w += W;
+        // Ring of D windows: D - 1 in flight while one is multiplied. Window i sits in ring slot
+        // i % D and, once its X is staged, in X buffer i & 1.
+        MfmaWindow<TC> ring[D];
+        auto load = [&](int i, MfmaWindow<TC> &win) {
+            const int w = wave + i * W;
+            win.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w, i < nmine, tc0,
+                                    ngroups, gr, q, CH, K);
+        };
+#pragma unroll
+        for (int i = 0; i < D - 1; i++)
+            load(i, ring[i]);
+        ring[0].stage(xbuf[0], lane);
+        for (int i0 = 0; i0 < nmine; i0 += D) {
+#pragma unroll
+            for (int u = 0; u < D; u++) {
+                const int i = i0 + u;
+                if (i < nmine) {
+                    load(i + D - 1, ring[(u + D - 1) % D]);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
+                    ring[u].mul(acc, xbuf[i & 1], r, q, nt, sshift);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (i + 1 < nmine)
+                        ring[(u + 1) % D].stage(xbuf[(i + 1) & 1], lane);
+                }
+            }
         }
 
         // acc[t][e] is the partial Y[m0 + 4 q + e][c0 + 16 (tc0 + t) + r] of this wavefront.

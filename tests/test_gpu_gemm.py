@@ -148,3 +148,29 @@ def test_batch_remainder_tiles(device, M, N, split):
     say(f"remainder path=batch split={split} M={M} N={N} K={K}")
     Y = gpu_gemm(X, to_device_packed(Wq, Ws, g, device), device, nv.PATH_BATCH, split)
     check_close(Y, Yref, A, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K,S", [(128, 1000, 2048, 2), (128, 1000, 2048, 8), (33, 520, 1040, 4),
+                                     (131, 300, 512, 4), (16, 257, 272, 2)])
+def test_batch_split_k(device, M, N, K, S):
+    """K cut into S slices across workgroups: partial sums in the workspace, added in slice order
+    by the reduce kernel (ragged K slices, ragged rows, two 128-row slabs)."""
+    X, Wq, Ws, g = random_case(700 + M + N + S, M, N, K, FINITE_SCALES)
+    Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
+    say(f"split-k S={S} M={M} N={N} K={K}")
+    packed = to_device_packed(Wq, Ws, g, device)
+    Y = gpu_gemm(X, packed, device, nv.PATH_BATCH_SPLITK, S)
+    check_close(Y, Yref, A, f"S={S} M={M} N={N} K={K}")
+    Y2 = gpu_gemm(X, packed, device, nv.PATH_BATCH_SPLITK, S)
+    assert np.array_equal(Y, Y2), "split K not reproducible"
+
+
+def test_auto_narrow_m128_splits_k(device):
+    """nvfp4_gemm on a narrow shape at M = 128 (few column tiles per compute unit), where the
+    planner cuts K across workgroups."""
+    M, N, K = 128, 2048, 4096
+    X, Wq, Ws, g = random_case(811, M, N, K, FINITE_SCALES)
+    Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
+    say(f"auto narrow M={M} N={N} K={K}")
+    Y = gpu_gemm(X, to_device_packed(Wq, Ws, g, device), device, nv.PATH_AUTO, 0)
+    check_close(Y, Yref, A, f"M={M} N={N} K={K}")
