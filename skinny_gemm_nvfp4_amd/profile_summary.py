@@ -6,7 +6,9 @@ Inputs are the CSV files rocprofv3 writes with ``-f csv``:
 
 GEMM dispatches are the kernels of the ``nvfp4::`` namespace other than the pack kernels. They
 are matched in launch order with the labels ``bench.py --launch-log`` wrote, so every duration
-and counter is attributed to a named GEMM of a named workload.
+and counter is attributed to a named GEMM of a named workload. A split-K call is two dispatches
+(the batch kernel, then ``batch_reduce_kernel``); the second is folded into the first: the
+duration spans both, counters are summed.
 
 HBM traffic: FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch but, on this part, do not
 necessarily count every memory channel; each is therefore scaled by bytes / counter of the
@@ -30,6 +32,7 @@ from collections import OrderedDict
 
 PACK_KERNELS = ("pack_clear_kernel", "pack_amax_kernel", "pack_scale_kernel",
                 "pack_quant_kernel")
+REDUCE_KERNEL = "batch_reduce_kernel"   # second dispatch of a split-K GEMM call
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -56,6 +59,7 @@ def read_trace(path: str):
                 "id": int(r["Dispatch_Id"]),
                 "name": r["Kernel_Name"],
                 "start": int(r["Start_Timestamp"]),
+                "end": int(r["End_Timestamp"]),
                 "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
                 "grid": (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"])),
                 "wg": int(r["Workgroup_Size_X"]),
@@ -79,9 +83,29 @@ def read_counters(path: str):
     return [per[k] for k in sorted(per)]
 
 
+def fold_reductions(gemms):
+    """Folds each split-K reduce dispatch into the GEMM dispatch before it."""
+    out = []
+    for d in gemms:
+        if REDUCE_KERNEL in d["name"]:
+            if not out:
+                raise ValueError("a split-K reduce dispatch with no GEMM dispatch before it")
+            prev = out[-1]
+            if "end" in d and "start" in prev:   # kernel trace: span of both dispatches
+                prev["end"] = d["end"]
+                prev["ns"] = prev["end"] - prev["start"]
+            for k, v in d.items():               # counter collection: sums
+                if k.isupper() and isinstance(v, float):
+                    prev[k] = prev.get(k, 0.0) + v
+            prev["split_k"] = True
+            continue
+        out.append(d)
+    return out
+
+
 def attach_labels(dispatches, labels):
     """Pairs the GEMM dispatches with the launch log. Raises if the counts differ."""
-    gemms = [d for d in dispatches if is_gemm(d["name"])]
+    gemms = fold_reductions([d for d in dispatches if is_gemm(d["name"])])
     if len(gemms) != len(labels):
         raise ValueError(f"{len(gemms)} GEMM dispatches in the profile but {len(labels)} "
                          "labels in the launch log")
@@ -104,8 +128,9 @@ def trace_summary(trace_csv: str, labels_path: str) -> str:
     for lab, ds in group(gemms).items():
         us = [d["ns"] / 1e3 for d in ds]
         d0 = ds[0]
+        kname = short_name(d0["name"]) + (" +reduce" if d0.get("split_k") else "")
         lines.append(
-            f"{lab:44s} {short_name(d0['name'])[:44]:44s} {len(us):4d} "
+            f"{lab:44s} {kname[:44]:44s} {len(us):4d} "
             f"{statistics.fmean(us):8.2f} {statistics.median(us):8.2f} {min(us):8.2f}  "
             f"{d0['grid'][0]:>5d}x{d0['grid'][1]:<4d} {d0['wg']:5d} {d0['lds']:6d} "
             f"{d0['vgpr']:4d} {d0['agpr']:4d} {d0['scratch']:6d}")
