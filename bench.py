@@ -18,6 +18,10 @@ Protocol
   * The GPU output is checked against the oracle, and the oracle itself is timed on the host
     cores on the same layer (cpu_baseline).
   * "also": the verify shapes at M = 16 and M = 128, timed the same way (per-kernel events).
+  * "full_pass": 64 layers of those shapes plus an NVFP4 lm_head (N = 151936), 12.33 GB of
+    packed weights (weights seed 9 drawn on the device one tensor at a time and packed, x seed
+    10), at M = 1 and M = 16: the 257 GEMMs captured as one HIP graph per M, replays timed with
+    HIP events. 12.33 GB is 48x the Infinity Cache, so every pass streams from HBM.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -187,6 +191,63 @@ def cpu_baseline(workload, seconds: float):
     return rec, refs
 
 
+def full_pass(dev, launches, reps: int):
+    """The whole synthetic weight pass (64 dense layers + lm_head) at M = 1 and M = 16."""
+    import torch
+    import skinny_gemm_nvfp4_amd as nv
+    from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+    shapes = inputs.full_pass_shapes()
+    gen = torch.Generator(device=dev).manual_seed(9)
+    packed = []
+    for name, K, N in shapes:
+        W = inputs.weights_on_device(gen, K, N, dev)
+        packed.append(nv.pack(W))
+        del W
+    torch.cuda.synchronize()
+    weight_bytes = sum(rl.weight_bytes(K, N) for _, K, N in shapes)
+    out = {"gemms": len(shapes), "weight_bytes": weight_bytes,
+           "timing": "HIP events around replays of one graph holding the whole pass"}
+    for M in (1, 16):
+        xs = {K: x.to(dev) for K, x in inputs.full_pass_activations(M).items()}
+        ys = {N: torch.empty((M, N), dtype=torch.float32, device=dev)
+              for N in {N for _, _, N in shapes}}
+        labels = [f"full_pass_m{M}.{name.split('.')[-1]} M={M} N={N} K={K}"
+                  for name, K, N in shapes]
+
+        def one_pass():
+            for (_, K, N), p in zip(shapes, packed):
+                nv.gemm(xs[K], *p, out=ys[N])
+
+        one_pass()                                     # eager: one-time set-up
+        torch.cuda.synchronize()
+        launches.extend(labels)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_pass()
+        graph.replay()                                 # warm
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        launches.extend(labels * (reps + 1))
+        ms = e0.elapsed_time(e1) / reps
+        total = sum(rl.compulsory_bytes(M, N, K) for _, K, N in shapes)
+        gbs = total / (ms * 1e-3) / 1e9
+        out[f"m{M}"] = {"ms_per_pass": round(ms, 4), "bytes_per_pass": total,
+                        "GB_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / rl.HBM_PEAK_GBS, 2),
+                        "passes_per_s": round(1e3 / ms, 1),
+                        "equiv_tok_s_17_9GB": round(gbs / EQUIV_MODEL_GB, 1)}
+        del graph, xs, ys
+    del packed
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +257,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the M=16 / M=128 shapes")
+    ap.add_argument("--no-full-pass", action="store_true",
+                    help="skip the 64-layer + lm_head weight pass at M=1 and M=16")
+    ap.add_argument("--full-pass-reps", type=int, default=20)
     ap.add_argument("--launch-log", default=None,
                     help="write the label of every GEMM dispatch, in order, to this file (for "
                          "matching a rocprofv3 kernel trace to the GEMMs)")
@@ -309,6 +373,11 @@ def main() -> int:
             del lay
             torch.cuda.empty_cache()
 
+    fp = None
+    if not args.no_full_pass:
+        log("generating, packing and timing the full weight pass (64 layers + lm_head)")
+        fp = full_pass(dev, launches, max(1, args.full_pass_reps))
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -327,6 +396,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "parity": parity,
         "also": also,
+        "full_pass": fp,
         "source_hash": ps.source_hash(),
     }
     if args.launch_log:
