@@ -15,8 +15,13 @@ necessarily count every memory channel; each is therefore scaled by bytes / coun
 calibration copy bench.py runs first (the largest ``__amd_rocclr_copyBuffer`` dispatch, a plain
 device-to-device copy of ``--calibration-bytes``).
 
+MFMA busy (``mfma``): SQ_VALU_MFMA_BUSY_CYCLES counts the matrix-core busy cycles of every SIMD
+(16 per v_mfma_f32_16x16x32_bf16); GRBM_GUI_ACTIVE counts the active cycles of the dispatch,
+summed over the XCDs. Busy fraction = MFMA busy / (SIMDs x GRBM_GUI_ACTIVE / XCDs).
+
 Usage:
   python -m skinny_gemm_nvfp4_amd.profile_summary trace --trace T.csv --labels L.txt
+  python -m skinny_gemm_nvfp4_amd.profile_summary mfma --counters C.csv --labels L.txt
   python -m skinny_gemm_nvfp4_amd.profile_summary traffic --fetch F.csv --write W.csv \
       --labels L.txt [--calibration-bytes B] [--json profiles/traffic.json]
 """
@@ -137,6 +142,24 @@ def trace_summary(trace_csv: str, labels_path: str) -> str:
     return "\n".join(lines)
 
 
+MI355X_SIMDS = 256 * 4    # 256 compute units of 4 SIMDs
+MI355X_XCDS = 8
+
+
+def mfma_summary(counters_csv: str, labels_path: str) -> str:
+    gemms = attach_labels(read_counters(counters_csv), read_labels(labels_path))
+    lines = [f"{'GEMM':48s} {'n':>4s} {'MFMA instr':>11s} {'busy cycles':>12s} "
+             f"{'active cyc':>11s} {'busy %':>7s}"]
+    for lab, ds in group(gemms).items():
+        med = {k: statistics.median(d.get(k, 0.0) for d in ds)
+               for k in ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")}
+        active = med["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+        frac = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (MI355X_SIMDS * active) if active else 0.0
+        lines.append(f"{lab:48s} {len(ds):4d} {med['SQ_INSTS_MFMA']:11.4g} "
+                     f"{med['SQ_VALU_MFMA_BUSY_CYCLES']:12.4g} {active:11.4g} {100 * frac:7.1f}")
+    return "\n".join(lines)
+
+
 def calibration(dispatches, counter: str, nbytes: int) -> float:
     copies = [d for d in dispatches if d["name"].startswith(COPY_KERNEL) and counter in d]
     if not copies:
@@ -195,9 +218,15 @@ def main(argv=None) -> int:
     w.add_argument("--labels", required=True)
     w.add_argument("--calibration-bytes", type=int, default=256 << 20)
     w.add_argument("--json", default=None, help="also merge bytes per launch into this file")
+    m = sub.add_parser("mfma")
+    m.add_argument("--counters", required=True)
+    m.add_argument("--labels", required=True)
     args = ap.parse_args(argv)
     if args.cmd == "trace":
         print(trace_summary(args.trace, args.labels))
+        return 0
+    if args.cmd == "mfma":
+        print(mfma_summary(args.counters, args.labels))
         return 0
     kf, kw, rows = traffic_summary(args.fetch, args.write, args.labels, args.calibration_bytes)
     print(f"calibration: FETCH_SIZE x {kf:.4f}, WRITE_SIZE x {kw:.4f} "

@@ -75,3 +75,50 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path):
     assert r["fetch_bytes"] == 200 * 1024 * 2       # median of 100, 300, 200 KiB, x2
     assert r["write_bytes"] == 1 * 1024 * 8
     assert r["bytes_per_launch"] == r["fetch_bytes"] + r["write_bytes"]
+
+
+BATCH = "void nvfp4::mfma_batch_kernel<3, 8, 1, 0>(nvfp4::GemmArgs)"
+REDUCE = "nvfp4::batch_reduce_kernel(float const*, int, long long, long long, float const*, float*)"
+
+
+def test_split_k_reduce_is_folded_into_its_gemm(tmp_path):
+    # batch kernel 100..2100 ns, its reduce 2200..2700: one GEMM of 2.6 us; then a plain GEMM
+    _trace(tmp_path / "t.csv", [(BATCH, 100, 2000), (REDUCE, 2200, 500), (GEMM, 5000, 1000)])
+    (tmp_path / "l.txt").write_text("s M=128 N=16 K=64\np M=1 N=16 K=64\n")
+    lines = ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt")).splitlines()
+    assert len(lines) == 3
+    assert "+reduce" in lines[1] and "    2.60" in lines[1]
+    assert "+reduce" not in lines[2] and "    1.00" in lines[2]
+
+
+def test_split_k_counters_are_summed(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    _pmc(tmp_path / "f.csv", [(copy, [512.0]), (BATCH, [100.0]), (REDUCE, [50.0])], "FETCH_SIZE")
+    _pmc(tmp_path / "w.csv", [(copy, [1024.0]), (BATCH, [10.0]), (REDUCE, [5.0])], "WRITE_SIZE")
+    (tmp_path / "l.txt").write_text("s M=128 N=16 K=64\n")
+    _, _, rows = ps.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                    str(tmp_path / "l.txt"), 1 << 20)
+    assert rows["s M=128 N=16 K=64"]["fetch_bytes"] == 150 * 1024 * 2
+    assert rows["s M=128 N=16 K=64"]["write_bytes"] == 15 * 1024
+
+
+def test_reduce_without_a_gemm_is_an_error(tmp_path):
+    _trace(tmp_path / "t.csv", [(REDUCE, 100, 500)])
+    (tmp_path / "l.txt").write_text("s\n")
+    with pytest.raises(ValueError):
+        ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt"))
+
+
+def test_mfma_busy_fraction(tmp_path):
+    # 1000 MFMAs of 16 busy cycles on one SIMD's share: busy = 16000 over 1024 SIMDs of a
+    # dispatch active for 8 XCDs x 100 cycles -> 16000 / (1024 * 100) = 15.6 %
+    with open(tmp_path / "c.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, PMC_COLS)
+        w.writeheader()
+        for name, value in (("SQ_INSTS_MFMA", 1000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 16000.0),
+                            ("GRBM_GUI_ACTIVE", 800.0)):
+            w.writerow({**{c: 0 for c in PMC_COLS}, "Dispatch_Id": 1, "Kernel_Name": BATCH,
+                        "Grid_Size": 256, "Counter_Name": name, "Counter_Value": value})
+    (tmp_path / "l.txt").write_text("m M=128 N=16 K=64\n")
+    lines = ps.mfma_summary(str(tmp_path / "c.csv"), str(tmp_path / "l.txt")).splitlines()
+    assert lines[1].startswith("m M=128") and lines[1].rstrip().endswith("15.6")
