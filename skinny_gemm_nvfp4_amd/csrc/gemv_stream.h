@@ -5,9 +5,9 @@
 // reaches the HBM roof only if every compute unit keeps the same number of bytes in flight until
 // the very end, so the work is split evenly by construction instead of by tile count:
 //
-//   * One workgroup of W wavefronts per compute unit. Workgroup b owns the 4-column groups
-//     [b NG / G, (b + 1) NG / G) of the NG groups, so all hold the same number of weight bytes
-//     (to within one group).
+//   * One workgroup of W wavefronts per compute unit. With NG = q G + r 4-column groups,
+//     workgroup b owns q + (b < r) consecutive groups from b q + min(b, r), so all hold the same
+//     number of weight bytes (to within one group).
 //   * A unit is one (group, 512-k window) pair: 16 chunks of 32 k x 4 columns, 1 KB of codes in
 //     one contiguous piece of the packed layout. Lane l of a wavefront reads its 16 bytes at
 //     16 l: column l % 4 of the group, chunk l / 4 of the window. The units of a workgroup,
@@ -24,6 +24,10 @@
 //     wavefront order (= k order) at the end, times the tensor scale g. Results are reproducible.
 //   * FAST (K % 512 == 0) needs no per-lane K test; otherwise a lane whose chunk is past the
 //     last one reads zeros instead of the next group's bytes.
+//   * The set-up before the first weight load is kept short: a wavefront issues about one
+//     instruction per four cycles, and every instruction before the loads delays the first
+//     bytes. The launcher passes the split of the groups and 1 / nwin, so the set-up has no
+//     64-bit and no generic integer division.
 #pragma once
 
 #include "device.h"
@@ -43,12 +47,27 @@ struct StreamLayout {
     int slots;       // most wavefronts one group is split over
     int x_bytes;     // M * row_bytes
     int part_bytes;  // ngroups * slots * MR * 4 floats
+    int gq, gr;      // NG = gq G + gr: workgroup b owns gq + (b < gr) groups
+    float rnwin;     // 1.0f / nwin
 };
 
 // First wavefront of the W whose run [u0(w), u0(w+1)), u0(w) = floor(w units / W), holds unit u.
 __host__ __device__ inline int stream_owner(long long u, int W, long long units)
 {
     return (int)(((u + 1) * W - 1) / units);
+}
+
+// floor(x / d) for x < 2^22, given rd = 1.0f / d rounded to nearest. The float estimate is within
+// one of the quotient and is corrected with the exact remainder.
+__device__ __forceinline__ uint32_t div_small(uint32_t x, uint32_t d, float rd)
+{
+    uint32_t q = (uint32_t)((float)x * rd);
+    const int r = (int)(x - q * d);
+    if (r < 0)
+        q--;
+    else if (r >= (int)d)
+        q++;
+    return q;
 }
 
 template <int MR, int W, int D, bool FAST>
@@ -64,15 +83,17 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     const int N = a.N;
     const int CH = num_chunks(K);
     const int NG = num_groups(N);
-    const int G = gridDim.x;
-    const int g0 = (int)(((long long)blockIdx.x * NG) / G);
-    const int ngroups = (int)(((long long)(blockIdx.x + 1) * NG) / G) - g0;
+    const int b = blockIdx.x;
+    const int g0 = b * L.gq + min(b, L.gr);
+    const int ngroups = L.gq + (b < L.gr ? 1 : 0);
     const int c0 = kGroupCols * g0;
     const int ncols = min(N - c0, kGroupCols * ngroups);
     const int nwin = L.nwin;
-    const long long units = (long long)ngroups * nwin;
-    const int u0 = (int)(((long long)wave * units) / W);
-    const int u1 = (int)(((long long)(wave + 1) * units) / W);
+    const uint32_t units = (uint32_t)ngroups * (uint32_t)nwin;   // < 2^21
+    auto run_start = [&](int w) { return (int)(((uint32_t)w * units) / (uint32_t)W); };
+    const int u0 = run_start(wave);
+    const int u1 = run_start(wave + 1);
+    const int gstart = (int)div_small((uint32_t)u0, (uint32_t)nwin, L.rnwin);
 
     const uint32_t gq = (uint32_t)CH * kChunkCodeBytes;    // code bytes per group
     const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;   // scale bytes per group
@@ -86,7 +107,7 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
 
     // Prefetch cursor: unit up = (gp, wp).
     int up = u0;
-    int gp = u0 / nwin;
+    int gp = gstart;
     int wp = u0 - gp * nwin;
     auto load_next = [&]() -> Chunk {
         Chunk c;
@@ -119,7 +140,7 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
 #pragma unroll
     for (int i = 0; i < kXPerThread; i++) {
         const int idx = threadIdx.x + i * kWave * W;
-        const int m = idx / row_pieces;
+        const int m = MR == 1 ? 0 : (int)div_small((uint32_t)idx >> 6, (uint32_t)nwin, L.rnwin);
         const int e = idx - m * row_pieces;
         const uint32_t src = ((uint32_t)m * (uint32_t)K + (uint32_t)e * 8u) * 2u;
         xv0[i] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -135,14 +156,15 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     for (int i = 0; i < kXPerThread; i++) {
         const int idx = threadIdx.x + i * kWave * W;
         if (idx < xpieces) {
-            const int m = idx / row_pieces;
+            const int m =
+                MR == 1 ? 0 : (int)div_small((uint32_t)idx >> 6, (uint32_t)nwin, L.rnwin);
             const int e = idx - m * row_pieces;
             *reinterpret_cast<u32x4_t *>(lds + m * L.row_bytes + (e >> 2) * kStreamSlot +
                                          16 * (e & 3)) = xv0[i];
         }
     }
     for (int idx = threadIdx.x + kXPerThread * kWave * W; idx < xpieces; idx += kWave * W) {
-        const int m = idx / row_pieces;
+        const int m = (int)div_small((uint32_t)idx >> 6, (uint32_t)nwin, L.rnwin);
         const int e = idx - m * row_pieces;
         const uint32_t src = ((uint32_t)m * (uint32_t)K + (uint32_t)e * 8u) * 2u;
         const u32x4_t v =
@@ -162,9 +184,12 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     for (int m = 0; m < MR; m++)
         acc[m] = 0.0f;
     // Compute cursor: unit uc = (gc, wc); slot of the current group for this wavefront.
-    int gc = u0 / nwin;
+    int gc = gstart;
     int wc = u0 - gc * nwin;
-    int slot = (gc * nwin >= u0) ? 0 : wave - stream_owner((long long)gc * nwin, W, units);
+    // Slot = number of earlier wavefronts whose runs reach into group gc.
+    int slot = 0;
+    for (int w = wave; w > 0 && run_start(w) > gc * nwin; w--)
+        slot++;
     const uint32_t xlane = (uint32_t)j * kStreamSlot;
 
     auto flush = [&]() {
@@ -223,11 +248,12 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     __syncthreads();
 
     const float g = *a.gscale;
-    for (int idx = threadIdx.x; idx < ncols * MR; idx += kWave * W) {
-        const int m = idx / ncols;
-        const int c = idx - m * ncols;
-        if (m < a.M) {
-            const int grp = c / 4;
+#pragma unroll
+    for (int m = 0; m < MR; m++) {
+        if (m >= a.M)
+            break;
+        for (int c = threadIdx.x; c < ncols; c += kWave * W) {
+            const int grp = c >> 2;
             float sum = 0.0f;
             for (int sl = 0; sl < L.slots; sl++)
                 sum += part[((grp * L.slots + sl) * MR + m) * 4 + (c & 3)];

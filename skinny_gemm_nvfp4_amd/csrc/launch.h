@@ -25,6 +25,18 @@ constexpr int kChunkCodeBytes = kGroupCols * 16;   // 64
 constexpr int kChunkScaleBytes = kGroupCols * 2;   // 8
 
 __host__ __device__ inline int num_groups(int N) { return (N + kGroupCols - 1) / kGroupCols; }
+
+// The NG column groups dealt to G workgroups: NG / G each and one more to the first NG % G, so
+// every workgroup streams the same weight bytes to within one group. Workgroup b owns groups
+// [*first, *first + *count). 32-bit arithmetic only (a 64-bit division costs the kernel hundreds
+// of scalar instructions before its first load).
+__device__ __forceinline__ void group_range(int NG, int G, int b, int *first, int *count)
+{
+    const uint32_t q = (uint32_t)NG / (uint32_t)G;
+    const uint32_t r = (uint32_t)NG - q * (uint32_t)G;
+    *first = (int)((uint32_t)b * q + min((uint32_t)b, r));
+    *count = (int)(q + ((uint32_t)b < r ? 1u : 0u));
+}
 __host__ __device__ inline int num_chunks(int K) { return (K + kChunkK - 1) / kChunkK; }
 
 // Byte offset of the 16 code bytes of (column n, chunk c) and of the scale pair of the same.

@@ -5,9 +5,9 @@
 // bounds the kernel, so every weight is decoded once per workgroup and multiplied against all
 // row blocks of X while it sits in registers.
 //
-// Work split (one workgroup of 8 wavefronts per compute unit; workgroup b owns the 4-column groups
-// [b NG / G, (b + 1) NG / G), i.e. T tiles of 16 columns, for all of K and one slab of at most
-// 16 MB rows of X; the tiles are taken PT = 4 TCW / KS at a time)
+// Work split (one workgroup of 8 wavefronts per compute unit; workgroup b owns NG / G or
+// NG / G + 1 consecutive 4-column groups (group_range), i.e. T tiles of 16 columns, for all of K
+// and one slab of at most 16 MB rows of X; the tiles are taken PT = 4 TCW / KS at a time)
 //   * K is cut into windows of 128 (4 chunks of 32). Every window passes through LDS once, in two
 //     buffers, with one barrier per window:
 //       - wavefronts 4 and 5 load X: rows 8 MB p .. 8 MB p + 8 MB - 1 of the window, as 16-byte
@@ -293,16 +293,17 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
     const int M = a.M;   // rows of this slab: 16 (MB - 1) < M <= 16 MB
     const int CH = num_chunks(K);
     const int NG = num_groups(N);
-    const int G = gridDim.x;
-    const int g0 = (int)(((long long)blockIdx.x * NG) / G);
-    const int ngroups = (int)(((long long)(blockIdx.x + 1) * NG) / G) - g0;
+    int g0, ngroups;
+    group_range(NG, (int)gridDim.x, (int)blockIdx.x, &g0, &ngroups);
     const int c0 = kGroupCols * g0;
     const int ncols = min(N - c0, kGroupCols * ngroups);
     const int T = (ngroups + 3) / 4;
     const int nwin_all = (K + kBatchWindow - 1) / kBatchWindow;
     const int nslice = gridDim.y;   // K slices
-    const int w0 = (int)(((long long)blockIdx.y * nwin_all) / nslice);
-    const int nwin = (int)(((long long)(blockIdx.y + 1) * nwin_all) / nslice) - w0;
+    // nwin_all <= 2^15 and nslice <= 8: 32-bit products and divisions suffice.
+    const int w0 = (int)(((uint32_t)blockIdx.y * (uint32_t)nwin_all) / (uint32_t)nslice);
+    const int nwin =
+        (int)(((uint32_t)(blockIdx.y + 1) * (uint32_t)nwin_all) / (uint32_t)nslice) - w0;
 
     // Each role runs its own loop over the passes (tiles tc0 .. tc0 + PT - 1), so that what it
     // precomputes stays inside its branch; all roles meet the same barriers in the same order.

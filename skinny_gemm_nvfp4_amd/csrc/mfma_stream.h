@@ -6,9 +6,9 @@
 // rows run as more 16-row blocks (blockIdx.y).
 //
 // Work split
-//   * One workgroup of W wavefronts per compute unit and row block; workgroup b owns the 4-column
-//     groups [b NG / G, (b + 1) NG / G) (equal weight bytes per compute unit). Four consecutive
-//     groups form a tile of 16 columns; the tiles are taken TC at a time.
+//   * One workgroup of W wavefronts per compute unit and row block; workgroup b owns NG / G or
+//     NG / G + 1 consecutive 4-column groups (group_range: equal weight bytes per compute unit).
+//     Four consecutive groups form a tile of 16 columns; the tiles are taken TC at a time.
 //   * K is cut into windows of 128 (4 chunks of 32); wavefront w owns the windows w, w + W, ...
 //     and, for those windows, every tile of the chunk.
 //   * Lane l = 16 q + r holds column r of the tile: it loads the 16 code bytes of chunk q of the
@@ -122,9 +122,8 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const int N = a.N;
     const int CH = num_chunks(K);
     const int NG = num_groups(N);
-    const int G = gridDim.x;
-    const int g0 = (int)(((long long)blockIdx.x * NG) / G);
-    const int ngroups = (int)(((long long)(blockIdx.x + 1) * NG) / G) - g0;
+    int g0, ngroups;
+    group_range(NG, (int)gridDim.x, (int)blockIdx.x, &g0, &ngroups);
     const int c0 = kGroupCols * g0;
     const int ncols = min(N - c0, kGroupCols * ngroups);
     const int T = (ngroups + 3) / 4;   // tiles of 16 columns
