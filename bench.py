@@ -18,6 +18,8 @@ Protocol
   * The GPU output is checked against the oracle, and the oracle itself is timed on the host
     cores on the same layer (cpu_baseline).
   * "also": the verify shapes at M = 16 and M = 128, timed the same way (per-kernel events).
+  * "invariant": the same three workloads in the batch-invariant mode (NVFP4_PATH_INVARIANT: row m
+    of Y is the same bits for any M), timed the same way.
   * "full_pass": 64 layers of those shapes plus an NVFP4 lm_head (N = 151936), 12.33 GB of
     packed weights (weights seed 9 drawn on the device one tensor at a time and packed, x seed
     10), at M = 1 and M = 16: the 257 GEMMs captured as one HIP graph per M, replays timed with
@@ -71,6 +73,7 @@ class Layer:
         import torch
         import skinny_gemm_nvfp4_amd as nv
         self.tag = tag
+        self.path = nv.PATH_AUTO   # nvfp4_gemm; PATH_INVARIANT times the batch-invariant mode
         self.launches = launches   # labels of the GEMM dispatches, in launch order
         self.capturing = False
         self.names = [g.name for g in gemms]
@@ -93,13 +96,15 @@ class Layer:
 
     def run(self, c: int, i: int) -> None:
         import skinny_gemm_nvfp4_amd as nv
-        nv.gemm(self.X[i], *self.packed[i][c], out=self.Y[i])
+        nv.gemm(self.X[i], *self.packed[i][c], out=self.Y[i], path=self.path)
         if not self.capturing:
             self.launches.append(self.label(i))
 
     def label(self, i: int) -> str:
+        import skinny_gemm_nvfp4_amd as nv
         M, N, K = self.shapes[i]
-        return f"{self.tag}.{self.names[i]} M={M} N={N} K={K}"
+        mode = "invariant." if self.path == nv.PATH_INVARIANT else ""
+        return f"{mode}{self.tag}.{self.names[i]} M={M} N={N} K={K}"
 
     def replayed(self) -> None:
         """Record the dispatches of one graph replay of `step`."""
@@ -260,6 +265,8 @@ def main() -> int:
     ap.add_argument("--no-full-pass", action="store_true",
                     help="skip the 64-layer + lm_head weight pass at M=1 and M=16")
     ap.add_argument("--full-pass-reps", type=int, default=20)
+    ap.add_argument("--no-invariant", action="store_true",
+                    help="skip timing the batch-invariant mode (NVFP4_PATH_INVARIANT)")
     ap.add_argument("--launch-log", default=None,
                     help="write the label of every GEMM dispatch, in order, to this file (for "
                          "matching a rocprofv3 kernel trace to the GEMMs)")
@@ -362,6 +369,15 @@ def main() -> int:
             raise RuntimeError(f"GPU output outside tolerance (worst ratio {worst})")
 
     also = {}
+    invariant = {}
+    if not args.no_invariant:
+        # The batch-invariant mode (row m of Y the same bits for any M) on the same layer.
+        log("timing the batch-invariant mode on dense_layer_m1")
+        layer.path = nv.PATH_INVARIANT
+        ius = layer.kernel_times_us(max(64, args.steps // 2))
+        invariant["dense_layer_m1"] = {n: gemm_report(s, t)
+                                       for n, s, t in zip(layer.names, layer.shapes, ius)}
+        layer.path = nv.PATH_AUTO
     if not args.no_also:
         for wname, make in (("verify_m16", inputs.verify_m16),
                             ("batched_verify_m128", inputs.batched_verify_m128)):
@@ -370,6 +386,11 @@ def main() -> int:
             lay = Layer(w.gemms, C, dev, wname, launches)
             us = lay.kernel_times_us(max(64, args.steps))
             also[wname] = {n: gemm_report(s, t) for n, s, t in zip(lay.names, lay.shapes, us)}
+            if not args.no_invariant:
+                lay.path = nv.PATH_INVARIANT
+                ius = lay.kernel_times_us(max(64, args.steps // 2))
+                invariant[wname] = {n: gemm_report(s, t)
+                                    for n, s, t in zip(lay.names, lay.shapes, ius)}
             del lay
             torch.cuda.empty_cache()
 
@@ -396,6 +417,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "parity": parity,
         "also": also,
+        "invariant": invariant or None,
         "full_pass": fp,
         "source_hash": ps.source_hash(),
     }

@@ -48,8 +48,8 @@
  *     first call that needs it, grown when a call needs more, never freed before the process ends
  *     (a captured graph may still use it). A call that would have to allocate while its stream is
  *     being captured runs without split K instead; run one such call eagerly first.
- *     Because the workspace is shared, calls that may split K (M > 16, or NVFP4_PATH_BATCH_SPLITK)
- *     must not run concurrently on different streams of the same device.
+ *     Because the workspace is shared, calls that may split K (M > 16, NVFP4_PATH_BATCH_SPLITK or
+ *     NVFP4_PATH_INVARIANT) must not run concurrently on different streams of the same device.
  *   - Sizes: 1 <= M, 1 <= N, 16 <= K <= 4194304 (2^22), K % 16 == 0, and every array must have
  *     fewer than 2^62 bytes. Anything else returns NVFP4_ERROR_INVALID_VALUE.
  *   - Alignment: X, Wq, Wscale and W must be 16-byte aligned, Y and gscale 4-byte aligned;
@@ -137,9 +137,22 @@ typedef enum {
                              loader wavefronts stage X and the weights in LDS, four consumer
                              wavefronts decode and multiply; any M, meant for M > 16. It may cut
                              K across workgroups (see below) */
-    NVFP4_PATH_BATCH_SPLITK = 4 /* NVFP4_PATH_BATCH with K cut into `split` slices across
+    NVFP4_PATH_BATCH_SPLITK = 4, /* NVFP4_PATH_BATCH with K cut into `split` slices across
                              workgroups: partial sums go to a workspace, a second kernel adds
                              them in slice order and applies g */
+    NVFP4_PATH_INVARIANT = 5 /* batch-invariant mode: row m of Y is the same bits for every M
+                             and whatever the other rows of X hold, so a request verified
+                             alone or with others gets exactly what M = 1 decode gives it
+                             ("SparkInfer" README, speculative decoding sections: a request
+                             speculating alone is bit-identical to speculation off). The
+                             batch kernel with one plan per (N, K) for all M, the plan
+                             nvfp4_gemm takes for 128 rows, K slices included; slower than
+                             NVFP4_PATH_AUTO at small M. A split plan needs the workspace
+                             (above) sized for 128 rows: a call under stream capture that
+                             would have to grow it returns NVFP4_ERROR_LAUNCH and launches
+                             nothing (there is no unsplit fallback, which would change the
+                             bits), so run one call per shape before capturing. split must be
+                             0. */
 } nvfp4_path_t;
 
 /*
@@ -153,6 +166,7 @@ typedef enum {
  *   NVFP4_PATH_BATCH: 1, 2 or 4, the number of consumer wavefronts that share the K steps of one
  *     column tile (4 / split tiles are processed side by side).
  *   NVFP4_PATH_BATCH_SPLITK: 2, 4 or 8 K slices (at most one per 128 k).
+ *   NVFP4_PATH_INVARIANT: 0 only.
  * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
 nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const uint16_t *X,

@@ -24,6 +24,7 @@ PATH_DOT = 1
 PATH_MFMA = 2
 PATH_BATCH = 3
 PATH_BATCH_SPLITK = 4
+PATH_INVARIANT = 5   # row m of Y is the same bits for every M
 
 _lib = None
 

@@ -59,7 +59,7 @@ nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const u
         return NVFP4_ERROR_INVALID_VALUE;
     if (!X || !Wq || !Wscale || !gscale || !Y)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_BATCH_SPLITK)
+    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_INVARIANT)
         return NVFP4_ERROR_INVALID_VALUE;
     if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 16)
         return NVFP4_ERROR_INVALID_VALUE;

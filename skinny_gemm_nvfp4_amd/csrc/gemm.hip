@@ -390,6 +390,26 @@ float *batch_workspace(size_t bytes, hipStream_t stream)
     return static_cast<float *>(p);
 }
 
+// Batch-invariant mode: one plan per (N, K), the plan of a full 128-row slab (K slices included),
+// used for every slab whatever its rows. Only the row-block count MB follows the rows, and a row's
+// arithmetic does not depend on it: each row block has its own accumulators, the weight fragment
+// it multiplies is the same, and the steps, the step split, the remainder partials and the K
+// slices are added in the same order. So row m of Y is the same bits for any M. The workspace of
+// a split plan is sized for a full slab on every call, so one call outside stream capture covers
+// every later M.
+bool invariant_plan(int N, int K, BatchPlan *P)
+{
+    return batch_plan(16 * kBatchMaxBlocks, N, K, 0, 0, P);
+}
+
+// The invariant plan adapted to a slab of `rows` rows: the row-block count and LDS bytes only.
+void plan_for_rows(BatchPlan *P, int rows)
+{
+    P->mbi = rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 64 ? 2 : 3;
+    P->mb = 1 << P->mbi;
+    P->lds = P->nr > 0 ? kBatchNrLds[P->nri][P->mbi] : kBatchLds[P->tcw - 1][P->mbi][P->ksi];
+}
+
 // Tiles of 16 columns per workgroup when every compute unit takes an equal share of the groups.
 int tiles_per_workgroup(int N)
 {
@@ -418,6 +438,10 @@ bool choose_config(int M, int N, int K, int *path, int *split)
             return false;
         *split = 1 << P.ksi;
         return true;
+    }
+    if (*path == kPathInvariant) {
+        BatchPlan P;
+        return *split == 0 && invariant_plan(N, K, &P);
     }
     if (*path == kPathBatchSplit) {
         if (*split != 2 && *split != 4 && *split != 8)
@@ -466,15 +490,20 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
         hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * split), lds, stream, a, L);
         return hipGetLastError();
     }
-    if (path == kPathBatch || path == kPathBatchSplit) {
+    if (path == kPathBatch || path == kPathBatchSplit || path == kPathInvariant) {
         const int ks_req = path == kPathBatch ? split : 0;
         const int s_req = path == kPathBatch ? 0 : split;
+        BatchPlan fixed = {};
+        if (path == kPathInvariant && !invariant_plan(a.N, a.K, &fixed))
+            return hipErrorInvalidValue;
         // Slabs of 128 rows, one launch each (the last one may be smaller).
         constexpr int kSlab = 16 * kBatchMaxBlocks;
         for (int m0 = 0; m0 < a.M; m0 += kSlab) {
             const int rows = std::min(kSlab, a.M - m0);
-            BatchPlan P;
-            if (!batch_plan(rows, a.N, a.K, ks_req, s_req, &P))
+            BatchPlan P = fixed;
+            if (path == kPathInvariant)
+                plan_for_rows(&P, rows);
+            else if (!batch_plan(rows, a.N, a.K, ks_req, s_req, &P))
                 return hipErrorInvalidValue;
             GemmArgs b = a;
             b.X = a.X + (size_t)m0 * (size_t)a.K;
@@ -482,7 +511,13 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
             b.M = rows;
             float *ws = nullptr;
             const size_t stride = batch_slice_stride(rows, a.N);
-            if (P.nslice > 1) {
+            if (P.nslice > 1 && path == kPathInvariant) {
+                // The slices are part of the invariant arithmetic: no unsplit fallback.
+                ws = batch_workspace(
+                    (size_t)P.nslice * batch_slice_stride(kSlab, a.N) * sizeof(float), stream);
+                if (ws == nullptr)
+                    return hipErrorStreamCaptureUnsupported;
+            } else if (P.nslice > 1) {
                 ws = batch_workspace((size_t)P.nslice * stride * sizeof(float), stream);
                 if (ws == nullptr && !batch_plan(rows, a.N, a.K, ks_req, 1, &P))
                     return hipErrorInvalidValue;   // no workspace: run unsplit

@@ -60,7 +60,14 @@ inline uint64_t scales_bytes(int N, int K)
     return (uint64_t)num_groups(N) * (uint64_t)num_chunks(K) * kChunkScaleBytes;
 }
 
-enum Path { kPathAuto = 0, kPathDot = 1, kPathMfma = 2, kPathBatch = 3, kPathBatchSplit = 4 };
+enum Path {
+    kPathAuto = 0,
+    kPathDot = 1,
+    kPathMfma = 2,
+    kPathBatch = 3,
+    kPathBatchSplit = 4,
+    kPathInvariant = 5
+};
 
 // Largest M the dot-product kernel is instantiated for.
 constexpr int kDotMaxM = 8;

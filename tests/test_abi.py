@@ -83,7 +83,7 @@ def test_gemm_rejects_misaligned_pointers(lib):
 
 def test_gemm_path_rejects_bad_options(lib):
     ptrs = [A16, A16B, A16C, A16D, A16E]
-    assert nv.nvfp4_gemm_path(5, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_gemm_path(6, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
     assert nv.nvfp4_gemm_path(-1, 0, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
     for split in (1, 2, 3, 32, -1):
         assert nv.nvfp4_gemm_path(0, split, 1, 16, 256, *ptrs, None) == nv.ERROR_INVALID_VALUE
@@ -99,6 +99,10 @@ def test_gemm_path_rejects_bad_options(lib):
     # the split-K batch path takes 2, 4 or 8 slices, at most one per 128 k (K = 256: 2 windows)
     for split in (0, 1, 4, 16):
         assert nv.nvfp4_gemm_path(nv.PATH_BATCH_SPLITK, split, 128, 16, 256, *ptrs, None) == \
+            nv.ERROR_INVALID_VALUE
+    # the batch-invariant mode has no split to choose
+    for split in (1, 2, 4, 8):
+        assert nv.nvfp4_gemm_path(nv.PATH_INVARIANT, split, 16, 16, 256, *ptrs, None) == \
             nv.ERROR_INVALID_VALUE
     # the wave counts of the other kernels are 4, 8 or 16
     for split in (1, 2):
