@@ -173,6 +173,53 @@ nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const u
                                const uint8_t *Wq, const uint8_t *Wscale, const float *gscale,
                                float *Y, void *stream);
 
+/*
+ * nvfp4_gemm_argmax -- greedy token per row of the GEMM, without writing Y.
+ *
+ * Greedy decode and greedy speculative verification take, for every row of X, the column of the
+ * largest output of the lm_head GEMM ("SparkInfer" README: decode, DSpark and DFlash2 figures are
+ * greedy, and a request speculating alone gets exactly the tokens it gets without the drafter).
+ * The lm_head is a full-vocabulary GEMM on every token ("Qwen3.8-27B-NVFP4-RTX5090" model card,
+ * section on why lm_head is NVFP4), so its M x N fp32 logits are the largest output of a pass;
+ * here they stay in registers: each kernel folds its outputs into per-row (value, column) keys,
+ * and a second small kernel picks the winner per row.
+ *
+ * Result, for the Y that nvfp4_gemm (or nvfp4_gemm_path with the same path and split) computes
+ * from the same inputs, bit for bit:
+ *   index[m] = the smallest n with Y[m][n] == max over n of Y[m][n]
+ *   value[m] = that maximum (fp32)
+ * Ranking: -0 equals +0 (a -0 maximum is returned as +0); NaN ranks above every number (NaN
+ * inputs are outside the contract of the GEMM itself). Like nvfp4_gemm the result is
+ * deterministic; with NVFP4_PATH_INVARIANT it is also the same for row m whatever M is.
+ *
+ *   M, N, K, X, Wq, Wscale, gscale   as for nvfp4_gemm
+ *   index      out: int32 [M], device, 4-byte aligned
+ *   value      out: fp32 [M], device, 4-byte aligned
+ *   workspace  scratch owned by the caller: at least nvfp4_argmax_workspace_bytes(M) bytes of
+ *              device memory, 8-byte aligned; its contents on entry do not matter and are left
+ *              undefined. Calls that overlap in time must not share a workspace.
+ *   workspace_bytes  its size; smaller than required returns NVFP4_ERROR_INVALID_VALUE
+ *   stream     hipStream_t
+ * Errors as for nvfp4_gemm. The split-K workspace rules of the batch kernel (above) apply too.
+ */
+nvfp4_status_t nvfp4_gemm_argmax(int M, int N, int K, const uint16_t *X, const uint8_t *Wq,
+                                 const uint8_t *Wscale, const float *gscale, int32_t *index,
+                                 float *value, void *workspace, uint64_t workspace_bytes,
+                                 void *stream);
+
+/* nvfp4_gemm_argmax with the kernel family and its split forced (path and split exactly as for
+ * nvfp4_gemm_path; the result matches nvfp4_gemm_path with the same two values). */
+nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
+                                      const uint16_t *X, const uint8_t *Wq,
+                                      const uint8_t *Wscale, const float *gscale, int32_t *index,
+                                      float *value, void *workspace, uint64_t workspace_bytes,
+                                      void *stream);
+
+/* Workspace bytes nvfp4_gemm_argmax needs for M rows on the current device:
+ * 8 * 16 * (compute units) per row (one 8-byte key per wavefront of the widest kernel);
+ * 0 if M < 1. */
+uint64_t nvfp4_argmax_workspace_bytes(int M);
+
 /* Bytes of Wq for an N x K weight: 64 * ceil(N/4) * ceil(K/32); 0 if N < 1 or K < 1. */
 uint64_t nvfp4_codes_bytes(int N, int K);
 
@@ -183,7 +230,7 @@ uint64_t nvfp4_scales_bytes(int N, int K);
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

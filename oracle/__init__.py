@@ -10,6 +10,7 @@ What it computes, from the pages and the workload recipe:
   size 16; section "Why lm_head is NVFP4": decode streams every weight once per token.
   Per tensor g = amax / (6*448); per 16-block along K an E4M3 scale s = round(block_amax / (6g));
   codes = round-to-nearest E2M1 of w / (s*g); Y = X . (e2m1(code) * s * g).
+  Greedy token per row = first column of the row maximum ("SparkInfer" README, greedy decode).
 Pins for every function live in tests/test_oracle_*.py; none is "parity unpinned".
 """
 import ctypes
@@ -151,6 +152,23 @@ def gemm(X_bits: np.ndarray, Wq: np.ndarray, Ws: np.ndarray, g, cols=None):
     if rc:
         raise MemoryError("oracle_gemm could not allocate its buffers")
     return Y, A
+
+
+def argmax_rows(Y: np.ndarray) -> np.ndarray:
+    """Greedy token of every row: the first column n holding max over n of Y[m, n] (int64 [M]).
+
+    Greedy decode and greedy speculative verification pick this column of the lm_head's logits
+    for each row ("SparkInfer" README: decode and the DSpark/DFlash2 figures are measured greedy,
+    and a request speculating alone gets the tokens it gets without the drafter). Y is the
+    oracle's own float64 result. Equal values (including -0 and +0) go to the smaller column;
+    numpy's argmax is that definition (first occurrence of the maximum).
+    """
+    Y = np.asarray(Y, dtype=np.float64)
+    if Y.ndim != 2 or Y.shape[1] == 0:
+        raise ValueError("Y must be [M][N] with N >= 1")
+    if np.isnan(Y).any():
+        raise ValueError("NaN logits are outside the oracle's contract")
+    return np.argmax(Y, axis=1)
 
 
 def num_threads() -> int:

@@ -58,6 +58,13 @@ def load_library() -> ctypes.CDLL:
     L.nvfp4_gemm.restype = ci
     L.nvfp4_gemm_path.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp]
     L.nvfp4_gemm_path.restype = ci
+    L.nvfp4_gemm_argmax.argtypes = [ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+    L.nvfp4_gemm_argmax.restype = ci
+    L.nvfp4_gemm_argmax_path.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_uint64, vp]
+    L.nvfp4_gemm_argmax_path.restype = ci
+    L.nvfp4_argmax_workspace_bytes.argtypes = [ci]
+    L.nvfp4_argmax_workspace_bytes.restype = ctypes.c_uint64
     L.nvfp4_status_string.argtypes = [ci]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_abi_version.argtypes = []
@@ -93,6 +100,24 @@ def nvfp4_gemm(M: int, N: int, K: int, X: int, Wq: int, Wscale: int, gscale: int
 def nvfp4_gemm_path(path: int, split: int, M: int, N: int, K: int, X: int, Wq: int, Wscale: int,
                     gscale: int, Y: int, stream: Optional[int]) -> int:
     return load_library().nvfp4_gemm_path(path, split, M, N, K, X, Wq, Wscale, gscale, Y, stream)
+
+
+def nvfp4_gemm_argmax(M: int, N: int, K: int, X: int, Wq: int, Wscale: int, gscale: int,
+                      index: int, value: int, workspace: int, workspace_bytes: int,
+                      stream: Optional[int]) -> int:
+    return load_library().nvfp4_gemm_argmax(M, N, K, X, Wq, Wscale, gscale, index, value,
+                                            workspace, workspace_bytes, stream)
+
+
+def nvfp4_gemm_argmax_path(path: int, split: int, M: int, N: int, K: int, X: int, Wq: int,
+                           Wscale: int, gscale: int, index: int, value: int, workspace: int,
+                           workspace_bytes: int, stream: Optional[int]) -> int:
+    return load_library().nvfp4_gemm_argmax_path(path, split, M, N, K, X, Wq, Wscale, gscale,
+                                                 index, value, workspace, workspace_bytes, stream)
+
+
+def nvfp4_argmax_workspace_bytes(M: int) -> int:
+    return load_library().nvfp4_argmax_workspace_bytes(M)
 
 
 def nvfp4_codes_bytes(N: int, K: int) -> int:
@@ -186,3 +211,47 @@ def gemm(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Tensor, N
     if st != SUCCESS:
         raise NVFP4Error(st, "nvfp4_gemm")
     return out
+
+
+def argmax_workspace(M: int, device) -> torch.Tensor:
+    """A workspace for gemm_argmax with M rows on `device` (uint8, nvfp4_argmax_workspace_bytes)."""
+    with torch.cuda.device(device):
+        nbytes = nvfp4_argmax_workspace_bytes(M)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gemm_argmax(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Tensor, N: int,
+                stream=None, out=None, workspace: Optional[torch.Tensor] = None,
+                path: int = PATH_AUTO, split: int = 0):
+    """Greedy token per row of X . dequant(Wq, Ws, g) without writing the logits: returns
+    (index int32 [M], value fp32 [M]), the first column of each row's maximum and that maximum,
+    for the Y that gemm() with the same path and split computes."""
+    M, K = X.shape
+    _check_device(X, "X", torch.bfloat16, (M, K))
+    _check_device(Wq, "Wq", torch.uint8, codes_shape(N, K))
+    _check_device(Ws, "Ws", torch.uint8, scales_shape(N, K))
+    _check_device(g, "g", torch.float32, (1,))
+    if out is None:
+        index = torch.empty(M, dtype=torch.int32, device=X.device)
+        value = torch.empty(M, dtype=torch.float32, device=X.device)
+    else:
+        index, value = out
+        _check_device(index, "index", torch.int32, (M,))
+        _check_device(value, "value", torch.float32, (M,))
+    if workspace is None:
+        workspace = argmax_workspace(M, X.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if path == PATH_AUTO and split == 0:
+        st = nvfp4_gemm_argmax(M, N, K, X.data_ptr(), Wq.data_ptr(), Ws.data_ptr(), g.data_ptr(),
+                               index.data_ptr(), value.data_ptr(), workspace.data_ptr(),
+                               ws_bytes, _stream(stream))
+    else:
+        st = nvfp4_gemm_argmax_path(path, split, M, N, K, X.data_ptr(), Wq.data_ptr(),
+                                    Ws.data_ptr(), g.data_ptr(), index.data_ptr(),
+                                    value.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                    _stream(stream))
+    if st != SUCCESS:
+        raise NVFP4Error(st, "nvfp4_gemm_argmax")
+    return index, value

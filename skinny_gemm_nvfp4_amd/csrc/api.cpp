@@ -87,6 +87,60 @@ nvfp4_status_t nvfp4_gemm(int M, int N, int K, const uint16_t *X, const uint8_t 
     return nvfp4_gemm_path(NVFP4_PATH_AUTO, 0, M, N, K, X, Wq, Wscale, gscale, Y, stream);
 }
 
+uint64_t nvfp4_argmax_workspace_bytes(int M)
+{
+    if (M < 1)
+        return 0;
+    return (uint64_t)M * (uint64_t)nvfp4::kArgmaxSlotsPerCu *
+           (uint64_t)nvfp4::device_compute_units() * 8u;
+}
+
+nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
+                                      const uint16_t *X, const uint8_t *Wq,
+                                      const uint8_t *Wscale, const float *gscale, int32_t *index,
+                                      float *value, void *workspace, uint64_t workspace_bytes,
+                                      void *stream)
+{
+    if (!sizes_ok(M, N, K))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!X || !Wq || !Wscale || !gscale || !index || !value || !workspace)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_INVARIANT)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 16)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
+        !aligned(index, 4) || !aligned(value, 4) || !aligned(workspace, 8))
+        return NVFP4_ERROR_MISALIGNED;
+    if (workspace_bytes < nvfp4_argmax_workspace_bytes(M))
+        return NVFP4_ERROR_INVALID_VALUE;
+    int p = path, s = split;
+    if (!nvfp4::choose_config(M, N, K, &p, &s))
+        return NVFP4_ERROR_INVALID_VALUE;
+    nvfp4::GemmArgs a;
+    a.X = X;
+    a.Wq = Wq;
+    a.Ws = Wscale;
+    a.gscale = gscale;
+    a.Y = nullptr;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.keys = static_cast<unsigned long long *>(workspace);
+    a.key_slots = 0;
+    return from_hip(nvfp4::launch_gemm_argmax(p, s, a, index, value,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status_t nvfp4_gemm_argmax(int M, int N, int K, const uint16_t *X, const uint8_t *Wq,
+                                 const uint8_t *Wscale, const float *gscale, int32_t *index,
+                                 float *value, void *workspace, uint64_t workspace_bytes,
+                                 void *stream)
+{
+    return nvfp4_gemm_argmax_path(NVFP4_PATH_AUTO, 0, M, N, K, X, Wq, Wscale, gscale, index, value,
+                                  workspace, workspace_bytes, stream);
+}
+
 const char *nvfp4_status_string(nvfp4_status_t status)
 {
     switch (status) {

@@ -67,17 +67,20 @@ const int kMfmaTiles[6] = {1, 2, 3, 4, 6, 9};
 const KernelFn kMfma[2][6][2] = {NVFP4_MFMA_TABLE(false), NVFP4_MFMA_TABLE(true)};
 
 // ---- batch kernels: [TCW - 1][MB index: 1, 2, 4, 8 row blocks][KS index: 1, 2, 4] ----
-#define NVFP4_BATCH_KS(TCW, MB)                                                            \
+// (second index of kBatchAll: 0 stores Y, 1 folds it into argmax keys)
+#define NVFP4_BATCH_KS(TCW, MB, A)                                                         \
     {                                                                                      \
-        &mfma_batch_kernel<TCW, MB, 1>, &mfma_batch_kernel<TCW, MB, 2>,                    \
-            &mfma_batch_kernel<TCW, MB, 4>                                                 \
+        &mfma_batch_kernel<TCW, MB, 1, 0, A>, &mfma_batch_kernel<TCW, MB, 2, 0, A>,        \
+            &mfma_batch_kernel<TCW, MB, 4, 0, A>                                           \
     }
-#define NVFP4_BATCH_MB(TCW)                                                                \
+#define NVFP4_BATCH_MB(TCW, A)                                                             \
     {                                                                                      \
-        NVFP4_BATCH_KS(TCW, 1), NVFP4_BATCH_KS(TCW, 2), NVFP4_BATCH_KS(TCW, 4),           \
-            NVFP4_BATCH_KS(TCW, 8)                                                         \
+        NVFP4_BATCH_KS(TCW, 1, A), NVFP4_BATCH_KS(TCW, 2, A), NVFP4_BATCH_KS(TCW, 4, A),   \
+            NVFP4_BATCH_KS(TCW, 8, A)                                                      \
     }
-const KernelFn kBatch[3][4][3] = {NVFP4_BATCH_MB(1), NVFP4_BATCH_MB(2), NVFP4_BATCH_MB(3)};
+const KernelFn kBatchAll[2][3][4][3] = {
+    {NVFP4_BATCH_MB(1, false), NVFP4_BATCH_MB(2, false), NVFP4_BATCH_MB(3, false)},
+    {NVFP4_BATCH_MB(1, true), NVFP4_BATCH_MB(2, true), NVFP4_BATCH_MB(3, true)}};
 
 template <int TCW, int MB, int KS>
 constexpr int batch_lds()
@@ -100,13 +103,16 @@ constexpr int kBatchLds[3][4][3] = {NVFP4_BATCH_LDS_MB(1), NVFP4_BATCH_LDS_MB(2)
 constexpr int kBatchNrCombos = 3;
 constexpr int kBatchNrTcw[kBatchNrCombos] = {1, 1, 2};
 constexpr int kBatchNrNr[kBatchNrCombos] = {1, 2, 1};
-#define NVFP4_BATCH_NR_MB(TCW, NR)                                                         \
+#define NVFP4_BATCH_NR_MB(TCW, NR, A)                                                      \
     {                                                                                      \
-        &mfma_batch_kernel<TCW, 1, 1, NR>, &mfma_batch_kernel<TCW, 2, 1, NR>,              \
-            &mfma_batch_kernel<TCW, 4, 1, NR>, &mfma_batch_kernel<TCW, 8, 1, NR>           \
+        &mfma_batch_kernel<TCW, 1, 1, NR, A>, &mfma_batch_kernel<TCW, 2, 1, NR, A>,        \
+            &mfma_batch_kernel<TCW, 4, 1, NR, A>, &mfma_batch_kernel<TCW, 8, 1, NR, A>     \
     }
-const KernelFn kBatchNr[kBatchNrCombos][4] = {NVFP4_BATCH_NR_MB(1, 1), NVFP4_BATCH_NR_MB(1, 2),
-                                              NVFP4_BATCH_NR_MB(2, 1)};
+const KernelFn kBatchNrAll[2][kBatchNrCombos][4] = {
+    {NVFP4_BATCH_NR_MB(1, 1, false), NVFP4_BATCH_NR_MB(1, 2, false),
+     NVFP4_BATCH_NR_MB(2, 1, false)},
+    {NVFP4_BATCH_NR_MB(1, 1, true), NVFP4_BATCH_NR_MB(1, 2, true),
+     NVFP4_BATCH_NR_MB(2, 1, true)}};
 #define NVFP4_BATCH_NR_LDS(TCW, NR)                                                        \
     {                                                                                      \
         BatchShape<TCW, 1, 1, NR>::LDS, BatchShape<TCW, 2, 1, NR>::LDS,                    \
@@ -473,8 +479,26 @@ bool choose_config(int M, int N, int K, int *path, int *split)
     return mfma_plan(N, K, *split, &P);
 }
 
-hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t stream)
+namespace {
+
+// Turns the keys of `rows` rows (row stride `slots`) into index and value.
+hipError_t launch_finalize(const argkey_t *keys, int slots, int rows, int32_t *index,
+                           float *value, hipStream_t stream)
 {
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3((unsigned)rows), dim3(256), 0, stream, keys,
+                       slots, index, value);
+    return hipGetLastError();
+}
+
+// launch_gemm, and in argmax mode (index != nullptr, a.keys the workspace of M *
+// kArgmaxSlotsPerCu * compute units keys) the same kernels folding Y into keys, then the
+// finalize kernel.
+hipError_t launch_impl(int path, int split, const GemmArgs &a0, int32_t *index, float *value,
+                       hipStream_t stream)
+{
+    const bool argmax = index != nullptr;
+    const int cap = kArgmaxSlotsPerCu * compute_units();   // key row stride of the workspace
+    GemmArgs a = a0;
     (void)hipGetLastError();  // start from a clean error state
     if (path == kPathDot) {
         StreamLayout L;
@@ -487,8 +511,15 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
         const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), lds);
         if (e != hipSuccess)
             return e;
+        if (argmax)
+            a.key_slots = grid * split;   // one key per wavefront
+        if (a.key_slots > cap)
+            return hipErrorInvalidValue;
         hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * split), lds, stream, a, L);
-        return hipGetLastError();
+        const hipError_t le = hipGetLastError();
+        if (le != hipSuccess || !argmax)
+            return le;
+        return launch_finalize(a.keys, a.key_slots, a.M, index, value, stream);
     }
     if (path == kPathBatch || path == kPathBatchSplit || path == kPathInvariant) {
         const int ks_req = path == kPathBatch ? split : 0;
@@ -507,7 +538,7 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
                 return hipErrorInvalidValue;
             GemmArgs b = a;
             b.X = a.X + (size_t)m0 * (size_t)a.K;
-            b.Y = a.Y + (size_t)m0 * (size_t)a.N;
+            b.Y = a.Y != nullptr ? a.Y + (size_t)m0 * (size_t)a.N : nullptr;
             b.M = rows;
             float *ws = nullptr;
             const size_t stride = batch_slice_stride(rows, a.N);
@@ -522,24 +553,50 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
                 if (ws == nullptr && !batch_plan(rows, a.N, a.K, ks_req, 1, &P))
                     return hipErrorInvalidValue;   // no workspace: run unsplit
             }
-            const KernelFn fn = P.nr > 0 ? kBatchNr[P.nri][P.mbi] : kBatch[P.tcw - 1][P.mbi][P.ksi];
+            // Argmax mode: the kernel folds Y into keys itself unless K is split, in which case
+            // the partials go to the workspace as usual and the reduce kernel folds the sums.
+            const int fold = (argmax && P.nslice == 1) ? 1 : 0;
+            const KernelFn fn = P.nr > 0 ? kBatchNrAll[fold][P.nri][P.mbi]
+                                         : kBatchAll[fold][P.tcw - 1][P.mbi][P.ksi];
             const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), P.lds);
             if (e != hipSuccess)
                 return e;
             GemmArgs kb = b;
+            kb.keys = nullptr;
             if (P.nslice > 1)
                 kb.Y = ws;   // unscaled partial sums, slice by slice
+            argkey_t *slab_keys = argmax ? a.keys + (size_t)m0 * (size_t)cap : nullptr;
+            if (fold) {
+                kb.keys = slab_keys;
+                kb.key_slots = kBatchConsumers * P.grid;   // one key per consumer wavefront
+                if (kb.key_slots > cap)
+                    return hipErrorInvalidValue;
+            }
             hipLaunchKernelGGL(fn, dim3((unsigned)P.grid, (unsigned)P.nslice),
                                dim3(kWave * kBatchWaves), P.lds, stream, kb);
             hipError_t le = hipGetLastError();
             if (le != hipSuccess)
                 return le;
-            if (P.nslice > 1) {
+            int slots = kb.key_slots;
+            if (P.nslice > 1 && argmax) {
+                slots = std::min(cap, std::max(1, std::min((a.N + 255) / 256, 256)));
+                hipLaunchKernelGGL(batch_reduce_argmax_kernel, dim3((unsigned)slots, (unsigned)rows),
+                                   dim3(256), 0, stream, ws, P.nslice, a.N, (long long)stride,
+                                   a.gscale, slab_keys, slots);
+                le = hipGetLastError();
+                if (le != hipSuccess)
+                    return le;
+            } else if (P.nslice > 1) {
                 const long long count = (long long)rows * a.N;
                 const unsigned blocks = (unsigned)((count + 4 * 256 - 1) / (4 * 256));
                 hipLaunchKernelGGL(batch_reduce_kernel, dim3(blocks), dim3(256), 0, stream, ws,
                                    P.nslice, count, (long long)stride, a.gscale, b.Y);
                 le = hipGetLastError();
+                if (le != hipSuccess)
+                    return le;
+            }
+            if (argmax) {
+                le = launch_finalize(slab_keys, slots, rows, index + m0, value + m0, stream);
                 if (le != hipSuccess)
                     return le;
             }
@@ -557,9 +614,36 @@ hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t strea
     if (e != hipSuccess)
         return e;
     const unsigned mblocks = (unsigned)((a.M + 15) / 16);
+    if (argmax)
+        a.key_slots = P.grid * (split / 4);   // one key per four wavefronts
+    if (a.key_slots > cap)
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3((unsigned)P.grid, mblocks), dim3(kWave * split), P.lds, stream,
                        a);
-    return hipGetLastError();
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess || !argmax)
+        return le;
+    return launch_finalize(a.keys, a.key_slots, a.M, index, value, stream);
 }
+
+}  // namespace
+
+hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t stream)
+{
+    GemmArgs b = a;
+    b.keys = nullptr;
+    b.key_slots = 0;
+    return launch_impl(path, split, b, nullptr, nullptr, stream);
+}
+
+hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *index,
+                              float *value, hipStream_t stream)
+{
+    if (a.keys == nullptr || index == nullptr || value == nullptr)
+        return hipErrorInvalidValue;
+    return launch_impl(path, split, a, index, value, stream);
+}
+
+int device_compute_units() { return compute_units(); }
 
 }  // namespace nvfp4

@@ -30,6 +30,7 @@
 //     64-bit and no generic integer division.
 #pragma once
 
+#include "argmax.h"
 #include "device.h"
 #include "launch.h"
 
@@ -252,12 +253,22 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     for (int m = 0; m < MR; m++) {
         if (m >= a.M)
             break;
+        argkey_t best = 0;
         for (int c = threadIdx.x; c < ncols; c += kWave * W) {
             const int grp = c >> 2;
             float sum = 0.0f;
             for (int sl = 0; sl < L.slots; sl++)
                 sum += part[((grp * L.slots + sl) * MR + m) * 4 + (c & 3)];
-            a.Y[(size_t)m * N + c0 + c] = sum * g;
+            if (a.keys == nullptr)
+                a.Y[(size_t)m * N + c0 + c] = sum * g;
+            else
+                best = key_max(best, argmax_key(sum * g, c0 + c));
+        }
+        if (a.keys != nullptr) {
+            // Argmax mode: one key per row and wavefront, slot b W + wave of the row.
+            best = key_max_64(best);
+            if (lane == 0)
+                a.keys[(size_t)m * a.key_slots + b * W + wave] = best;
         }
     }
 }

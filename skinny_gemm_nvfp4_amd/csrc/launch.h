@@ -12,8 +12,12 @@ struct GemmArgs {
     const uint8_t *Wq;       // [NG][CH][4][16]
     const uint8_t *Ws;       // [NG][CH][4][2]
     const float *gscale;     // [1]
-    float *Y;                // [M][N]
+    float *Y;                // [M][N]; unused when keys is set
     int M, N, K;
+    // Argmax mode (nvfp4_gemm_argmax): instead of storing Y, each writer folds the outputs it
+    // owns into one argmax key per row (argmax.h) and stores it at keys[m * key_slots + slot].
+    unsigned long long *keys = nullptr;
+    int key_slots = 0;
 };
 
 // Packed layout: 4-column groups, 32-k chunks. One chunk of one group is 4 x 16 code bytes
@@ -81,6 +85,20 @@ bool choose_config(int M, int N, int K, int *path, int *split);
 
 // Launch the GEMM with a resolved path and split. Returns the hipError_t of the launch.
 hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t stream);
+
+// Largest number of argmax key slots per row for a device with `cus` compute units: the
+// dot-product kernel writes one per wavefront (at most 16 per workgroup, one workgroup per
+// compute unit); the other writers fewer.
+constexpr int kArgmaxSlotsPerCu = 16;
+
+// Argmax variant of launch_gemm: the same kernels and plan, outputs folded into per-row keys in
+// `keys` ([M][key_slots], key_slots <= kArgmaxSlotsPerCu * compute units), then one key per row
+// turned into index and value.
+hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *index,
+                              float *value, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_compute_units();
 
 // Launch the pack sequence (clear, amax, tensor scale, quantise) on the stream.
 hipError_t launch_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Ws, float *gscale,

@@ -38,6 +38,7 @@
 //     reproducible.
 #pragma once
 
+#include "argmax.h"
 #include "device.h"
 #include "launch.h"
 
@@ -278,7 +279,9 @@ struct BatchXWin {
     u32x4_t x[NXP];
 };
 
-template <int TCW, int MB, int KS, int NR = 0>
+// ARGMAX: instead of storing Y, fold it into one argmax key per row and consumer (argmax.h),
+// slot 4 blockIdx.x + consumer of a.keys; only for unsplit K (gridDim.y == 1).
+template <int TCW, int MB, int KS, int NR = 0, bool ARGMAX = false>
 __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs a)
 {
     using S = BatchShape<TCW, MB, KS, NR>;
@@ -410,6 +413,13 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
         const rsrc_t ry = make_rsrc(a.Y + (size_t)blockIdx.y * batch_slice_stride(M, N),
                                     (uint32_t)M * (uint32_t)N * 4u);
         const float g = nslice > 1 ? 1.0f : *a.gscale;
+        // Argmax mode: best[b][e] is the key of row 16 b + 4 q + e over the lane's columns.
+        argkey_t best[ARGMAX ? MB : 1][4];
+#pragma unroll
+        for (int b = 0; b < (ARGMAX ? MB : 1); b++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                best[b][e] = 0;
         for (int tc0 = 0; tc0 < T; tc0 += S::PT) {
             const int nt = max(0, min(TCW, (T - tc0 - ts + S::TS - 1) / S::TS));
             f32x4_t acc[MB][S::NACC];
@@ -469,8 +479,14 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
                                 for (int k2 = 1; k2 < KS; k2++)
                                     v += red_at(k2, j, b, e);
                                 const uint32_t ro = (uint32_t)(16 * b + e) * (uint32_t)N * 4u;
-                                __builtin_amdgcn_raw_buffer_store_b32(
-                                    __float_as_uint(v * g), ry, off_if(cv, vo + ro), 0, 0);
+                                if constexpr (ARGMAX) {
+                                    if (cv)
+                                        best[b][e] = key_max(best[b][e],
+                                                             argmax_key(v * g, c0 + colx));
+                                } else {
+                                    __builtin_amdgcn_raw_buffer_store_b32(
+                                        __float_as_uint(v * g), ry, off_if(cv, vo + ro), 0, 0);
+                                }
                             }
                     }
                 }
@@ -504,12 +520,31 @@ __global__ __launch_bounds__(kWave *kBatchWaves) void mfma_batch_kernel(GemmArgs
                             for (int c = 0; c < kBatchConsumers; c++)
                                 v += rred[(((c * NR + ts) * MB + b) * 4 + e) * kWave + lane];
                             const uint32_t ro = (uint32_t)(16 * b + e) * (uint32_t)N * 4u;
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * g), ry,
-                                                                  off_if(cv, vo + ro), 0, 0);
+                            if constexpr (ARGMAX) {
+                                if (cv)
+                                    best[b][e] =
+                                        key_max(best[b][e], argmax_key(v * g, c0 + colx));
+                            } else {
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    __float_as_uint(v * g), ry, off_if(cv, vo + ro), 0, 0);
+                            }
                         }
                 }
                 batch_barrier();   // partial sums read before the next pass refills the buffers
             }
+        }
+        if constexpr (ARGMAX) {
+            // Every consumer writes all its rows' keys (0 where it stored nothing).
+#pragma unroll
+            for (int b = 0; b < (ARGMAX ? MB : 1); b++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const argkey_t k = key_max_16(best[b][e]);
+                    const int row = 16 * b + 4 * q + e;
+                    if (r == 0 && row < M)
+                        a.keys[(size_t)row * a.key_slots + kBatchConsumers * blockIdx.x + wave] =
+                            k;
+                }
         }
     }
 }
@@ -539,6 +574,34 @@ __global__ __launch_bounds__(256) void batch_reduce_kernel(const float *P, int S
             Y[e] = v * g;
         }
     }
+}
+
+// Split K in argmax mode: the outputs of batch_reduce_kernel (the same sums in the same order),
+// folded into keys instead of stored. Workgroup (x, m) takes columns x * 256 + t, stepping by
+// gridDim.x * 256, of row m and writes its key to keys[m * key_slots + x].
+__global__ __launch_bounds__(256) void batch_reduce_argmax_kernel(const float *P, int S, int N,
+                                                                  long long stride,
+                                                                  const float *gscale,
+                                                                  argkey_t *keys, int key_slots)
+{
+    __shared__ argkey_t best[4];
+    const int m = blockIdx.y;
+    const float g = *gscale;
+    argkey_t k = 0;
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < N; c += gridDim.x * 256) {
+        const long long e = (long long)m * N + c;
+        float v = P[e];
+        for (int s = 1; s < S; s++)
+            v += P[s * stride + e];
+        k = key_max(k, argmax_key(v * g, c));
+    }
+    k = key_max_64(k);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        best[threadIdx.x / kWave] = k;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        keys[(size_t)m * key_slots + blockIdx.x] =
+            key_max(key_max(best[0], best[1]), key_max(best[2], best[3]));
 }
 
 }  // namespace nvfp4

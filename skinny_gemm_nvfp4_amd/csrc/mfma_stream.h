@@ -27,6 +27,7 @@
 //   * FAST (K % 128 == 0) needs no per-lane K test; otherwise lanes past the last chunk read zeros.
 #pragma once
 
+#include "argmax.h"
 #include "device.h"
 #include "launch.h"
 
@@ -149,6 +150,9 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const float g = *a.gscale;
     // This wavefront's windows: wave, wave + W, ...; window i of the wavefront is wave + i W.
     const int nmine = (nwin - wave + W - 1) / W;
+    // Argmax mode: every output this thread adds up below is in row 4 q + wave % 4 of the block
+    // (W is a multiple of 4), so one key per thread.
+    argkey_t best = 0;
 
     for (int tc0 = 0; tc0 < T; tc0 += TC) {
         const int nt = min(TC, T - tc0);
@@ -203,10 +207,21 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
                 float sum = red[(t * 4 + e) * kWave + ln];
                 for (int v = 1; v < W; v++)
                     sum += red[((v * TC + t) * 4 + e) * kWave + ln];
-                a.Y[(size_t)(m0 + row) * N + c0 + colx] = sum * g;
+                if (a.keys == nullptr)
+                    a.Y[(size_t)(m0 + row) * N + c0 + colx] = sum * g;
+                else
+                    best = key_max(best, argmax_key(sum * g, c0 + colx));
             }
         }
         __syncthreads();  // red and the X buffers are reused by the next chunk
+    }
+    if (a.keys != nullptr) {
+        // One key per row and group of 4 wavefronts: slot blockIdx.x (W / 4) + wave / 4.
+        static_assert(W % 4 == 0, "rows per thread assume W % 4 == 0");
+        best = key_max_16(best);
+        const int row = 4 * q + wave % 4;
+        if (r == 0 && row < mrows)
+            a.keys[(size_t)(m0 + row) * a.key_slots + blockIdx.x * (W / 4) + wave / 4] = best;
     }
 }
 

@@ -41,7 +41,9 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"nvfp4_pack", "nvfp4_gemm", "nvfp4_gemm_path", "nvfp4_status_string",
-                          "nvfp4_abi_version", "nvfp4_codes_bytes", "nvfp4_scales_bytes"}
+                          "nvfp4_abi_version", "nvfp4_codes_bytes", "nvfp4_scales_bytes",
+                          "nvfp4_gemm_argmax", "nvfp4_gemm_argmax_path",
+                          "nvfp4_argmax_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
@@ -51,7 +53,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert nv.abi_version() == 2
+    assert nv.abi_version() == 3
     for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH):
         assert nv.status_string(st)
     assert nv.status_string(99) == "unknown status"
@@ -159,3 +161,48 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(ImportError):
         binding.load_library()
+
+
+# ---- nvfp4_gemm_argmax: the same validation, plus the outputs and the workspace ----
+
+A8F = 0x7F0000500000   # index
+A8G = 0x7F0000600000   # value
+A8H = 0x7F0000700000   # workspace
+BIG_WS = 1 << 40       # larger than any workspace the library asks for
+
+
+def _argmax(M, N, K, ptrs=None, ws_bytes=BIG_WS, path=None, split=0):
+    p = ptrs or [A16, A16B, A16C, A16D, A8F, A8G, A8H]
+    if path is None:
+        return nv.nvfp4_gemm_argmax(M, N, K, *p, ws_bytes, None)
+    return nv.nvfp4_gemm_argmax_path(path, split, M, N, K, *p, ws_bytes, None)
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 16, 256), (1, 0, 256), (1, 16, 8), (1, 16, 17),
+                                   (1, 16, 2 ** 22 + 16)])
+def test_argmax_rejects_bad_sizes(lib, M, N, K):
+    assert _argmax(M, N, K) == nv.ERROR_INVALID_VALUE
+
+
+def test_argmax_rejects_null_and_misaligned(lib):
+    good = [A16, A16B, A16C, A16D, A8F, A8G, A8H]
+    for i in range(len(good)):
+        bad = list(good)
+        bad[i] = 0
+        assert _argmax(1, 16, 256, bad) == nv.ERROR_INVALID_VALUE, i
+    # X, Wq, Wscale need 16 bytes; gscale, index, value 4; the workspace 8
+    for i, off in [(0, 8), (1, 8), (2, 4), (3, 2), (4, 2), (5, 2), (6, 4)]:
+        bad = list(good)
+        bad[i] += off
+        assert _argmax(1, 16, 256, bad) == nv.ERROR_MISALIGNED, i
+
+
+def test_argmax_rejects_small_workspace_and_bad_paths(lib):
+    need = nv.nvfp4_argmax_workspace_bytes(3)
+    assert need >= 3 * 8 * 16 and need % (3 * 8) == 0
+    assert nv.nvfp4_argmax_workspace_bytes(0) == 0
+    assert nv.nvfp4_argmax_workspace_bytes(6) == 2 * need
+    assert _argmax(3, 16, 256, ws_bytes=need - 1) == nv.ERROR_INVALID_VALUE
+    assert _argmax(1, 16, 256, path=6) == nv.ERROR_INVALID_VALUE
+    assert _argmax(9, 16, 256, path=nv.PATH_DOT) == nv.ERROR_INVALID_VALUE
+    assert _argmax(16, 16, 256, path=nv.PATH_INVARIANT, split=2) == nv.ERROR_INVALID_VALUE
