@@ -20,6 +20,8 @@ Protocol
   * "also": the verify shapes at M = 16 and M = 128, timed the same way (per-kernel events).
   * "invariant": the same three workloads in the batch-invariant mode (NVFP4_PATH_INVARIANT: row m
     of Y is the same bits for any M), timed the same way.
+  * "lm_head_argmax": the lm_head (N = 151936) at M = 1, 16, 128, writing the logits
+    (nvfp4_gemm) and folding them into the greedy token per row (nvfp4_gemm_argmax).
   * "full_pass": 64 layers of those shapes plus an NVFP4 lm_head (N = 151936), 12.33 GB of
     packed weights (weights seed 9 drawn on the device one tensor at a time and packed, x seed
     10), at M = 1 and M = 16: the 257 GEMMs captured as one HIP graph per M, replays timed with
@@ -253,6 +255,95 @@ def full_pass(dev, launches, reps: int):
     return out
 
 
+def graph_time_us(call, copies: int, launches: int, label: str, log_list) -> float:
+    """Average duration of one call(c): a HIP graph of LAUNCHES_PER_GRAPH back-to-back calls
+    rotating over `copies` cold weight copies, replayed until about `launches` calls ran, HIP
+    events on the stream the graph runs on around the replays (as Layer.kernel_times_us)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    call(0)                                    # eager first call: one-time set-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(LAUNCHES_PER_GRAPH):
+            call(j % copies)
+    replays = max(1, -(-launches // LAUNCHES_PER_GRAPH))
+    graph.replay()                             # warm
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    log_list.extend([label] * (1 + (replays + 1) * LAUNCHES_PER_GRAPH))
+    del graph
+    return 1e3 * e0.elapsed_time(e1) / (replays * LAUNCHES_PER_GRAPH)
+
+
+def lm_head_argmax(dev, launches, steps: int):
+    """The lm_head (K = 5120, N = 151936; weights seed 9 drawn on the device and packed, x seed
+    10) at M = 1, 16 and 128: nvfp4_gemm writing the fp32 logits, and nvfp4_gemm_argmax folding
+    them into the greedy token per row (index and value; logits never written). Both timed per
+    call over cold weight copies; the greedy tokens are checked against the argmax of the
+    logits of the same call."""
+    import numpy as np
+    import torch
+    import skinny_gemm_nvfp4_amd as nv
+    from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+    K, N = inputs.LM_HEAD_SHAPE
+    gen = torch.Generator(device=dev).manual_seed(9)
+    W = inputs.weights_on_device(gen, K, N, dev)
+    p0 = nv.pack(W)
+    del W
+    copies = max(2, -(-COLD_BYTES // rl.weight_bytes(K, N)))
+    packs = [p0] + [Layer._clone(p0) for _ in range(copies - 1)]
+    xgen = inputs.generator(10)
+    out = {"K": K, "N": N, "cold_copies": copies,
+           "timing": "HIP events around graph replays of 32 calls rotating over cold copies"}
+    for M in (1, 16, 128):
+        X = inputs.activations(xgen, M, K).to(dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        idx = torch.empty(M, dtype=torch.int32, device=dev)
+        val = torch.empty(M, dtype=torch.float32, device=dev)
+        ws = nv.argmax_workspace(M, dev)
+
+        def call_gemm(c):
+            nv.gemm(X, *packs[c], out=Y)
+
+        def call_argmax(c):
+            p = packs[c]
+            nv.gemm_argmax(X, p.Wq, p.Ws, p.g, p.N, out=(idx, val), workspace=ws)
+
+        call_gemm(0)
+        call_argmax(0)
+        torch.cuda.synchronize()
+        want = np.argmax(Y.cpu().numpy(), axis=1)
+        if not np.array_equal(idx.cpu().numpy(), want):
+            raise RuntimeError(f"lm_head M={M}: greedy tokens differ from the logits' argmax")
+        launches.extend([f"lm_head.gemm M={M} N={N} K={K}",
+                         f"lm_head.argmax M={M} N={N} K={K}"])
+        gus = graph_time_us(call_gemm, copies, max(64, steps), f"lm_head.gemm M={M} N={N} K={K}",
+                            launches)
+        aus = graph_time_us(call_argmax, copies, max(64, steps),
+                            f"lm_head.argmax M={M} N={N} K={K}", launches)
+        # compulsory bytes of the greedy-token call: weights, X and the M (index, value) pairs
+        abytes = rl.weight_bytes(K, N) + 2 * M * K + 8 * M
+        agbs = abytes / (aus * 1e-6) / 1e9
+        roof_s = max(abytes / (rl.HBM_PEAK_GBS * 1e9), rl.mfma_time_s(M, N, K))
+        out[f"m{M}"] = {"gemm": gemm_report((M, N, K), gus),
+                        "argmax": {"us": round(aus, 3), "bytes": abytes, "GB_s": round(agbs, 1),
+                                   "pct_hbm_peak": round(100 * agbs / rl.HBM_PEAK_GBS, 2),
+                                   "binding_roof": rl.binding_roof(M, N, K),
+                                   "pct_binding_roof": round(100 * roof_s / (aus * 1e-6), 2)},
+                        "logit_bytes_not_written": 4 * M * N}
+        del X, Y, idx, val, ws
+    del packs
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +356,8 @@ def main() -> int:
     ap.add_argument("--no-full-pass", action="store_true",
                     help="skip the 64-layer + lm_head weight pass at M=1 and M=16")
     ap.add_argument("--full-pass-reps", type=int, default=20)
+    ap.add_argument("--no-lm-head", action="store_true",
+                    help="skip the lm_head GEMM vs greedy-token (argmax) timing at M=1/16/128")
     ap.add_argument("--no-invariant", action="store_true",
                     help="skip timing the batch-invariant mode (NVFP4_PATH_INVARIANT)")
     ap.add_argument("--launch-log", default=None,
@@ -394,6 +487,11 @@ def main() -> int:
             del lay
             torch.cuda.empty_cache()
 
+    lmh = None
+    if not args.no_lm_head:
+        log("timing the lm_head: logits vs greedy token per row (nvfp4_gemm_argmax)")
+        lmh = lm_head_argmax(dev, launches, args.steps)
+
     fp = None
     if not args.no_full_pass:
         log("generating, packing and timing the full weight pass (64 layers + lm_head)")
@@ -418,6 +516,7 @@ def main() -> int:
         "parity": parity,
         "also": also,
         "invariant": invariant or None,
+        "lm_head_argmax": lmh,
         "full_pass": fp,
         "source_hash": ps.source_hash(),
     }

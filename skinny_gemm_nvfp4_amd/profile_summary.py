@@ -37,7 +37,9 @@ from collections import OrderedDict
 
 PACK_KERNELS = ("pack_clear_kernel", "pack_amax_kernel", "pack_scale_kernel",
                 "pack_quant_kernel")
-REDUCE_KERNEL = "batch_reduce_kernel"   # second dispatch of a split-K GEMM call
+# Dispatches that finish a GEMM call started by the dispatch before them: the split-K reduce (plain
+# or folding into argmax keys) and the greedy-token finalize of nvfp4_gemm_argmax.
+FOLLOW_KERNELS = ("batch_reduce_kernel", "batch_reduce_argmax_kernel", "argmax_finalize_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -88,13 +90,18 @@ def read_counters(path: str):
     return [per[k] for k in sorted(per)]
 
 
+def is_follow(name: str) -> bool:
+    return any(f"nvfp4::{k}" in name for k in FOLLOW_KERNELS)
+
+
 def fold_reductions(gemms):
-    """Folds each split-K reduce dispatch into the GEMM dispatch before it."""
+    """Folds each follow-on dispatch (split-K reduce, argmax finalize) into the GEMM dispatch
+    before it."""
     out = []
     for d in gemms:
-        if REDUCE_KERNEL in d["name"]:
+        if is_follow(d["name"]):
             if not out:
-                raise ValueError("a split-K reduce dispatch with no GEMM dispatch before it")
+                raise ValueError("a follow-on dispatch with no GEMM dispatch before it")
             prev = out[-1]
             if "end" in d and "start" in prev:   # kernel trace: span of both dispatches
                 prev["end"] = d["end"]
@@ -102,7 +109,10 @@ def fold_reductions(gemms):
             for k, v in d.items():               # counter collection: sums
                 if k.isupper() and isinstance(v, float):
                     prev[k] = prev.get(k, 0.0) + v
-            prev["split_k"] = True
+            if "argmax" in d["name"]:
+                prev["argmax"] = True
+            if "batch_reduce" in d["name"]:
+                prev["split_k"] = True
             continue
         out.append(d)
     return out
@@ -128,14 +138,15 @@ def group(gemms):
 
 def trace_summary(trace_csv: str, labels_path: str) -> str:
     gemms = attach_labels(read_trace(trace_csv), read_labels(labels_path))
-    lines = [f"{'GEMM':44s} {'kernel':44s} {'n':>4s} {'mean_us':>8s} {'med_us':>8s} "
+    lines = [f"{'GEMM':44s} {'kernel':56s} {'n':>4s} {'mean_us':>8s} {'med_us':>8s} "
              f"{'min_us':>8s}  grid        wg   lds    vgpr agpr scratch"]
     for lab, ds in group(gemms).items():
         us = [d["ns"] / 1e3 for d in ds]
         d0 = ds[0]
-        kname = short_name(d0["name"]) + (" +reduce" if d0.get("split_k") else "")
+        kname = (short_name(d0["name"]) + (" +reduce" if d0.get("split_k") else "") +
+                 (" +argmax" if d0.get("argmax") else ""))
         lines.append(
-            f"{lab:44s} {kname[:44]:44s} {len(us):4d} "
+            f"{lab:44s} {kname[:56]:56s} {len(us):4d} "
             f"{statistics.fmean(us):8.2f} {statistics.median(us):8.2f} {min(us):8.2f}  "
             f"{d0['grid'][0]:>5d}x{d0['grid'][1]:<4d} {d0['wg']:5d} {d0['lds']:6d} "
             f"{d0['vgpr']:4d} {d0['agpr']:4d} {d0['scratch']:6d}")

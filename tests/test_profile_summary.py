@@ -122,3 +122,22 @@ def test_mfma_busy_fraction(tmp_path):
     (tmp_path / "l.txt").write_text("m M=128 N=16 K=64\n")
     lines = ps.mfma_summary(str(tmp_path / "c.csv"), str(tmp_path / "l.txt")).splitlines()
     assert lines[1].startswith("m M=128") and lines[1].rstrip().endswith("15.6")
+
+
+FINALIZE = ("nvfp4::argmax_finalize_kernel(unsigned long long const*, int, int*, float*)")
+REDUCE_ARGMAX = ("nvfp4::batch_reduce_argmax_kernel(float const*, int, int, long long, "
+                 "float const*, unsigned long long*, int)")
+
+
+def test_argmax_follow_on_dispatches_are_folded(tmp_path):
+    # greedy-token call: GEMM 0..1000 then finalize 1100..1300 (1.3 us); a split-K greedy-token
+    # call: batch 2000..4000, reduce-argmax 4100..4400, finalize 4500..4600 (2.6 us); a plain GEMM
+    _trace(tmp_path / "t.csv", [(GEMM, 0, 1000), (FINALIZE, 1100, 200), (BATCH, 2000, 2000),
+                                (REDUCE_ARGMAX, 4100, 300), (FINALIZE, 4500, 100),
+                                (GEMM, 6000, 1000)])
+    (tmp_path / "l.txt").write_text("a M=1 N=16 K=64\nb M=128 N=16 K=64\np M=1 N=16 K=64\n")
+    lines = ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt")).splitlines()
+    assert len(lines) == 4
+    assert "+argmax" in lines[1] and "    1.30" in lines[1]
+    assert "+reduce +argmax" in lines[2] and "    2.60" in lines[2]
+    assert "+argmax" not in lines[3] and "    1.00" in lines[3]
