@@ -11,6 +11,8 @@ What it computes, from the pages and the workload recipe:
   Per tensor g = amax / (6*448); per 16-block along K an E4M3 scale s = round(block_amax / (6g));
   codes = round-to-nearest E2M1 of w / (s*g); Y = X . (e2m1(code) * s * g).
   Greedy token per row = first column of the row maximum ("SparkInfer" README, greedy decode).
+  Grouped GEMM: expert-sorted rows through their expert's weights ("SparkInfer" README, fused
+  MoE FFN and expert dispatch).
 Pins for every function live in tests/test_oracle_*.py; none is "parity unpinned".
 """
 import ctypes
@@ -151,6 +153,35 @@ def gemm(X_bits: np.ndarray, Wq: np.ndarray, Ws: np.ndarray, g, cols=None):
                            _ptr(Y, ctypes.c_double), _ptr(A, ctypes.c_double))
     if rc:
         raise MemoryError("oracle_gemm could not allocate its buffers")
+    return Y, A
+
+
+def grouped_gemm(X_bits: np.ndarray, offsets, Wq: np.ndarray, Ws: np.ndarray, g):
+    """Grouped (mixture-of-experts) GEMM: rows offsets[e] .. offsets[e+1]-1 of X go through
+    expert e's weights, Y[t] = X[t] . dequant(Wq[e], Ws[e], g[e]). Returns Y and A = sum |x*w|,
+    float64 [T][N].
+
+    The pages' engine has a fused MoE FFN kernel and a sync-free router with expert dispatch
+    ("SparkInfer" README, section "Layout & scoring"); its MoE targets read only the routed
+    experts' weights per token. Rows arrive sorted by expert (the router's dispatch order);
+    offsets has E + 1 non-decreasing entries from 0 to T. Each expert's block is the plain GEMM
+    of this module, so the arithmetic is exactly gemm()'s.
+    """
+    X_bits = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = Wq.shape[0]
+    T, K = X_bits.shape
+    N = Wq.shape[1]
+    if offsets.shape != (E + 1,) or offsets[0] != 0 or offsets[-1] != T or \
+            np.any(np.diff(offsets) < 0):
+        raise ValueError("offsets must be E + 1 non-decreasing entries from 0 to T")
+    g = np.broadcast_to(np.asarray(g, dtype=np.float32), (E,))
+    Y = np.zeros((T, N), dtype=np.float64)
+    A = np.zeros((T, N), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            Y[r0:r1], A[r0:r1] = gemm(X_bits[r0:r1], Wq[e], Ws[e], g[e])
     return Y, A
 
 
