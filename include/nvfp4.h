@@ -220,6 +220,46 @@ nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
  * 0 if M < 1. */
 uint64_t nvfp4_argmax_workspace_bytes(int M);
 
+/*
+ * nvfp4_gemm_grouped -- grouped (mixture-of-experts) GEMM, one launch, no host synchronisation:
+ *
+ *     Y[t] = X[t] . dequant(Wq_e, Wscale_e, gscale[e])   for offsets[e] <= t < offsets[e+1]
+ *
+ * The pages' engine runs mixture-of-experts models with a fused MoE FFN kernel and a router that
+ * dispatches tokens to experts on the device ("SparkInfer" README, section "Layout & scoring"; its
+ * MoE targets). At decode each token reads only its routed experts, a few rows per expert: the
+ * same bandwidth-bound dot product as nvfp4_gemm at M = 1, over pieces whose sizes only the device
+ * knows. The rows of X arrive grouped by expert (the dispatch order of the router, which is not
+ * part of this library); the kernel reads the row counts from `offsets` on the device and deals
+ * the (row chunk, 4-column group) items evenly to every wavefront of the grid.
+ *
+ *   T        rows of X and Y (token-expert pairs); 0 is allowed and does nothing
+ *   E        experts, 1 <= E <= 2048
+ *   N, K     the shape of every expert's weight (K % 16 == 0, as for nvfp4_gemm)
+ *   X        in:  bf16 bits [T][K], device, rows sorted by expert
+ *   offsets  in:  int32 [E + 1], device: expert e owns rows offsets[e] .. offsets[e+1] - 1;
+ *                 meant to be non-decreasing from 0 to T. Entries are clamped to [0, T] and an
+ *                 expert whose end precedes its start has no rows: bad offsets give unspecified
+ *                 values in Y (rows no expert owns are not written), never an access out of range
+ *   Wq       in:  E packed code arrays back to back, expert e at Wq + e * nvfp4_codes_bytes(N, K)
+ *                 (each as nvfp4_pack writes it)
+ *   Wscale   in:  E packed scale arrays, expert e at Wscale + e * nvfp4_scales_bytes(N, K)
+ *   gscale   in:  fp32 [E], device: tensor scale of each expert
+ *   Y        out: fp32 [T][N], device; every row some expert owns is fully written
+ *   rows_per_item  rows of one expert taken together (each weight byte is read once per chunk of
+ *                 this many rows): 1, 2 or 4, or 0 to choose from T and E. Results are the same
+ *                 bits for every value.
+ *   stream   hipStream_t
+ * Accuracy as nvfp4_gemm (fp32 accumulation, g once per output). Sizes: T * ceil(N / 4) < 2^40
+ * and E * nvfp4_codes_bytes(N, K) < 2^62, else NVFP4_ERROR_INVALID_VALUE. Alignment: X, Wq, Wscale
+ * 16 bytes; offsets, gscale, Y 4 bytes. Deterministic; a row's result does not depend on the
+ * other rows, on rows_per_item or on the grid.
+ */
+nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
+                                  const int32_t *offsets, const uint8_t *Wq,
+                                  const uint8_t *Wscale, const float *gscale, float *Y,
+                                  int rows_per_item, void *stream);
+
 /* Bytes of Wq for an N x K weight: 64 * ceil(N/4) * ceil(K/32); 0 if N < 1 or K < 1. */
 uint64_t nvfp4_codes_bytes(int N, int K);
 
@@ -230,7 +270,7 @@ uint64_t nvfp4_scales_bytes(int N, int K);
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

@@ -65,6 +65,8 @@ def load_library() -> ctypes.CDLL:
     L.nvfp4_gemm_argmax_path.restype = ci
     L.nvfp4_argmax_workspace_bytes.argtypes = [ci]
     L.nvfp4_argmax_workspace_bytes.restype = ctypes.c_uint64
+    L.nvfp4_gemm_grouped.argtypes = [ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, ci, vp]
+    L.nvfp4_gemm_grouped.restype = ci
     L.nvfp4_status_string.argtypes = [ci]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_abi_version.argtypes = []
@@ -118,6 +120,13 @@ def nvfp4_gemm_argmax_path(path: int, split: int, M: int, N: int, K: int, X: int
 
 def nvfp4_argmax_workspace_bytes(M: int) -> int:
     return load_library().nvfp4_argmax_workspace_bytes(M)
+
+
+def nvfp4_gemm_grouped(T: int, E: int, N: int, K: int, X: int, offsets: int, Wq: int,
+                       Wscale: int, gscale: int, Y: int, rows_per_item: int,
+                       stream: Optional[int]) -> int:
+    return load_library().nvfp4_gemm_grouped(T, E, N, K, X, offsets, Wq, Wscale, gscale, Y,
+                                             rows_per_item, stream)
 
 
 def nvfp4_codes_bytes(N: int, K: int) -> int:
@@ -255,3 +264,41 @@ def gemm_argmax(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Te
     if st != SUCCESS:
         raise NVFP4Error(st, "nvfp4_gemm_argmax")
     return index, value
+
+
+def pack_experts(Ws_fp32, stream=None):
+    """Quantise a list of E fp32 W[K, N] (device) into back-to-back expert arrays:
+    (Wq [E][codes_shape], Ws [E][scales_shape], g [E]), one nvfp4_pack per expert."""
+    K, N = Ws_fp32[0].shape
+    E = len(Ws_fp32)
+    dev = Ws_fp32[0].device
+    Wq = torch.empty((E,) + codes_shape(N, K), dtype=torch.uint8, device=dev)
+    Wsc = torch.empty((E,) + scales_shape(N, K), dtype=torch.uint8, device=dev)
+    g = torch.empty(E, dtype=torch.float32, device=dev)
+    for e, W in enumerate(Ws_fp32):
+        pack(W, stream=stream, out=(Wq[e], Wsc[e], g[e:e + 1]))
+    return Wq, Wsc, g
+
+
+def gemm_grouped(X: torch.Tensor, offsets: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor,
+                 g: torch.Tensor, N: int, rows_per_item: int = 0, stream=None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Grouped GEMM: rows offsets[e] .. offsets[e+1]-1 of X (bf16 [T, K], sorted by expert)
+    through expert e's packed weights Wq[e], Ws[e], g[e]; returns fp32 Y [T, N]."""
+    T, K = X.shape
+    E = Wq.shape[0]
+    _check_device(X, "X", torch.bfloat16, (T, K))
+    _check_device(offsets, "offsets", torch.int32, (E + 1,))
+    _check_device(Wq, "Wq", torch.uint8, (E,) + codes_shape(N, K))
+    _check_device(Ws, "Ws", torch.uint8, (E,) + scales_shape(N, K))
+    _check_device(g, "g", torch.float32, (E,))
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=X.device)
+    else:
+        _check_device(out, "out", torch.float32, (T, N))
+    st = nvfp4_gemm_grouped(T, E, N, K, X.data_ptr(), offsets.data_ptr(), Wq.data_ptr(),
+                            Ws.data_ptr(), g.data_ptr(), out.data_ptr(), rows_per_item,
+                            _stream(stream))
+    if st != SUCCESS:
+        raise NVFP4Error(st, "nvfp4_gemm_grouped")
+    return out

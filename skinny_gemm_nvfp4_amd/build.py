@@ -26,7 +26,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
-SOURCES = ["api.cpp", "pack.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "pack.hip", "gemm.hip", "grouped.hip"]
 ARCH = "gfx950"
 
 

@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "launch.h"
 
 namespace {
@@ -139,6 +141,42 @@ nvfp4_status_t nvfp4_gemm_argmax(int M, int N, int K, const uint16_t *X, const u
 {
     return nvfp4_gemm_argmax_path(NVFP4_PATH_AUTO, 0, M, N, K, X, Wq, Wscale, gscale, index, value,
                                   workspace, workspace_bytes, stream);
+}
+
+nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
+                                  const int32_t *offsets, const uint8_t *Wq,
+                                  const uint8_t *Wscale, const float *gscale, float *Y,
+                                  int rows_per_item, void *stream)
+{
+    if (T < 0 || E < 1 || E > nvfp4::kGroupedMaxExperts)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!sizes_ok(std::max(T, 1), N, K))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (rows_per_item != 0 && rows_per_item != 1 && rows_per_item != 2 && rows_per_item != 4)
+        return NVFP4_ERROR_INVALID_VALUE;
+    // Every expert's weights, and the work items (row chunks x column groups), in range.
+    const unsigned long long per = nvfp4::codes_bytes(N, K);
+    if ((unsigned long long)E * per >= kMaxBytes ||
+        (unsigned long long)T * (unsigned long long)nvfp4::num_groups(N) >= (1ULL << 40))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!X || !offsets || !Wq || !Wscale || !gscale || !Y)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(offsets, 4) ||
+        !aligned(gscale, 4) || !aligned(Y, 4))
+        return NVFP4_ERROR_MISALIGNED;
+    nvfp4::GroupedArgs a;
+    a.X = X;
+    a.offsets = offsets;
+    a.Wq = Wq;
+    a.Ws = Wscale;
+    a.gscale = gscale;
+    a.Y = Y;
+    a.T = T;
+    a.E = E;
+    a.N = N;
+    a.K = K;
+    const int mr = nvfp4::grouped_rows_per_item(T, E, rows_per_item);
+    return from_hip(nvfp4::launch_grouped(a, mr, static_cast<hipStream_t>(stream)));
 }
 
 const char *nvfp4_status_string(nvfp4_status_t status)

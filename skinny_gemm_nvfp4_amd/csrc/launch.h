@@ -100,6 +100,26 @@ hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *i
 // Compute units of the current device (cached per device).
 int device_compute_units();
 
+// Grouped (mixture-of-experts) GEMM: rows offsets[e] .. offsets[e+1] - 1 of X through expert e.
+constexpr int kGroupedMaxExperts = 2048;
+
+struct GroupedArgs {
+    const uint16_t *X;        // bf16 [T][K], rows sorted by expert
+    const int *offsets;       // [E + 1], device
+    const uint8_t *Wq;        // E packed weights, each codes_bytes(N, K) bytes
+    const uint8_t *Ws;        // E packed scales, each scales_bytes(N, K) bytes
+    const float *gscale;      // [E]
+    float *Y;                 // fp32 [T][N]
+    int T, E, N, K;
+};
+
+// Rows of one expert per work item of the grouped kernel: `requested` (1, 2 or 4) or, for 0, a
+// choice from the total rows T and the expert count E.
+int grouped_rows_per_item(int T, int E, int requested);
+
+// Launch the grouped (mixture-of-experts) GEMM. Largest E: kGroupedMaxExperts (grouped.h).
+hipError_t launch_grouped(const GroupedArgs &a, int rows_per_item, hipStream_t stream);
+
 // Launch the pack sequence (clear, amax, tensor scale, quantise) on the stream.
 hipError_t launch_pack(int K, int N, const float *W, uint8_t *Wq, uint8_t *Ws, float *gscale,
                        hipStream_t stream);

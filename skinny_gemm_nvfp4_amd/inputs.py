@@ -169,3 +169,33 @@ def integer_activations(gen: torch.Generator, M: int, K: int, lo: int = -8, hi: 
     """bf16 X[M, K] holding integers in [lo, hi] (exact in bf16)."""
     x = torch.randint(lo, hi + 1, (M, K), generator=gen, dtype=torch.int32)
     return x.to(torch.float32).to(torch.bfloat16)
+
+
+# ---- mixture-of-experts workload (grouped GEMM) ----
+# Expert shapes of a small mixture-of-experts model of the pages' family (a 3B-active MoE of the
+# size the SparkInfer README benchmarks): hidden 2048, 128 experts, 8 routed per token, expert
+# intermediate 768, so gate/up is K = 2048, N = 2 * 768 and down is K = 768, N = 2048.
+MOE_HIDDEN = 2048
+MOE_EXPERTS = 128
+MOE_TOPK = 8
+MOE_INTERMEDIATE = 768
+MOE_SHAPES: Dict[str, Tuple[int, int]] = {
+    "gate_up": (MOE_HIDDEN, 2 * MOE_INTERMEDIATE),
+    "down": (MOE_INTERMEDIATE, MOE_HIDDEN),
+}
+
+
+def moe_routing(gen: torch.Generator, tokens: int, experts: int, topk: int):
+    """Synthetic router output, sorted for dispatch: each token picks `topk` distinct experts
+    uniformly (randperm per token). Returns (token of each dispatched row, offsets [E + 1]): rows
+    are grouped by expert, tokens ascending within an expert; expert e owns rows offsets[e] ..
+    offsets[e+1] - 1."""
+    picks = [torch.randperm(experts, generator=gen)[:topk] for _ in range(tokens)]
+    pairs = sorted((int(e), t) for t, p in enumerate(picks) for e in p)
+    token_of_row = torch.tensor([t for _, t in pairs], dtype=torch.int64)
+    counts = torch.zeros(experts, dtype=torch.int64)
+    for e, _ in pairs:
+        counts[e] += 1
+    offsets = torch.zeros(experts + 1, dtype=torch.int32)
+    offsets[1:] = torch.cumsum(counts, 0).to(torch.int32)
+    return token_of_row, offsets

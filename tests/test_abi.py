@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert nv.abi_version() == 3
+    assert nv.abi_version() == 4
     for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH):
         assert nv.status_string(st)
     assert nv.status_string(99) == "unknown status"
@@ -206,3 +206,37 @@ def test_argmax_rejects_small_workspace_and_bad_paths(lib):
     assert _argmax(1, 16, 256, path=6) == nv.ERROR_INVALID_VALUE
     assert _argmax(9, 16, 256, path=nv.PATH_DOT) == nv.ERROR_INVALID_VALUE
     assert _argmax(16, 16, 256, path=nv.PATH_INVARIANT, split=2) == nv.ERROR_INVALID_VALUE
+
+
+# ---- nvfp4_gemm_grouped: sizes, experts, pointers, alignment, rows per item ----
+
+def _grouped(T, E, N, K, ptrs=None, rpi=0):
+    p = ptrs or [A16, A8F, A16B, A16C, A16D, A16E]
+    return nv.nvfp4_gemm_grouped(T, E, N, K, *p, rpi, None)
+
+
+@pytest.mark.parametrize("T,E,N,K", [(-1, 4, 16, 256), (1, 0, 16, 256), (1, 2049, 16, 256),
+                                     (1, 4, 0, 256), (1, 4, 16, 8), (1, 4, 16, 24),
+                                     (1, 4, 16, 2 ** 22 + 16), (2 ** 31 - 1, 4, 2 ** 12, 16)])
+def test_grouped_rejects_bad_sizes(lib, T, E, N, K):
+    assert _grouped(T, E, N, K) == nv.ERROR_INVALID_VALUE
+
+
+def test_grouped_rejects_null_misaligned_and_rows_per_item(lib):
+    good = [A16, A8F, A16B, A16C, A16D, A16E]
+    for i in range(len(good)):
+        bad = list(good)
+        bad[i] = 0
+        assert _grouped(4, 8, 16, 256, bad) == nv.ERROR_INVALID_VALUE, i
+    # X, Wq, Wscale need 16 bytes; offsets, gscale, Y 4
+    for i, off in [(0, 8), (1, 2), (2, 4), (3, 8), (4, 2), (5, 2)]:
+        bad = list(good)
+        bad[i] += off
+        assert _grouped(4, 8, 16, 256, bad) == nv.ERROR_MISALIGNED, i
+    for rpi in (-1, 3, 8):
+        assert _grouped(4, 8, 16, 256, rpi=rpi) == nv.ERROR_INVALID_VALUE
+
+
+def test_grouped_with_no_rows_does_nothing(lib):
+    # T = 0 is valid and launches nothing (so it needs no GPU)
+    assert _grouped(0, 8, 16, 256) == nv.SUCCESS
