@@ -22,6 +22,8 @@ Protocol
     of Y is the same bits for any M), timed the same way.
   * "lm_head_argmax": the lm_head (N = 151936) at M = 1, 16, 128, writing the logits
     (nvfp4_gemm) and folding them into the greedy token per row (nvfp4_gemm_argmax).
+  * "moe_grouped": the grouped (mixture-of-experts) GEMM, 128 experts with 8 routed per token,
+    at decode (1 token) and verification (16 tokens), per call over rotating routings.
   * "full_pass": 64 layers of those shapes plus an NVFP4 lm_head (N = 151936), 12.33 GB of
     packed weights (weights seed 9 drawn on the device one tensor at a time and packed, x seed
     10), at M = 1 and M = 16: the 257 GEMMs captured as one HIP graph per M, replays timed with
@@ -344,6 +346,58 @@ def lm_head_argmax(dev, launches, steps: int):
     return out
 
 
+def moe_grouped(dev, launches, steps: int):
+    """The grouped (mixture-of-experts) GEMM on the expert shapes of the workload (128 experts,
+    8 routed per token; gate/up K = 2048, N = 1536 and down K = 768, N = 2048): decode (1 token,
+    8 rows) and verification (16 tokens, 128 rows). Weights (seed 11, drawn on the device) in 4
+    copies; 32 synthetic routings (seed 12) rotate with the copies, so consecutive calls read
+    different experts and the weights stream from HBM. Bytes of a call: the routed experts'
+    packed weights (each read once), X, Y and the offsets."""
+    import torch
+    import skinny_gemm_nvfp4_amd as nv
+    from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+    E, topk = inputs.MOE_EXPERTS, inputs.MOE_TOPK
+    copies, nrout = 4, LAUNCHES_PER_GRAPH
+    wgen = torch.Generator(device=dev).manual_seed(11)
+    rgen = inputs.generator(12)
+    out = {"experts": E, "topk": topk, "cold_copies": copies, "routings": nrout,
+           "timing": "HIP events around graph replays of 32 calls (routing r, copy r % 4)"}
+    for shape, (K, N) in inputs.MOE_SHAPES.items():
+        Ws_fp32 = [inputs.weights_on_device(wgen, K, N, dev) for _ in range(E)]
+        packed = [nv.pack_experts(Ws_fp32)]
+        del Ws_fp32
+        packed += [tuple(t.clone() for t in packed[0]) for _ in range(copies - 1)]
+        torch.cuda.synchronize()
+        for tokens in (1, 16):
+            rows = tokens * topk
+            cases = []
+            for _ in range(nrout):
+                tok, offs = inputs.moe_routing(rgen, tokens, E, topk)
+                x = inputs.activations(rgen, tokens, K)
+                used = int((offs[1:] > offs[:-1]).sum())
+                cases.append((x[tok].to(dev), offs.to(dev), used))
+            Y = torch.empty((rows, N), dtype=torch.float32, device=dev)
+
+            def call(c, cases=cases, Y=Y, N=N):
+                X, offs, _ = cases[call.i % nrout]
+                call.i += 1
+                nv.gemm_grouped(X, offs, *packed[c], N, out=Y)
+            call.i = 0
+            label = f"moe.{shape} tokens={tokens} T={rows} N={N} K={K}"
+            us = graph_time_us(lambda c: call(c), copies, max(64, steps), label, launches)
+            nbytes = (sum(u for _, _, u in cases) / nrout) * rl.weight_bytes(K, N) + \
+                2 * rows * K + 4 * rows * N + 4 * (E + 1)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[f"{shape}_tokens{tokens}"] = {
+                "T": rows, "N": N, "K": K, "us": round(us, 3),
+                "experts_read_avg": round(sum(u for _, _, u in cases) / nrout, 2),
+                "bytes_avg": round(nbytes), "GB_s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / rl.HBM_PEAK_GBS, 2)}
+        del packed
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +410,8 @@ def main() -> int:
     ap.add_argument("--no-full-pass", action="store_true",
                     help="skip the 64-layer + lm_head weight pass at M=1 and M=16")
     ap.add_argument("--full-pass-reps", type=int, default=20)
+    ap.add_argument("--no-moe", action="store_true",
+                    help="skip the grouped (mixture-of-experts) GEMM timing")
     ap.add_argument("--no-lm-head", action="store_true",
                     help="skip the lm_head GEMM vs greedy-token (argmax) timing at M=1/16/128")
     ap.add_argument("--no-invariant", action="store_true",
@@ -492,6 +548,11 @@ def main() -> int:
         log("timing the lm_head: logits vs greedy token per row (nvfp4_gemm_argmax)")
         lmh = lm_head_argmax(dev, launches, args.steps)
 
+    moe = None
+    if not args.no_moe:
+        log("timing the grouped (mixture-of-experts) GEMM: decode and verify routings")
+        moe = moe_grouped(dev, launches, args.steps)
+
     fp = None
     if not args.no_full_pass:
         log("generating, packing and timing the full weight pass (64 layers + lm_head)")
@@ -517,6 +578,7 @@ def main() -> int:
         "also": also,
         "invariant": invariant or None,
         "lm_head_argmax": lmh,
+        "moe_grouped": moe,
         "full_pass": fp,
         "source_hash": ps.source_hash(),
     }
