@@ -13,6 +13,8 @@ What it computes, from the pages and the workload recipe:
   Greedy token per row = first column of the row maximum ("SparkInfer" README, greedy decode).
   Grouped GEMM: expert-sorted rows through their expert's weights ("SparkInfer" README, fused
   MoE FFN and expert dispatch).
+  Layer neighbours: RMSNorm to bf16 before the GEMM, SiLU(gate) * up after it ("SparkInfer"
+  README, RMSNorm and fused FFN kernels).
 Pins for every function live in tests/test_oracle_*.py; none is "parity unpinned".
 """
 import ctypes
@@ -183,6 +185,61 @@ def grouped_gemm(X_bits: np.ndarray, offsets, Wq: np.ndarray, Ws: np.ndarray, g)
         if r1 > r0:
             Y[r0:r1], A[r0:r1] = gemm(X_bits[r0:r1], Wq[e], Ws[e], g[e])
     return Y, A
+
+
+def bf16_round(v: np.ndarray):
+    """Round float64 values to bf16, to nearest with ties to even, in one step (no float32 in
+    between). Returns (bf16 bit patterns uint16, the exact rounded values float64, the spacing
+    of bf16 values at each input's binade float64, the distance of each input to the nearest
+    rounding boundary float64). Finite inputs below the bf16 overflow threshold only."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)                       # v = f * 2^e, 0.5 <= |f| < 1
+    e = np.maximum(e, -125)                  # subnormal bf16 spacing stays 2^-133
+    ulp = np.ldexp(1.0, e - 8)               # 8 significant bits
+    q = v / ulp                              # exact: division by a power of two
+    r = np.rint(q)                           # nearest integer, ties to even
+    vals = r * ulp
+    dist = np.abs(np.abs(q - np.floor(q)) - 0.5) * ulp
+    bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return bits, vals, ulp, dist
+
+
+def rmsnorm_bf16(X_bits: np.ndarray, gamma_bits: np.ndarray, eps: float, window: float):
+    """RMSNorm of bf16 rows, rounded to the bf16 activations a GEMM takes:
+    xhat[m, k] = bf16( x[m, k] * gamma[k] / sqrt(mean_k x[m, k]^2 + eps) ), computed in float64
+    and rounded once.
+
+    The pages' engine has an RMSNorm kernel next to its decode GEMV ("SparkInfer" README, section
+    "Layout & scoring"); in a dense decoder layer it produces the input of the q/k/v and gate/up
+    projections. The pages fix neither the precision nor the rounding of its output; the reading
+    here is the exact value rounded to nearest-even bf16.
+
+    A kernel computes the same value in fp32, within a relative error it states; where the exact
+    value lies within `window` (relative) of a bf16 rounding boundary, either neighbour is a
+    correct result. Returns (xhat bits uint16 [M][K], flag bool [M][K] marking those elements,
+    ulp float64 [M][K] = the bf16 spacing there).
+    """
+    X_bits = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    gamma_bits = np.ascontiguousarray(gamma_bits, dtype=np.uint16)
+    x = (X_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    gam = (gamma_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if x.ndim != 2 or gam.shape != (x.shape[1],):
+        raise ValueError("X must be [M][K] and gamma [K]")
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    v = x * gam[None, :] / np.sqrt(ms + float(eps))
+    bits, _, ulp, dist = bf16_round(v)
+    flag = dist < window * np.abs(v)
+    return bits, flag, ulp
+
+
+def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """Gated FFN activation of the dense layer family: SiLU(gate) * up = gate * up / (1 + e^-gate),
+    float64, elementwise. The pages name the fused FFN next to the GEMMs ("SparkInfer" README,
+    "Layout & scoring"); the SiLU gate is the reading taken for that family's FFN."""
+    gate = np.asarray(gate, dtype=np.float64)
+    up = np.asarray(up, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return gate * up / (1.0 + np.exp(-gate))
 
 
 def argmax_rows(Y: np.ndarray) -> np.ndarray:
