@@ -260,6 +260,43 @@ nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
                                   const uint8_t *Wscale, const float *gscale, float *Y,
                                   int rows_per_item, void *stream);
 
+/*
+ * nvfp4_gemm_fused -- the GEMM with its decode-layer neighbours folded in: an RMSNorm of X
+ * before it and/or the gated FFN activation SiLU(gate) * up after it.
+ *
+ * The pages' engine has RMSNorm and fused FFN kernels next to its decode GEMV ("SparkInfer"
+ * README, section "Layout & scoring"). In a dense decoder layer the q/k/v and gate/up projections
+ * read RMSNorm(hidden), and down_proj reads SiLU(gate) * up of the gate/up projection (the SiLU
+ * gate is the reading taken for the model family's FFN). Folding them in saves the round trips of
+ * the normalised activations and of the M x N gate/up output, and two launches.
+ *
+ * fuse = NVFP4_FUSE_RMSNORM, NVFP4_FUSE_SILU_MUL or both (bitwise or):
+ *   NVFP4_FUSE_RMSNORM   X is replaced by xhat[m][k] = bf16((x[m][k] * r_m) * gamma[k]), rounded
+ *                        to nearest even, with r_m = 1 / sqrt(mean_k x[m][k]^2 + eps) in fp32
+ *                        (the sum of squares within a relative (K / 64 + 32) * 2^-24 of exact);
+ *                        then the GEMM runs on xhat.
+ *   NVFP4_FUSE_SILU_MUL  the weight is a fused gate/up matrix whose columns interleave in groups of
+ *                        four: columns 8q .. 8q + 3 are gate columns 4q .. 4q + 3 and columns
+ *                        8q + 4 .. 8q + 7 are up columns 4q .. 4q + 3 (N % 8 == 0, I = N / 2).
+ *                        Instead of Y the call writes H[m][j] = bf16(SiLU(gate) * up), with gate
+ *                        and up the fp32 outputs of columns 8q + c and 8q + 4 + c for
+ *                        j = 4q + c, SiLU(v) = v / (1 + e^-v).
+ *   M, N, K, X, Wq, Wscale, gscale   as for nvfp4_gemm
+ *   gamma    in: bf16 bits [K], device, 16-byte aligned (RMSNorm only; else ignored)
+ *   eps      RMSNorm epsilon, finite and >= 0 (e.g. 1e-6)
+ *   out      out: fp32 Y [M][N] (4-byte aligned) without NVFP4_FUSE_SILU_MUL, bf16 bits
+ *            H [M][N / 2] (2-byte aligned) with it; device
+ * Kernels: the dot-product kernel for M <= 4 (X normalised once in LDS), else the 16-row
+ * matrix-core kernel per 16-row block of X (which reads the weights once per block). Errors as
+ * for nvfp4_gemm.
+ */
+enum { NVFP4_FUSE_RMSNORM = 1, NVFP4_FUSE_SILU_MUL = 2 };
+
+nvfp4_status_t nvfp4_gemm_fused(int fuse, int M, int N, int K, const uint16_t *X,
+                                const uint16_t *gamma, float eps, const uint8_t *Wq,
+                                const uint8_t *Wscale, const float *gscale, void *out,
+                                void *stream);
+
 /* Bytes of Wq for an N x K weight: 64 * ceil(N/4) * ceil(K/32); 0 if N < 1 or K < 1. */
 uint64_t nvfp4_codes_bytes(int N, int K);
 
@@ -270,7 +307,7 @@ uint64_t nvfp4_scales_bytes(int N, int K);
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

@@ -26,6 +26,9 @@ PATH_BATCH = 3
 PATH_BATCH_SPLITK = 4
 PATH_INVARIANT = 5   # row m of Y is the same bits for every M
 
+FUSE_RMSNORM = 1     # nvfp4_gemm_fused: RMSNorm of X before the GEMM
+FUSE_SILU_MUL = 2    # nvfp4_gemm_fused: SiLU(gate) * up of the interleaved gate/up output
+
 _lib = None
 
 
@@ -67,6 +70,8 @@ def load_library() -> ctypes.CDLL:
     L.nvfp4_argmax_workspace_bytes.restype = ctypes.c_uint64
     L.nvfp4_gemm_grouped.argtypes = [ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, ci, vp]
     L.nvfp4_gemm_grouped.restype = ci
+    L.nvfp4_gemm_fused.argtypes = [ci, ci, ci, ci, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp]
+    L.nvfp4_gemm_fused.restype = ci
     L.nvfp4_status_string.argtypes = [ci]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_abi_version.argtypes = []
@@ -127,6 +132,12 @@ def nvfp4_gemm_grouped(T: int, E: int, N: int, K: int, X: int, offsets: int, Wq:
                        stream: Optional[int]) -> int:
     return load_library().nvfp4_gemm_grouped(T, E, N, K, X, offsets, Wq, Wscale, gscale, Y,
                                              rows_per_item, stream)
+
+
+def nvfp4_gemm_fused(fuse: int, M: int, N: int, K: int, X: int, gamma: int, eps: float,
+                     Wq: int, Wscale: int, gscale: int, out: int, stream: Optional[int]) -> int:
+    return load_library().nvfp4_gemm_fused(fuse, M, N, K, X, gamma, eps, Wq, Wscale, gscale,
+                                           out, stream)
 
 
 def nvfp4_codes_bytes(N: int, K: int) -> int:
@@ -301,4 +312,49 @@ def gemm_grouped(X: torch.Tensor, offsets: torch.Tensor, Wq: torch.Tensor, Ws: t
                             _stream(stream))
     if st != SUCCESS:
         raise NVFP4Error(st, "nvfp4_gemm_grouped")
+    return out
+
+
+def interleave_gate_up(W: torch.Tensor) -> torch.Tensor:
+    """Column order nvfp4_gemm_fused's SiLU(gate) * up expects, from a fused gate/up weight
+    W[K, 2I] whose first I columns are gate and last I are up: columns 8q .. 8q+3 become gate
+    4q .. 4q+3 and 8q+4 .. 8q+7 up 4q .. 4q+3 (I % 4 == 0). A permutation, no arithmetic."""
+    K, N2 = W.shape
+    I = N2 // 2
+    if N2 % 8:
+        raise ValueError("the gate/up weight needs 2I columns with I % 4 == 0")
+    g = W[:, :I].reshape(K, I // 4, 4)
+    u = W[:, I:].reshape(K, I // 4, 4)
+    return torch.stack([g, u], dim=2).reshape(K, N2).contiguous()
+
+
+def gemm_fused(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Tensor, N: int,
+               gamma: Optional[torch.Tensor] = None, eps: float = 1e-6, silu_mul: bool = False,
+               stream=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The GEMM with its layer neighbours: RMSNorm(X; gamma, eps) first when gamma is given, and
+    SiLU(gate) * up of an interleaved gate/up weight (interleave_gate_up) when silu_mul. Returns
+    fp32 Y [M, N], or bf16 H [M, N/2] with silu_mul."""
+    M, K = X.shape
+    _check_device(X, "X", torch.bfloat16, (M, K))
+    _check_device(Wq, "Wq", torch.uint8, codes_shape(N, K))
+    _check_device(Ws, "Ws", torch.uint8, scales_shape(N, K))
+    _check_device(g, "g", torch.float32, (1,))
+    fuse = 0
+    if gamma is not None:
+        _check_device(gamma, "gamma", torch.bfloat16, (K,))
+        fuse |= FUSE_RMSNORM
+    if silu_mul:
+        fuse |= FUSE_SILU_MUL
+    if fuse == 0:
+        raise ValueError("gemm_fused needs gamma, silu_mul or both (else use gemm)")
+    shape, dtype = ((M, N // 2), torch.bfloat16) if silu_mul else ((M, N), torch.float32)
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=X.device)
+    else:
+        _check_device(out, "out", dtype, shape)
+    st = nvfp4_gemm_fused(fuse, M, N, K, X.data_ptr(), 0 if gamma is None else gamma.data_ptr(),
+                          float(eps), Wq.data_ptr(), Ws.data_ptr(), g.data_ptr(), out.data_ptr(),
+                          _stream(stream))
+    if st != SUCCESS:
+        raise NVFP4Error(st, "nvfp4_gemm_fused")
     return out

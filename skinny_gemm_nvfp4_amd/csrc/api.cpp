@@ -179,6 +179,39 @@ nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
     return from_hip(nvfp4::launch_grouped(a, mr, static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status_t nvfp4_gemm_fused(int fuse, int M, int N, int K, const uint16_t *X,
+                                const uint16_t *gamma, float eps, const uint8_t *Wq,
+                                const uint8_t *Wscale, const float *gscale, void *out,
+                                void *stream)
+{
+    if (fuse < 1 || fuse > (NVFP4_FUSE_RMSNORM | NVFP4_FUSE_SILU_MUL))
+        return NVFP4_ERROR_INVALID_VALUE;
+    const bool norm = (fuse & NVFP4_FUSE_RMSNORM) != 0;
+    const bool silu = (fuse & NVFP4_FUSE_SILU_MUL) != 0;
+    if (!sizes_ok(M, N, K) || (silu && N % 8 != 0))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (norm && !(eps >= 0.0f && eps <= 3.0e38f))   // also rejects NaN
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!X || !Wq || !Wscale || !gscale || !out || (norm && !gamma))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
+        (norm && !aligned(gamma, 16)) || !aligned(out, silu ? 2 : 4))
+        return NVFP4_ERROR_MISALIGNED;
+    nvfp4::GemmArgs a;
+    a.X = X;
+    a.Wq = Wq;
+    a.Ws = Wscale;
+    a.gscale = gscale;
+    a.Y = silu ? nullptr : static_cast<float *>(out);
+    a.H = silu ? static_cast<uint16_t *>(out) : nullptr;
+    a.gamma = norm ? gamma : nullptr;
+    a.eps = eps;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    return from_hip(nvfp4::launch_gemm_fused(a, static_cast<hipStream_t>(stream)));
+}
+
 const char *nvfp4_status_string(nvfp4_status_t status)
 {
     switch (status) {

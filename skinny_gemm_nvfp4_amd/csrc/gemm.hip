@@ -166,37 +166,48 @@ hipError_t allow_lds(const void *fn, int bytes)
     std::lock_guard<std::mutex> lock(mu);
     if (done.count({dev, fn}))
         return hipSuccess;
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    // The dynamic limit is what the kernel's static arrays leave of the compute unit's LDS.
+    hipFuncAttributes attr;
+    e = hipFuncGetAttributes(&attr, fn);
+    if (e != hipSuccess)
+        return e;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLds - (int)attr.sharedSizeBytes);
     if (e == hipSuccess)
         done.insert({dev, fn});
     return e;
 }
 
-// Workgroups over the 4-column groups: one per compute unit, at most one per group.
-int group_grid(int N)
+// Workgroups over the 4-column groups: one per compute unit, at most one per group (per pair of
+// groups when `pair`: the SiLU(gate) * up epilogue needs the gate and up groups of a pair in the
+// same workgroup).
+int group_grid(int N, bool pair = false)
 {
-    return std::max(1, std::min(compute_units(), num_groups(N)));
+    return std::max(1, std::min(compute_units(), num_groups(N) / (pair ? 2 : 1)));
 }
 
 // A workgroup's code bytes must stay below 2^31 (buffer offsets are 32-bit).
-bool bytes_fit(int N, int K, int grid)
+bool bytes_fit(int N, int K, int grid, bool pair = false)
 {
-    const long long gmax = (num_groups(N) + grid - 1) / grid;
+    const int u = pair ? 2 : 1;
+    const long long gmax = u * ((num_groups(N) / u + grid - 1) / grid);
     return gmax * (long long)num_chunks(K) * kChunkCodeBytes < (1LL << 31);
 }
 
 // Workgroups and LDS layout of the dot-product kernel; false if X does not fit in LDS.
-bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L)
+bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L, bool pair = false)
 {
-    const int G = group_grid(N);
+    const int G = group_grid(N, pair);
+    const int u = pair ? 2 : 1;   // groups are dealt in units of u
     L->nwin = (K + kStreamWindow - 1) / kStreamWindow;
     L->row_bytes = L->nwin * (kStreamWindow / 32) * kStreamSlot;
     const long long x_bytes = (long long)M * L->row_bytes;
-    const int NG = num_groups(N);
-    L->ngroups = (NG + G - 1) / G;
+    const int NU = num_groups(N) / u;
+    L->gunit = u;
+    L->ngroups = u * ((NU + G - 1) / G);
     // A group of nwin consecutive units touches every wavefront whose run starts inside it.
     L->slots = 1;
-    const int sizes[2] = {NG / G, L->ngroups};
+    const int sizes[2] = {u * (NU / G), L->ngroups};
     for (int i = 0; i < 2; i++) {
         const long long units = (long long)sizes[i] * L->nwin;
         if (units == 0)
@@ -208,12 +219,13 @@ bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L)
         }
     }
     const long long part_bytes = (long long)L->ngroups * L->slots * MR * 4 * 4;
-    if (x_bytes + part_bytes > kMaxLds || !bytes_fit(N, K, G))
+    // (1 KB of the LDS is left for the kernel's static arrays: the RMSNorm row sums.)
+    if (x_bytes + part_bytes > kMaxLds - 1024 || !bytes_fit(N, K, G, pair))
         return false;
     L->x_bytes = (int)x_bytes;
     L->part_bytes = (int)part_bytes;
-    L->gq = NG / G;
-    L->gr = NG % G;
+    L->gq = NU / G;
+    L->gr = NU % G;
     L->rnwin = 1.0f / (float)L->nwin;
     *grid = G;
     return true;
@@ -224,12 +236,13 @@ struct MfmaPlan {
     int grid, tc_index, lds;
 };
 
-bool mfma_plan(int N, int K, int waves, MfmaPlan *P)
+bool mfma_plan(int N, int K, int waves, MfmaPlan *P, bool pair = false)
 {
-    const int G = group_grid(N);
-    if (!bytes_fit(N, K, G))
+    const int G = group_grid(N, pair);
+    if (!bytes_fit(N, K, G, pair))
         return false;
-    const int gmax = (num_groups(N) + G - 1) / G;
+    const int u = pair ? 2 : 1;
+    const int gmax = u * ((num_groups(N) / u + G - 1) / G);
     const int tiles = (gmax + 3) / 4;
     int ti = 5;
     for (int i = 0; i < 6; i++)
@@ -240,7 +253,7 @@ bool mfma_plan(int N, int K, int waves, MfmaPlan *P)
     P->grid = G;
     P->tc_index = ti;
     P->lds = mfma_stream_lds_bytes(kMfmaTiles[ti], waves);
-    return P->lds <= kMaxLds;
+    return P->lds + 256 <= kMaxLds;   // (plus the kernel's static RMSNorm array)
 }
 
 // Wavefronts of the matrix-core kernel when the caller leaves it open: wide chunks keep more
@@ -503,7 +516,7 @@ hipError_t launch_impl(int path, int split, const GemmArgs &a0, int32_t *index, 
     if (path == kPathDot) {
         StreamLayout L;
         int grid = 0;
-        if (!stream_plan(a.M, a.N, a.K, a.M, split, &grid, &L))
+        if (!stream_plan(a.M, a.N, a.K, a.M, split, &grid, &L, a.H != nullptr))
             return hipErrorInvalidValue;
         const int fast = (a.K % kStreamWindow == 0) ? 1 : 0;
         const StreamFn fn = kStream[fast][a.M - 1][wave_index(split)];
@@ -606,7 +619,7 @@ hipError_t launch_impl(int path, int split, const GemmArgs &a0, int32_t *index, 
     if (path != kPathMfma)
         return hipErrorInvalidValue;
     MfmaPlan P;
-    if (!mfma_plan(a.N, a.K, split, &P))
+    if (!mfma_plan(a.N, a.K, split, &P, a.H != nullptr))
         return hipErrorInvalidValue;
     const int fast = (a.K % kMfmaWindow == 0) ? 1 : 0;
     const KernelFn fn = kMfma[fast][P.tc_index][split == 4 ? 0 : 1];
@@ -645,5 +658,30 @@ hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *i
 }
 
 int device_compute_units() { return compute_units(); }
+
+hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream)
+{
+    // The dot-product kernel for the smallest M when X fits in LDS, else the 16-row matrix-core
+    // kernel (any M, one 16-row block per workgroup row).
+    const bool pair = a.H != nullptr;
+    int path = kPathMfma, split = 0;
+    StreamLayout L;
+    int grid;
+    if (a.M <= 4 && stream_plan(a.M, a.N, a.K, a.M, 16, &grid, &L, pair)) {
+        path = kPathDot;
+        split = 16;
+    } else {
+        MfmaPlan P;
+        split = 8;
+        if (!mfma_plan(a.N, a.K, 8, &P, pair) || kMfmaTiles[P.tc_index] >= 6)
+            split = 4;
+        if (!mfma_plan(a.N, a.K, split, &P, pair))
+            return hipErrorInvalidValue;
+    }
+    GemmArgs b = a;
+    b.keys = nullptr;
+    b.key_slots = 0;
+    return launch_impl(path, split, b, nullptr, nullptr, stream);
+}
 
 }  // namespace nvfp4

@@ -48,8 +48,9 @@ struct StreamLayout {
     int slots;       // most wavefronts one group is split over
     int x_bytes;     // M * row_bytes
     int part_bytes;  // ngroups * slots * MR * 4 floats
-    int gq, gr;      // NG = gq G + gr: workgroup b owns gq + (b < gr) groups
+    int gq, gr;      // NG = gunit (gq G + gr): workgroup b owns gunit (gq + (b < gr)) groups
     float rnwin;     // 1.0f / nwin
+    int gunit;       // groups dealt together: 2 keeps the gate/up pairs of a workgroup whole
 };
 
 // First wavefront of the W whose run [u0(w), u0(w+1)), u0(w) = floor(w units / W), holds unit u.
@@ -85,8 +86,8 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     const int CH = num_chunks(K);
     const int NG = num_groups(N);
     const int b = blockIdx.x;
-    const int g0 = b * L.gq + min(b, L.gr);
-    const int ngroups = L.gq + (b < L.gr ? 1 : 0);
+    const int g0 = L.gunit * (b * L.gq + min(b, L.gr));
+    const int ngroups = L.gunit * (L.gq + (b < L.gr ? 1 : 0));
     const int c0 = kGroupCols * g0;
     const int ncols = min(N - c0, kGroupCols * ngroups);
     const int nwin = L.nwin;
@@ -180,6 +181,81 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     }
     __syncthreads();
 
+    if (a.gamma != nullptr) {
+        // RMSNorm of the staged rows: per row r = 1 / sqrt(mean x^2 + eps); every x becomes
+        // bf16((x * r) * gamma[k]) in place. The sum of squares: each thread adds its 8-value
+        // pieces in order (fma), then a fixed butterfly over the wavefront, then the wavefronts in
+        // order; its relative error stays below (K / 64 + 32) 2^-24.
+        __shared__ float nss[W][MR];
+        __shared__ float nr[MR];
+        float ss[MR];
+#pragma unroll
+        for (int m = 0; m < MR; m++)
+            ss[m] = 0.0f;
+        auto piece = [&](int idx, int *m, int *e) {
+            *m = MR == 1 ? 0 : (int)div_small((uint32_t)idx >> 6, (uint32_t)nwin, L.rnwin);
+            *e = idx - *m * row_pieces;
+        };
+        for (int idx = threadIdx.x; idx < xpieces; idx += kWave * W) {
+            int m, e;
+            piece(idx, &m, &e);
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                lds + m * L.row_bytes + (e >> 2) * kStreamSlot + 16 * (e & 3));
+            float t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float lo = __uint_as_float(v[i] << 16);
+                const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
+                t = __builtin_fmaf(lo, lo, t);
+                t = __builtin_fmaf(hi, hi, t);
+            }
+#pragma unroll
+            for (int mm = 0; mm < MR; mm++)
+                if (mm == m)
+                    ss[mm] += t;
+        }
+#pragma unroll
+        for (int m = 0; m < MR; m++) {
+            float t = ss[m];
+#pragma unroll
+            for (int d = kWave / 2; d >= 1; d >>= 1)
+                t += __shfl_xor(t, d);
+            if (lane == 0)
+                nss[wave][m] = t;
+        }
+        __syncthreads();
+        if (threadIdx.x < MR) {
+            float t = 0.0f;
+            for (int w = 0; w < W; w++)
+                t += nss[w][threadIdx.x];
+            nr[threadIdx.x] = 1.0f / __builtin_sqrtf(t / (float)K + a.eps);
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < xpieces; idx += kWave * W) {
+            int m, e;
+            piece(idx, &m, &e);
+            if (8 * e >= K)
+                continue;   // padding stays zero
+            u32x4_t *p = reinterpret_cast<u32x4_t *>(lds + m * L.row_bytes +
+                                                     (e >> 2) * kStreamSlot + 16 * (e & 3));
+            const u32x4_t v = *p;
+            const u32x4_t gm = *reinterpret_cast<const u32x4_t *>(a.gamma + 8 * e);
+            const float r = nr[m];
+            u32x4_t o;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float x0 = __uint_as_float(v[i] << 16) * r;
+                const float x1 = __uint_as_float(v[i] & 0xFFFF0000u) * r;
+                bf16x2_t y;
+                y[0] = (__bf16)(x0 * __uint_as_float(gm[i] << 16));
+                y[1] = (__bf16)(x1 * __uint_as_float(gm[i] & 0xFFFF0000u));
+                o[i] = __builtin_bit_cast(uint32_t, y);
+            }
+            *p = o;
+        }
+        __syncthreads();
+    }
+
     float acc[MR];
 #pragma unroll
     for (int m = 0; m < MR; m++)
@@ -249,6 +325,25 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     __syncthreads();
 
     const float g = *a.gscale;
+    if (a.H != nullptr) {
+        // SiLU(gate) * up: the workgroup owns whole pairs of groups (gate group 2p, up group
+        // 2p + 1; c0 is a multiple of 8), so column c's partner is c + 4.
+        const int I = N >> 1;
+        for (int m = 0; m < a.M && m < MR; m++)
+            for (int pidx = threadIdx.x; pidx < (ncols >> 1); pidx += kWave * W) {
+                const int c = 8 * (pidx >> 2) + (pidx & 3);
+                float sg = 0.0f, su = 0.0f;
+                for (int sl = 0; sl < L.slots; sl++) {
+                    sg += part[(((c >> 2) * L.slots + sl) * MR + m) * 4 + (c & 3)];
+                    su += part[((((c >> 2) + 1) * L.slots + sl) * MR + m) * 4 + (c & 3)];
+                }
+                const float gate = sg * g, up = su * g;
+                const float h = gate / (1.0f + __expf(-gate)) * up;
+                a.H[(size_t)m * I + (c0 >> 1) + 4 * (pidx >> 2) + (pidx & 3)] =
+                    __builtin_bit_cast(uint16_t, (__bf16)h);
+            }
+        return;
+    }
 #pragma unroll
     for (int m = 0; m < MR; m++) {
         if (m >= a.M)

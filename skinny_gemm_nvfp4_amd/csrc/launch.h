@@ -18,6 +18,13 @@ struct GemmArgs {
     // owns into one argmax key per row (argmax.h) and stores it at keys[m * key_slots + slot].
     unsigned long long *keys = nullptr;
     int key_slots = 0;
+    // Layer neighbours (nvfp4_gemm_fused). gamma set: X is replaced by its RMSNorm, rounded to
+    // bf16, xhat = bf16((x * r) * gamma[k]) with r = 1 / sqrt(mean_k x^2 + eps) per row. H set:
+    // instead of Y, H[m][j] = bf16(SiLU(gate) * up) from the column pairs of the interleaved
+    // gate/up weight (columns 8q + c and 8q + 4 + c, c < 4, give j = 4q + c); N % 8 == 0.
+    const uint16_t *gamma = nullptr;   // bf16 [K]
+    float eps = 0.0f;
+    uint16_t *H = nullptr;             // bf16 [M][N / 2]
 };
 
 // Packed layout: 4-column groups, 32-k chunks. One chunk of one group is 4 x 16 code bytes
@@ -96,6 +103,9 @@ constexpr int kArgmaxSlotsPerCu = 16;
 // turned into index and value.
 hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *index,
                               float *value, hipStream_t stream);
+
+// Launch of nvfp4_gemm_fused: RMSNorm prologue (a.gamma) and/or SiLU(gate) * up epilogue (a.H).
+hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_compute_units();

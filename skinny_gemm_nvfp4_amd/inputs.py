@@ -199,3 +199,12 @@ def moe_routing(gen: torch.Generator, tokens: int, experts: int, topk: int):
     offsets = torch.zeros(experts + 1, dtype=torch.int32)
     offsets[1:] = torch.cumsum(counts, 0).to(torch.int32)
     return token_of_row, offsets
+
+
+# ---- layer neighbours (RMSNorm before the GEMM) ----
+RMSNORM_EPS = 1e-6
+
+
+def norm_weight(gen: torch.Generator, K: int) -> torch.Tensor:
+    """bf16 RMSNorm gain gamma[K] = 1 + 0.1 N(0, 1) (a trained norm's gains sit around 1)."""
+    return (1.0 + 0.1 * torch.randn(K, generator=gen, dtype=torch.float32)).to(torch.bfloat16)

@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert nv.abi_version() == 4
+    assert nv.abi_version() == 5
     for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH):
         assert nv.status_string(st)
     assert nv.status_string(99) == "unknown status"
@@ -240,3 +240,36 @@ def test_grouped_rejects_null_misaligned_and_rows_per_item(lib):
 def test_grouped_with_no_rows_does_nothing(lib):
     # T = 0 is valid and launches nothing (so it needs no GPU)
     assert _grouped(0, 8, 16, 256) == nv.SUCCESS
+
+
+# ---- nvfp4_gemm_fused: fuse flags, sizes, eps, pointers, alignment ----
+
+def _fused(fuse, M, N, K, ptrs=None, eps=1e-6):
+    p = ptrs or [A16, A16B, A16C, A16D, A16E, A8F]     # X, gamma, Wq, Wscale, gscale, out
+    return nv.nvfp4_gemm_fused(fuse, M, N, K, p[0], p[1], eps, p[2], p[3], p[4], p[5], None)
+
+
+def test_fused_rejects_bad_arguments(lib):
+    for fuse in (0, 4, -1):
+        assert _fused(fuse, 1, 16, 256) == nv.ERROR_INVALID_VALUE
+    assert _fused(nv.FUSE_SILU_MUL, 1, 20, 256) == nv.ERROR_INVALID_VALUE      # N % 8
+    assert _fused(nv.FUSE_RMSNORM, 1, 16, 24) == nv.ERROR_INVALID_VALUE        # K % 16
+    assert _fused(nv.FUSE_RMSNORM, 0, 16, 256) == nv.ERROR_INVALID_VALUE
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert _fused(nv.FUSE_RMSNORM, 1, 16, 256, eps=eps) == nv.ERROR_INVALID_VALUE
+    good = [A16, A16B, A16C, A16D, A16E, A8F]
+    for i in range(6):
+        bad = list(good)
+        bad[i] = 0
+        st = _fused(nv.FUSE_RMSNORM, 1, 16, 256, bad)
+        assert st == nv.ERROR_INVALID_VALUE, i
+    # gamma is only needed for RMSNorm; then it needs 16 bytes
+    bad = list(good)
+    bad[1] += 8
+    assert _fused(nv.FUSE_RMSNORM, 1, 16, 256, bad) == nv.ERROR_MISALIGNED
+    # out: fp32 Y needs 4 bytes, bf16 H 2
+    bad = list(good)
+    bad[5] += 2
+    assert _fused(nv.FUSE_RMSNORM, 1, 16, 256, bad) == nv.ERROR_MISALIGNED
+    bad[5] = good[5] + 1
+    assert _fused(nv.FUSE_SILU_MUL, 1, 16, 256, bad) == nv.ERROR_MISALIGNED

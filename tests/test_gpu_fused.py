@@ -1,0 +1,142 @@
+"""The GEMM with its decode-layer neighbours (nvfp4_gemm_fused through the C ABI) against the
+oracle ("SparkInfer" README, section "Layout & scoring": RMSNorm and fused FFN kernels).
+
+Bars (derived in the design doc):
+  * RMSNorm: the oracle rounds the exact normalised activation to bf16 once; the kernel computes
+    it in fp32 within a relative (K/64 + 40) 2^-24, so where the exact value lies within twice
+    that of a bf16 rounding boundary either neighbour is correct (flagged by the oracle). The
+    GEMM bar becomes |Y - Y_ref| <= 2e-3 sum|xhat w| + 1e-6 + sum_flagged ulp |w|.
+  * SiLU(gate) * up: gate and up carry their GEMM tolerances t_g, t_u; SiLU has slope at most
+    1.1, so |H - h_ref| <= pre + 2^-8 (|h_ref| + pre) + 2e-5 |h_ref| + 1e-30 with
+    pre = 1.1 t_g (|up| + t_u) + (|silu(gate)| + 1.1 t_g) t_u (the 2^-8 covers the bf16 rounding
+    of H, 2e-5 the fp32 exponential).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import skinny_gemm_nvfp4_amd as nv
+from skinny_gemm_nvfp4_amd import inputs
+from parity import FINITE_SCALES, say, to_device_packed
+
+pytestmark = pytest.mark.gpu
+
+EPS = inputs.RMSNORM_EPS
+
+
+def _window(K):
+    return 2.0 * (K / 64 + 40) * 2.0 ** -24
+
+
+def _bits_of(t):
+    return inputs.bf16_bits(t)
+
+
+def _ref_gemm(X_bits, Wq, Ws, g, gamma_bits=None):
+    """Oracle Y and its bound for the (optionally RMSNorm-ed) activations."""
+    if gamma_bits is None:
+        Y, A = oracle.gemm(X_bits, Wq, Ws, g)
+        return Y, oracle.tolerance(A)
+    K = X_bits.shape[1]
+    xhat, flag, ulp = oracle.rmsnorm_bf16(X_bits, gamma_bits, EPS, _window(K))
+    Y, A = oracle.gemm(xhat, Wq, Ws, g)
+    allow_bits, _, _, _ = oracle.bf16_round(np.where(flag, ulp, 0.0))
+    _, A_allow = oracle.gemm(allow_bits, Wq, Ws, g)
+    return Y, oracle.tolerance(A) + A_allow
+
+
+def _check_y(Y, Yref, tol, label):
+    err = np.abs(Y.astype(np.float64) - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, f"{label}: {len(bad)} outputs outside the bound, first {bad[:3]}"
+
+
+def _check_h(H_bits, Yref, tol, label):
+    h = (H_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    M, N = Yref.shape
+    cols = np.arange(N).reshape(N // 8, 2, 4)
+    gi, ui = cols[:, 0, :].reshape(-1), cols[:, 1, :].reshape(-1)
+    gate, up, tg, tu = Yref[:, gi], Yref[:, ui], tol[:, gi], tol[:, ui]
+    href = oracle.silu_mul(gate, up)
+    sg = np.abs(oracle.silu_mul(gate, np.ones_like(gate)))
+    pre = 1.1 * tg * (np.abs(up) + tu) + (sg + 1.1 * tg) * tu
+    bound = pre + 2.0 ** -8 * (np.abs(href) + pre) + 2e-5 * np.abs(href) + 1e-30
+    bad = np.argwhere(~(np.abs(h - href) <= bound))
+    assert bad.size == 0, f"{label}: {len(bad)} outputs of H outside the bound, first {bad[:3]}"
+
+
+CASES = [(1, 1000, 1024), (3, 264, 5120), (4, 72, 272), (5, 200, 1024), (16, 1000, 512),
+         (20, 136, 5120), (40, 64, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", CASES)
+@pytest.mark.parametrize("fuse", [1, 2, 3])
+def test_fused_against_oracle(device, M, N, K, fuse):
+    gen = inputs.generator(3000 + 7 * M + N + K + fuse)
+    Wq, Ws = inputs.random_packed(gen, N, K, FINITE_SCALES)
+    g = np.float32(0.011)
+    X = inputs.activations(gen, M, K, outliers=4)
+    gamma = inputs.norm_weight(gen, K)
+    norm = bool(fuse & nv.FUSE_RMSNORM)
+    label = f"fused={fuse} M={M} N={N} K={K}"
+    say(label)
+    Yref, tol = _ref_gemm(_bits_of(X), Wq.numpy(), Ws.numpy(), g,
+                          _bits_of(gamma) if norm else None)
+    p = to_device_packed(Wq, Ws, g, device)
+    out = nv.gemm_fused(X.to(device), p.Wq, p.Ws, p.g, N,
+                        gamma=gamma.to(device) if norm else None, eps=EPS,
+                        silu_mul=bool(fuse & nv.FUSE_SILU_MUL))
+    torch.cuda.synchronize()
+    if fuse & nv.FUSE_SILU_MUL:
+        _check_h(out.cpu().view(torch.int16).numpy().view(np.uint16), Yref, tol, label)
+    else:
+        _check_y(out.cpu().numpy(), Yref, tol, label)
+
+
+def test_rmsnorm_constant_rows(device):
+    """Rows of one constant c with eps = 0 normalise to gamma * sign(c) exactly, so the fused
+    GEMM equals the plain GEMM of gamma (bit for bit in exact-sum cases)."""
+    M, N, K = 4, 96, 1024
+    gen = inputs.generator(4040)
+    Wq, Ws = inputs.random_packed(gen, N, K, scale_bytes=[0x30, 0x38, 0x40])
+    gamma = inputs.integer_activations(gen, 1, K, -4, 4)[0]
+    X = torch.tensor([[3.0], [-0.5], [1.0], [-96.0]]).repeat(1, K).to(torch.bfloat16)
+    sign = torch.tensor([1.0, -1.0, 1.0, -1.0])[:, None]
+    Xg = (sign * gamma.float()[None, :]).to(torch.bfloat16)
+    Yref, _ = oracle.gemm(_bits_of(Xg), Wq.numpy(), Ws.numpy(), 1.0)
+    p = to_device_packed(Wq, Ws, 1.0, device)
+    for M_ in (4, 16):   # the dot-product kernel, then the 16-row kernel (rows padded by zeros)
+        Xp = torch.cat([X, torch.zeros(M_ - 4, K, dtype=torch.bfloat16)]) if M_ > 4 else X
+        say(f"rmsnorm constant rows M={M_}")
+        Y = nv.gemm_fused(Xp.to(device), p.Wq, p.Ws, p.g, N, gamma=gamma.to(device), eps=0.0)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy()[:4].astype(np.float64), Yref)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_layer_shapes(device, M):
+    """The layer's q/k/v projection after the input RMSNorm, and its gate/up projection (weight
+    interleaved for the fused SiLU * up) after the post-attention RMSNorm, from the workload
+    recipe (weights packed by the GPU, and by the oracle from the same fp32 tensor)."""
+    gen = inputs.generator(5050 + M)
+    K = inputs.HIDDEN
+    X = inputs.activations(gen, M, K, outliers=4)
+    gamma = inputs.norm_weight(gen, K)
+    for name, fuse in (("qkv", 1), ("gate_up", 3)):
+        N = inputs.LAYER_SHAPES[name][1]
+        W = inputs.weights(gen, K, N)
+        if fuse & nv.FUSE_SILU_MUL:
+            W = nv.interleave_gate_up(W)
+        label = f"layer {name} M={M} fuse={fuse}"
+        say(label)
+        p = nv.pack(W.to(device))
+        Wq_o, Ws_o, g_o = oracle.quantize(W.numpy())
+        out = nv.gemm_fused(X.to(device), p.Wq, p.Ws, p.g, N, gamma=gamma.to(device), eps=EPS,
+                            silu_mul=bool(fuse & nv.FUSE_SILU_MUL))
+        torch.cuda.synchronize()
+        Yref, tol = _ref_gemm(_bits_of(X), Wq_o, Ws_o, g_o, _bits_of(gamma))
+        if fuse & nv.FUSE_SILU_MUL:
+            _check_h(out.cpu().view(torch.int16).numpy().view(np.uint16), Yref, tol, label)
+        else:
+            _check_y(out.cpu().numpy(), Yref, tol, label)

@@ -1,6 +1,9 @@
 """The test-side conversion between the oracle's plain byte layout and the library's packed
 layout, checked element by element against the layout's definition in include/nvfp4.h."""
 import numpy as np
+
+from skinny_gemm_nvfp4_amd import binding
+import torch
 import pytest
 
 from parity import from_library_layout, to_library_layout
@@ -41,3 +44,14 @@ def test_nonzero_padding_is_reported():
     q[1, 0, 3, 0] = 0
     s[0, 0, 0, 1] = 0x38       # block 1 of a K = 16 matrix
     assert not from_library_layout(q, s, 5, 16)[2]
+
+
+def test_interleave_is_a_column_permutation():
+    """interleave_gate_up only moves columns: gate column j lands at 8 (j // 4) + j % 4, up
+    column j at that + 4."""
+    K, I = 3, 12
+    W = torch.arange(K * 2 * I, dtype=torch.float32).reshape(K, 2 * I)
+    Wi = binding.interleave_gate_up(W)
+    for j in range(I):
+        assert torch.equal(Wi[:, 8 * (j // 4) + j % 4], W[:, j])
+        assert torch.equal(Wi[:, 8 * (j // 4) + 4 + j % 4], W[:, I + j])
