@@ -22,6 +22,8 @@ Protocol
     of Y is the same bits for any M), timed the same way.
   * "lm_head_argmax": the lm_head (N = 151936) at M = 1, 16, 128, writing the logits
     (nvfp4_gemm) and folding them into the greedy token per row (nvfp4_gemm_argmax).
+  * "fused_neighbours": q/k/v with the RMSNorm folded in and gate/up with RMSNorm and
+    SiLU(gate)*up folded in, at M = 1 and 16, beside the plain GEMMs.
   * "moe_grouped": the grouped (mixture-of-experts) GEMM, 128 experts with 8 routed per token,
     at decode (1 token) and verification (16 tokens), per call over rotating routings.
   * "full_pass": 64 layers of those shapes plus an NVFP4 lm_head (N = 151936), 12.33 GB of
@@ -398,6 +400,63 @@ def moe_grouped(dev, launches, steps: int):
     return out
 
 
+def fused_neighbours(dev, launches, steps: int):
+    """The layer's q/k/v projection with the input RMSNorm folded in, and its gate/up projection
+    with the post-attention RMSNorm and SiLU(gate) * up folded in (weight columns interleaved),
+    at M = 1 and M = 16 (weights seed 13 drawn on the device, x and gamma seed 14), next to the
+    plain GEMM of the same shape. Bytes of a fused call: weights, X, gamma and its output (fp32 Y
+    for q/k/v, bf16 H for gate/up)."""
+    import torch
+    import skinny_gemm_nvfp4_amd as nv
+    from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+    K = inputs.HIDDEN
+    wgen = torch.Generator(device=dev).manual_seed(13)
+    xgen = inputs.generator(14)
+    gamma = inputs.norm_weight(xgen, K).to(dev)
+    out = {"eps": inputs.RMSNORM_EPS,
+           "timing": "HIP events around graph replays of 32 calls rotating over cold copies"}
+    for name, silu in (("qkv", False), ("gate_up", True)):
+        N = inputs.LAYER_SHAPES[name][1]
+        W = inputs.weights_on_device(wgen, K, N, dev)
+        if silu:
+            W = nv.interleave_gate_up(W)
+        p0 = nv.pack(W)
+        del W
+        copies = max(2, -(-COLD_BYTES // rl.weight_bytes(K, N)))
+        packs = [p0] + [Layer._clone(p0) for _ in range(copies - 1)]
+        for M in (1, 16):
+            X = inputs.activations(xgen, M, K, outliers=4).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            O = torch.empty((M, N // 2) if silu else (M, N),
+                            dtype=torch.bfloat16 if silu else torch.float32, device=dev)
+
+            def plain(c, X=X, Y=Y, packs=packs):
+                nv.gemm(X, *packs[c], out=Y)
+
+            def fused(c, X=X, O=O, packs=packs, N=N, silu=silu):
+                p = packs[c]
+                nv.gemm_fused(X, p.Wq, p.Ws, p.g, N, gamma=gamma, eps=inputs.RMSNORM_EPS,
+                              silu_mul=silu, out=O)
+
+            lab = f"fused.{name} M={M} N={N} K={K}"
+            pus = graph_time_us(plain, copies, max(64, steps), f"{lab} plain", launches)
+            fus = graph_time_us(fused, copies, max(64, steps), lab, launches)
+            fbytes = rl.weight_bytes(K, N) + 2 * M * K + 2 * K + (2 * M * N // 2 if silu
+                                                                    else 4 * M * N)
+            gbs = fbytes / (fus * 1e-6) / 1e9
+            out[f"{name}_m{M}"] = {
+                "fused": "rmsnorm + gemm + silu*up" if silu else "rmsnorm + gemm",
+                "M": M, "N": N, "K": K, "fused_us": round(fus, 3), "plain_gemm_us": round(pus, 3),
+                "fused_bytes": fbytes, "fused_GB_s": round(gbs, 1),
+                "fused_pct_hbm_peak": round(100 * gbs / rl.HBM_PEAK_GBS, 2),
+                # the round trips a separate RMSNorm (bf16 xhat) and SiLU * up (fp32 gate/up)
+                # kernel would add
+                "bytes_not_moved": (8 * M * N + 4 * M * K) if silu else 4 * M * K}
+        del packs
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +469,8 @@ def main() -> int:
     ap.add_argument("--no-full-pass", action="store_true",
                     help="skip the 64-layer + lm_head weight pass at M=1 and M=16")
     ap.add_argument("--full-pass-reps", type=int, default=20)
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the RMSNorm / SiLU(gate)*up fused-neighbour timing")
     ap.add_argument("--no-moe", action="store_true",
                     help="skip the grouped (mixture-of-experts) GEMM timing")
     ap.add_argument("--no-lm-head", action="store_true",
@@ -548,6 +609,11 @@ def main() -> int:
         log("timing the lm_head: logits vs greedy token per row (nvfp4_gemm_argmax)")
         lmh = lm_head_argmax(dev, launches, args.steps)
 
+    fused = None
+    if not args.no_fused:
+        log("timing the fused layer neighbours (RMSNorm prologue, SiLU(gate)*up epilogue)")
+        fused = fused_neighbours(dev, launches, args.steps)
+
     moe = None
     if not args.no_moe:
         log("timing the grouped (mixture-of-experts) GEMM: decode and verify routings")
@@ -579,6 +645,7 @@ def main() -> int:
         "invariant": invariant or None,
         "lm_head_argmax": lmh,
         "moe_grouped": moe,
+        "fused_neighbours": fused,
         "full_pass": fp,
         "source_hash": ps.source_hash(),
     }

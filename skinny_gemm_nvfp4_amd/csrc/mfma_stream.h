@@ -186,26 +186,34 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const int nmine = (nwin - wave + W - 1) / W;
 
     // RMSNorm: r of each of the block's rows (wavefront w takes rows w, w + W, ...: lane sums of
-    // x^2 over k = 8 lane + 512 i in order, then a fixed butterfly; relative error below
-    // (K / 64 + 32) 2^-24), then each lane keeps r of its 4 staging rows.
+    // x^2 over k = 8 lane + 512 i in order, loads issued eight at a time, then a fixed butterfly;
+    // relative error below (K / 64 + 32) 2^-24), then each lane keeps r of its 4 staging rows.
+    // Done once, after the first weight windows are in flight.
     const bool norm = a.gamma != nullptr;
     const rsrc_t rg = make_rsrc(a.gamma, norm ? (uint32_t)K * 2u : 0u);
     float rr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (norm) {
-        __shared__ float nr[16];
+    __shared__ float nr[16];
+    auto row_norms = [&]() {
         for (int m = wave; m < 16; m += W) {
             float t = 0.0f;
-            for (int k = 8 * lane; k < K; k += 8 * kWave) {
-                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                    rx, off_if(m < mrows, ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u), 0,
-                    kAuxNormal);
+            for (int k0 = 8 * lane; k0 < K; k0 += 8 * 8 * kWave) {
+                u32x4_t v[8];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const float lo = __uint_as_float(v[i] << 16);
-                    const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
-                    t = __builtin_fmaf(lo, lo, t);
-                    t = __builtin_fmaf(hi, hi, t);
+                for (int b = 0; b < 8; b++) {
+                    const int k = k0 + 8 * kWave * b;
+                    v[b] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rx, off_if(m < mrows && k < K, ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u),
+                        0, kAuxNormal);
                 }
+#pragma unroll
+                for (int b = 0; b < 8; b++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float lo = __uint_as_float(v[b][i] << 16);
+                        const float hi = __uint_as_float(v[b][i] & 0xFFFF0000u);
+                        t = __builtin_fmaf(lo, lo, t);
+                        t = __builtin_fmaf(hi, hi, t);
+                    }
             }
 #pragma unroll
             for (int d = kWave / 2; d >= 1; d >>= 1)
@@ -217,7 +225,8 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
 #pragma unroll
         for (int p = 0; p < 4; p++)
             rr[p] = nr[4 * p + (lane >> 4)];
-    }
+    };
+
     // Argmax mode: every output this thread adds up below is in row 4 q + wave % 4 of the block
     // (W is a multiple of 4), so one key per thread.
     argkey_t best = 0;
@@ -240,6 +249,8 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
 #pragma unroll
         for (int i = 0; i < D - 1; i++)
             load(i, ring[i]);
+        if (norm && tc0 == 0)
+            row_norms();   // once, with the first windows of weights already requested
         if (norm)
             ring[0].stage_norm(xbuf[0], lane, rr);
         else
