@@ -238,9 +238,11 @@ uint64_t nvfp4_argmax_workspace_bytes(int M);
  *   N, K     the shape of every expert's weight (K % 16 == 0, as for nvfp4_gemm)
  *   X        in:  bf16 bits [T][K], device, rows sorted by expert
  *   offsets  in:  int32 [E + 1], device: expert e owns rows offsets[e] .. offsets[e+1] - 1;
- *                 meant to be non-decreasing from 0 to T. Entries are clamped to [0, T] and an
- *                 expert whose end precedes its start has no rows: bad offsets give unspecified
- *                 values in Y (rows no expert owns are not written), never an access out of range
+ *                 meant to be non-decreasing from 0 to T. Entries are clamped to [0, T] and made
+ *                 non-decreasing by a running maximum (expert e owns rows b_e .. b_{e+1} - 1,
+ *                 b_e = max over e' <= e of the clamped offsets[e']): bad offsets move rows
+ *                 between experts (rows before b_0 or from b_E on are not written), never cause
+ *                 an access out of range
  *   Wq       in:  E packed code arrays back to back, expert e at Wq + e * nvfp4_codes_bytes(N, K)
  *                 (each as nvfp4_pack writes it)
  *   Wscale   in:  E packed scale arrays, expert e at Wscale + e * nvfp4_scales_bytes(N, K)

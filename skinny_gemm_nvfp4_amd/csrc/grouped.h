@@ -17,13 +17,17 @@
 //     every wavefront streams the same number of weight bytes whatever the routing. A wavefront
 //     walks its run window by window (512 k: 1 KB of codes, one 16-byte load per lane, as the
 //     dot-product kernel), with D windows in flight across item boundaries.
-//   * Lane l takes column l % 4 of the group and chunk l / 4 of the window; its x values come
-//     straight from X (L2-resident: a few rows), 64 bytes per row and window.
+//   * Lane l takes column l % 4 of the group and chunk l / 4 of the window. LDSX: the workgroup
+//     first copies the X rows of every chunk its items touch into LDS (a few rows: the launcher
+//     sizes the space from T, E and the grid), 80 bytes per 32 k so that the lanes of a column
+//     quad read one broadcast; otherwise each lane fetches its 64 bytes per row and window from
+//     L2.
 //   * At the end of an item the 16 lanes of each column are summed in a fixed order, times the
 //     expert's g, and stored. No item is split between wavefronts, so there are no partial sums
 //     to exchange, and a row's result does not depend on MR, the grid or the other rows.
-//   * Offsets are clamped to [0, T]; an expert whose end is before its start has no rows. Bad
-//     offsets give unspecified rows, never an access outside X, Y or the weights.
+//   * Offsets are clamped to [0, T] and made non-decreasing (a running maximum), so the experts'
+//     rows never overlap and add up to at most T: bad offsets move rows between experts, never
+//     an access outside X, Y or the weights.
 #pragma once
 
 #include "device.h"
@@ -32,17 +36,20 @@
 namespace nvfp4 {
 
 constexpr int kGroupedWindow = 512;
+constexpr int kGroupedSlot = 80;   // LDS bytes per 32-k chunk of a staged X row (64 used)
 
-template <int MR>
+template <int MR, bool LDSX>
 struct GroupedUnit {
     uint32_t code[4];
     uint32_t scale;
-    u32x4_t x[MR][4];         // the lane's 32 k of each row: k = 8 p .. 8 p + 7 in x[m][p]
+    u32x4_t x[LDSX ? 1 : MR][4];   // (L2 path) the lane's 32 k of each row: k = 8 p .. 8 p + 7
 };
 
-template <int MR, int W, int D, bool FAST>
-__global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
+// LDSX: dynamic LDS holds xrows staged rows of row_bytes each, then xrows ints of row numbers.
+template <int MR, int W, int D, bool FAST, bool LDSX>
+__global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a, int xrows)
 {
+    extern __shared__ __align__(16) uint8_t xlds[];
     __shared__ int cum[kGroupedMaxExperts + 1];   // row chunks of experts < e
     __shared__ int rstart[kGroupedMaxExperts];    // first row of expert e (clamped)
     __shared__ int rcount[kGroupedMaxExperts];    // rows of expert e (>= 0)
@@ -60,14 +67,30 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
     const size_t sb = (size_t)NG * gs;                      // scale bytes per expert
 
     // Prefix sums of the row chunks, by wavefront 0: lane l takes a contiguous run of experts.
+    // Boundaries: offsets clamped to [0, T], then a running maximum (prefix max over the lanes'
+    // runs), so expert e owns rows [b_e, b_{e+1}) with b non-decreasing.
     if (wave == 0) {
         const int per = (E + kWave - 1) / kWave;
         const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
         auto clampT = [&](int v) { return min(max(v, 0), T); };
+        int lmax = 0;
+        for (int e = e0; e < e1; e++)
+            lmax = max(lmax, clampT(a.offsets[e]));
+        int pmax = lmax;   // inclusive prefix max over lanes
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int t = __shfl_up(pmax, d);
+            if (lane >= d)
+                pmax = max(pmax, t);
+        }
+        int bnd = __shfl_up(pmax, 1);   // max over the earlier lanes' runs
+        if (lane == 0)
+            bnd = 0;
         int local = 0;
         for (int e = e0; e < e1; e++) {
-            const int r0 = clampT(a.offsets[e]);
-            const int n = max(0, clampT(a.offsets[e + 1]) - r0);
+            const int r0 = max(bnd, clampT(a.offsets[e]));
+            bnd = max(r0, clampT(a.offsets[e + 1]));
+            const int n = bnd - r0;
             rstart[e] = r0;
             rcount[e] = n;
             local += (n + MR - 1) / MR;
@@ -95,12 +118,10 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
     const long long v = (long long)blockIdx.x * W + wave;
     const long long i0 = items * v / V;
     const long long i1 = items * (v + 1) / V;
-    if (i0 >= i1)
-        return;
 
     // Item i: row chunk ci = i / NG of expert e (the last e with cum[e] <= ci), group i % NG.
     struct Item {
-        int e, grp, row0, rows;
+        int e, grp, row0, rows, slot;   // slot: the row chunk
     };
     auto item_at = [&](long long i) -> Item {
         Item it;
@@ -118,8 +139,30 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
         const int first = (ci - cum[lo]) * MR;
         it.row0 = rstart[lo] + first;
         it.rows = min(MR, rcount[lo] - first);
+        it.slot = ci;
         return it;
     };
+    // The item after `it`: the next group of the same chunk, else group 0 of the next chunk,
+    // whose expert is found by a binary search from it.e on (no 64-bit division).
+    auto item_next = [&](Item &it) {
+        if (++it.grp < NG)
+            return;
+        it.grp = 0;
+        const int ci = ++it.slot;
+        int lo = it.e, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cum[mid] <= ci)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        it.e = lo;
+        const int first = (ci - cum[lo]) * MR;
+        it.row0 = rstart[lo] + first;
+        it.rows = min(MR, rcount[lo] - first);
+    };
+
 
     // Prefetch cursor: item ip (described by pit), window wp.
     long long ip = i0;
@@ -129,14 +172,16 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
     auto set_sources = [&]() {
         rq = make_rsrc(a.Wq + (size_t)pit.e * cb + (size_t)pit.grp * gq, gq);
         rs = make_rsrc(a.Ws + (size_t)pit.e * sb + (size_t)pit.grp * gs, gs);
-        rx = make_rsrc(a.X + (size_t)pit.row0 * (size_t)K, (uint32_t)pit.rows * (uint32_t)K * 2u);
+        if constexpr (!LDSX)
+            rx = make_rsrc(a.X + (size_t)pit.row0 * (size_t)K,
+                           (uint32_t)pit.rows * (uint32_t)K * 2u);
     };
     set_sources();
     const uint32_t vq = 16u * (uint32_t)lane;
     const uint32_t vs = 4u * (uint32_t)(lane >> 1);
     const uint32_t sshift = 16u * (uint32_t)(lane & 1);
-    auto load_next = [&]() -> GroupedUnit<MR> {
-        GroupedUnit<MR> u;
+    auto load_next = [&]() -> GroupedUnit<MR, LDSX> {
+        GroupedUnit<MR, LDSX> u;
         const bool live = ip < i1 && (FAST || kGroupedWindow / kChunkK * wp + j < CH);
         const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(
             rq, off_if(live, vq + (uint32_t)wp * (16u * kChunkCodeBytes)), 0, kAuxStream);
@@ -146,30 +191,66 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
         u.code[3] = c[3];
         u.scale = __builtin_amdgcn_raw_buffer_load_b32(
             rs, off_if(live, vs + (uint32_t)wp * (16u * kChunkScaleBytes)), 0, kAuxStream);
-        const int kc = kGroupedWindow * wp + kChunkK * j;   // first k of the lane's chunk
+        if constexpr (!LDSX) {
+            const int kc = kGroupedWindow * wp + kChunkK * j;   // first k of the lane's chunk
 #pragma unroll
-        for (int m = 0; m < MR; m++)
+            for (int m = 0; m < MR; m++)
 #pragma unroll
-            for (int p = 0; p < 4; p++) {
-                const bool xv = live && m < pit.rows && kc + 8 * p < K;
-                u.x[m][p] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rx, off_if(xv, ((uint32_t)m * (uint32_t)K + (uint32_t)(kc + 8 * p)) * 2u), 0,
-                    kAuxNormal);
-            }
+                for (int p = 0; p < 4; p++) {
+                    const bool xv = live && m < pit.rows && kc + 8 * p < K;
+                    u.x[m][p] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rx, off_if(xv, ((uint32_t)m * (uint32_t)K + (uint32_t)(kc + 8 * p)) * 2u),
+                        0, kAuxNormal);
+                }
+        }
         if (++wp == nwin) {
             wp = 0;
             if (++ip < i1) {
-                pit = item_at(ip);
+                item_next(pit);
                 set_sources();
             }
         }
         return u;
     };
 
-    GroupedUnit<MR> ring[D];
+    GroupedUnit<MR, LDSX> ring[D];
+    if (i0 < i1) {
 #pragma unroll
-    for (int s = 0; s < D - 1; s++)
-        ring[s] = load_next();
+        for (int s = 0; s < D - 1; s++)
+            ring[s] = load_next();
+    }
+
+    // LDSX: stage the rows of the chunks [cfirst, clast] this workgroup's items touch.
+    const int row_bytes = nwin * (kGroupedWindow / kChunkK) * kGroupedSlot;
+    int cfirst = 0;
+    if constexpr (LDSX) {
+        const long long I0 = items * ((long long)blockIdx.x * W) / V;
+        const long long I1 = items * ((long long)(blockIdx.x + 1) * W) / V;
+        if (I0 < I1) {
+            cfirst = (int)(I0 / NG);
+            const int nch = min((int)((I1 - 1) / NG) - cfirst + 1, xrows / MR);
+            int *srow = reinterpret_cast<int *>(xlds + (size_t)xrows * row_bytes);
+            for (int t = threadIdx.x; t < nch * MR; t += kWave * W) {
+                const Item it = item_at((long long)(cfirst + t / MR) * NG);
+                srow[t] = (t % MR) < it.rows ? it.row0 + t % MR : -1;
+            }
+            __syncthreads();
+            const int row_pieces = nwin * (kGroupedWindow / 8);   // 16-byte pieces per row
+            for (int idx = threadIdx.x; idx < nch * MR * row_pieces; idx += kWave * W) {
+                const int t = idx / row_pieces;
+                const int e = idx - t * row_pieces;
+                const int row = srow[t];
+                u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+                if (row >= 0 && 8 * e < K)
+                    v = *reinterpret_cast<const u32x4_t *>(a.X + (size_t)row * K + 8 * e);
+                *reinterpret_cast<u32x4_t *>(xlds + (size_t)t * row_bytes +
+                                             (e >> 2) * kGroupedSlot + 16 * (e & 3)) = v;
+            }
+        }
+        __syncthreads();
+    }
+    if (i0 >= i1)
+        return;
 
     // Compute cursor: item ic (described by cit), window wc.
     long long ic = i0;
@@ -186,7 +267,7 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
             ring[(s + D - 1) % D] = load_next();
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
             if (u + s < units) {
-                const GroupedUnit<MR> &c = ring[s];
+                const GroupedUnit<MR, LDSX> &c = ring[s];
                 const uint32_t sc = c.scale >> sshift;
                 const float s0 = e4m3_to_f32<0>(sc);
                 const float s1 = e4m3_to_f32<1>(sc);
@@ -194,15 +275,29 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
                 decode32_bf16(c.code, w);
 #pragma unroll
                 for (int m = 0; m < MR; m++) {
+                    u32x4_t xv[4];
+                    if constexpr (LDSX) {
+                        // row m of the item's chunk, window wc, the lane's 32-k chunk j
+                        const uint8_t *xp = xlds +
+                                            (size_t)((cit.slot - cfirst) * MR + m) * row_bytes +
+                                            ((uint32_t)wc * 16u + (uint32_t)j) * kGroupedSlot;
+#pragma unroll
+                        for (int p = 0; p < 4; p++)
+                            xv[p] = *reinterpret_cast<const u32x4_t *>(xp + 16 * p);
+                    } else {
+#pragma unroll
+                        for (int p = 0; p < 4; p++)
+                            xv[p] = c.x[m][p];
+                    }
                     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 8; i++)
-                        p0 = __builtin_amdgcn_fdot2_f32_bf16(
-                            w[i], as_bf16x2(c.x[m][i / 4][i % 4]), p0, false);
+                        p0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(xv[i / 4][i % 4]),
+                                                              p0, false);
 #pragma unroll
                     for (int i = 8; i < 16; i++)
-                        p1 = __builtin_amdgcn_fdot2_f32_bf16(
-                            w[i], as_bf16x2(c.x[m][i / 4][i % 4]), p1, false);
+                        p1 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(xv[i / 4][i % 4]),
+                                                              p1, false);
                     acc[m] = __builtin_fmaf(p0, s0, acc[m]);
                     acc[m] = __builtin_fmaf(p1, s1, acc[m]);
                 }
@@ -219,7 +314,7 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a)
                     }
                     wc = 0;
                     if (++ic < i1)
-                        cit = item_at(ic);
+                        item_next(cit);
                 }
             }
         }

@@ -8,16 +8,22 @@ namespace nvfp4 {
 
 namespace {
 
-typedef void (*GroupedFn)(GroupedArgs);
+typedef void (*GroupedFn)(GroupedArgs, int);
 
-// [FAST][MR index: 1, 2, 4 rows per item]. Wavefronts per workgroup and windows in flight per
-// wavefront shrink as the rows (and the x registers of a window) grow.
-const GroupedFn kGrouped[2][3] = {
-    {&grouped_gemv_kernel<1, 16, 3, false>, &grouped_gemv_kernel<2, 8, 3, false>,
-     &grouped_gemv_kernel<4, 8, 2, false>},
-    {&grouped_gemv_kernel<1, 16, 3, true>, &grouped_gemv_kernel<2, 8, 3, true>,
-     &grouped_gemv_kernel<4, 8, 2, true>}};
+// [LDSX][FAST][MR index: 1, 2, 4 rows per item]. Wavefronts per workgroup and windows in flight
+// per wavefront shrink as the rows (and, without LDSX, the x registers of a window) grow.
+#define NVFP4_GROUPED(L, F)                                                                \
+    {                                                                                      \
+        &grouped_gemv_kernel<1, 16, 3, F, L>, &grouped_gemv_kernel<2, 8, 3, F, L>,         \
+            &grouped_gemv_kernel<4, 8, 2, F, L>                                            \
+    }
+const GroupedFn kGrouped[2][2][3] = {{NVFP4_GROUPED(false, false), NVFP4_GROUPED(false, true)},
+                                     {NVFP4_GROUPED(true, false), NVFP4_GROUPED(true, true)}};
 const int kGroupedWaves[3] = {16, 8, 8};
+
+// Dynamic LDS for the staged X rows (within the 64 KB every kernel may use without opting in,
+// next to the 24 KB of the expert tables).
+constexpr int kGroupedXLds = 32 * 1024;
 
 }  // namespace
 
@@ -44,8 +50,19 @@ hipError_t launch_grouped(const GroupedArgs &a, int rows_per_item, hipStream_t s
         cus <= 0)
         cus = 256;
     const int fast = (a.K % kGroupedWindow == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kGrouped[fast][mi], dim3((unsigned)cus), dim3(kWave * kGroupedWaves[mi]), 0,
-                       stream, a);
+    // Rows a workgroup stages: its items span at most ceil(items / G) + 1 consecutive items, so at
+    // most ceil(chunks / G) + 2 row chunks, and chunks <= ceil(T / MR) + E (offsets are made
+    // non-decreasing, so the experts' rows add up to at most T).
+    const int MR = rows_per_item;
+    const long long chunks = ((long long)a.T + MR - 1) / MR + a.E;
+    const long long need = (long long)MR * ((chunks + cus - 1) / cus + 2);
+    const int nwin = (a.K + kGroupedWindow - 1) / kGroupedWindow;
+    const int row_bytes = nwin * (kGroupedWindow / kChunkK) * kGroupedSlot;
+    const int ldsx = need * (row_bytes + 4) <= kGroupedXLds ? 1 : 0;
+    const int xrows = ldsx ? (int)need : 0;
+    hipLaunchKernelGGL(kGrouped[ldsx][fast][mi], dim3((unsigned)cus),
+                       dim3(kWave * kGroupedWaves[mi]), (size_t)xrows * (row_bytes + 4), stream,
+                       a, xrows);
     return hipGetLastError();
 }
 

@@ -93,7 +93,9 @@ def test_exact_integer_sums(device):
 
 
 def test_offsets_are_clamped(device):
-    """Offsets outside [0, T] are clamped; an expert whose end precedes its start has no rows."""
+    """Offsets are clamped to [0, T] and made non-decreasing (running maximum): an expert whose
+    end precedes its start has no rows, and the next expert starts where the running maximum
+    stands."""
     T, N, K = 6, 40, 512
     gen = inputs.generator(707)
     Wq, Ws, g = _random_experts(gen, 3, N, K, [0, 1, 2])
@@ -106,12 +108,9 @@ def test_offsets_are_clamped(device):
             Yref, A = oracle.grouped_gemm(inputs.bf16_bits(X), clamped, Wq, Ws, g)
             check_close(Y, Yref, A, f"clamped {raw}")
         else:
-            # expert 1 (4 -> 1) has no rows; experts 0 and 2 own rows 0..3 and 1..5 (overlap:
-            # rows 1..3 unspecified); rows 0, 4, 5 are each owned by one expert
-            Y0, A0 = oracle.grouped_gemm(inputs.bf16_bits(X[:4]), [0, 4, 4, 4], Wq, Ws, g)
-            Y2, A2 = oracle.grouped_gemm(inputs.bf16_bits(X[4:]), [0, 0, 0, 2], Wq, Ws, g)
-            check_close(Y[:1], Y0[:1], A0[:1], "row 0")
-            check_close(Y[4:], Y2, A2, "rows 4-5")
+            # running maximum [0, 4, 4, 6]: expert 0 rows 0..3, expert 1 none, expert 2 rows 4, 5
+            Yref, A = oracle.grouped_gemm(inputs.bf16_bits(X), [0, 4, 4, 6], Wq, Ws, g)
+            check_close(Y, Yref, A, f"running maximum {raw}")
 
 
 @pytest.mark.parametrize("tokens", [1, 16])
