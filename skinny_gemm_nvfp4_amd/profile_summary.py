@@ -12,8 +12,8 @@ duration spans both, counters are summed.
 
 HBM traffic: FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch but, on this part, do not
 necessarily count every memory channel; each is therefore scaled by bytes / counter of the
-calibration copy bench.py runs first (the largest ``__amd_rocclr_copyBuffer`` dispatch, a plain
-device-to-device copy of ``--calibration-bytes``).
+calibration copy bench.py runs first (the first ``__amd_rocclr_copyBuffer`` dispatch of about
+that size, a plain device-to-device copy of ``--calibration-bytes``).
 
 MFMA busy (``mfma``): SQ_VALU_MFMA_BUSY_CYCLES counts the matrix-core busy cycles of every SIMD
 (16 per v_mfma_f32_16x16x32_bf16); GRBM_GUI_ACTIVE counts the active cycles of the dispatch,
@@ -172,11 +172,15 @@ def mfma_summary(counters_csv: str, labels_path: str) -> str:
 
 
 def calibration(dispatches, counter: str, nbytes: int) -> float:
+    """bytes / counter bytes of the calibration copy: the FIRST copy dispatch whose counter is at
+    least 1/64 of `nbytes` (bench.py copies before anything else; later device-to-device copies,
+    such as cloned weight copies, may be larger and must not be taken for it; a counter may see
+    only a fraction of the channels)."""
     copies = [d for d in dispatches if d["name"].startswith(COPY_KERNEL) and counter in d]
-    if not copies:
-        raise ValueError(f"no {COPY_KERNEL} dispatch with {counter} in the profile")
-    big = max(copies, key=lambda d: d[counter])
-    return nbytes / (big[counter] * 1024.0)
+    big = [d for d in copies if d[counter] * 1024.0 >= nbytes / 64]
+    if not big:
+        raise ValueError(f"no {COPY_KERNEL} dispatch of the calibration size with {counter}")
+    return nbytes / (big[0][counter] * 1024.0)
 
 
 def traffic_summary(fetch_csv: str, write_csv: str, labels_path: str, nbytes: int):

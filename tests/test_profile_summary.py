@@ -141,3 +141,14 @@ def test_argmax_follow_on_dispatches_are_folded(tmp_path):
     assert "+argmax" in lines[1] and "    1.30" in lines[1]
     assert "+reduce +argmax" in lines[2] and "    2.60" in lines[2]
     assert "+argmax" not in lines[3] and "    1.00" in lines[3]
+
+
+def test_calibration_is_the_first_copy_of_its_size(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    # calibration 512 KiB counted for 1 MiB; a later, larger clone of weights must not be taken
+    _pmc(tmp_path / "f.csv", [(copy, [512.0]), (GEMM, [100.0]), (copy, [4096.0])], "FETCH_SIZE")
+    _pmc(tmp_path / "w.csv", [(copy, [1024.0]), (GEMM, [1.0]), (copy, [8192.0])], "WRITE_SIZE")
+    (tmp_path / "l.txt").write_text("g M=1 N=16 K=64\n")
+    kf, kw, _ = ps.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                   str(tmp_path / "l.txt"), 1 << 20)
+    assert kf == pytest.approx(2.0) and kw == pytest.approx(1.0)
