@@ -19,6 +19,7 @@
 #include "launch.h"
 #include "mfma_batch.h"
 #include "mfma_stream.h"
+#include "neighbours.h"
 
 namespace nvfp4 {
 
@@ -381,18 +382,19 @@ bool batch_plan(int rows, int N, int K, int ks_req, int s_req, BatchPlan *P)
     return true;
 }
 
-// Split-K workspace: one per device, grown (never shrunk or freed: a captured graph may still
-// hold an older one) on first need. Returns null when it would have to grow while the stream is
-// being captured, or when the allocation fails; the caller then runs without split K.
-float *batch_workspace(size_t bytes, hipStream_t stream)
+// Library workspaces: one per device and kind (kind 0: the split-K partial sums; kind 1: the
+// normalised X and the gate/up output of a fused call at M > 16), grown (never shrunk or freed:
+// a captured graph may still hold an older one) on first need. Returns null when it would have
+// to grow while the stream is being captured, or when the allocation fails.
+float *batch_workspace(size_t bytes, hipStream_t stream, int kind = 0)
 {
     static std::mutex mu;
-    static std::map<int, std::pair<void *, size_t>> ws;
+    static std::map<std::pair<int, int>, std::pair<void *, size_t>> ws;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return nullptr;
     std::lock_guard<std::mutex> lock(mu);
-    auto &e = ws[dev];
+    auto &e = ws[{dev, kind}];
     if (e.first != nullptr && e.second >= bytes)
         return static_cast<float *>(e.first);
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
@@ -661,9 +663,45 @@ int device_compute_units() { return compute_units(); }
 
 hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream)
 {
-    // The dot-product kernel for the smallest M when X fits in LDS, else the 16-row matrix-core
-    // kernel (any M, one 16-row block per workgroup row).
     const bool pair = a.H != nullptr;
+    if (a.M > 16) {
+        // The batch kernel reads each weight once for up to 128 rows; the neighbours run as
+        // kernels of their own around it, through a workspace (normalised X, fp32 gate/up).
+        const size_t xbytes = a.gamma ? ((size_t)a.M * a.K * 2 + 255) & ~(size_t)255 : 0;
+        const size_t ybytes = pair ? (size_t)a.M * a.N * 4 : 0;
+        uint8_t *ws = reinterpret_cast<uint8_t *>(batch_workspace(xbytes + ybytes, stream, 1));
+        if (ws == nullptr)
+            return hipErrorStreamCaptureUnsupported;   // (or out of memory)
+        (void)hipGetLastError();
+        GemmArgs b = a;
+        b.gamma = nullptr;
+        b.H = nullptr;
+        b.keys = nullptr;
+        b.key_slots = 0;
+        if (a.gamma) {
+            uint16_t *Xn = reinterpret_cast<uint16_t *>(ws);
+            hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3((unsigned)a.M), dim3(256), 0, stream, a.X,
+                               a.gamma, a.eps, a.K, Xn);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+            b.X = Xn;
+        }
+        if (pair)
+            b.Y = reinterpret_cast<float *>(ws + xbytes);
+        int path = kPathAuto, split = 0;
+        if (!choose_config(a.M, a.N, a.K, &path, &split))
+            return hipErrorInvalidValue;
+        hipError_t e = launch_impl(path, split, b, nullptr, nullptr, stream);
+        if (e != hipSuccess || !pair)
+            return e;
+        const long long count = (long long)a.M * (a.N / 2);
+        hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                           stream, b.Y, count, a.N, a.H);
+        return hipGetLastError();
+    }
+    // The dot-product kernel for the smallest M when X fits in LDS, else the 16-row matrix-core
+    // kernel.
     int path = kPathMfma, split = 0;
     StreamLayout L;
     int grid;

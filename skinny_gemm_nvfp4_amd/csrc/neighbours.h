@@ -1,0 +1,75 @@
+// neighbours.h -- the decode layer's neighbours of the GEMM as kernels of their own, for the
+// fused entry point at M > 16 (nvfp4_gemm_fused), where the batch kernel reads each weight once
+// for up to 128 rows but has no prologue or epilogue: RMSNorm of X before it, SiLU(gate) * up of
+// its interleaved gate/up output after it ("SparkInfer" README, section "Layout & scoring":
+// RMSNorm and fused FFN kernels). At M <= 16 the same steps run inside the GEMM kernels.
+#pragma once
+
+#include "device.h"
+
+namespace nvfp4 {
+
+// One workgroup of 256 threads per row m: Xn[m][k] = bf16((x * r) * gamma[k]) with
+// r = 1 / sqrt(mean_k x^2 + eps). The sum of squares: thread t adds the 8-value pieces t,
+// t + 256, ... in order (fma), then a fixed butterfly over the wavefront, then the four
+// wavefronts in order, so its relative error stays below (K / 64 + 32) 2^-24, as in the GEMM
+// kernels' prologues.
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *X, const uint16_t *gamma,
+                                                           float eps, int K, uint16_t *Xn)
+{
+    __shared__ float wsum[4];
+    const size_t row = (size_t)blockIdx.x * (size_t)K;
+    float t = 0.0f;
+    for (int p = threadIdx.x; 8 * p < K; p += 256) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(X + row + 8 * p);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float lo = __uint_as_float(v[i] << 16);
+            const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
+            t = __builtin_fmaf(lo, lo, t);
+            t = __builtin_fmaf(hi, hi, t);
+        }
+    }
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1)
+        t += __shfl_xor(t, d);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        wsum[threadIdx.x / kWave] = t;
+    __syncthreads();
+    const float s = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    const float r = 1.0f / __builtin_sqrtf(s / (float)K + eps);
+    for (int p = threadIdx.x; 8 * p < K; p += 256) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(X + row + 8 * p);
+        const u32x4_t gm = *reinterpret_cast<const u32x4_t *>(gamma + 8 * p);
+        u32x4_t o;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float x0 = __uint_as_float(v[i] << 16) * r;
+            const float x1 = __uint_as_float(v[i] & 0xFFFF0000u) * r;
+            bf16x2_t y;
+            y[0] = (__bf16)(x0 * __uint_as_float(gm[i] << 16));
+            y[1] = (__bf16)(x1 * __uint_as_float(gm[i] & 0xFFFF0000u));
+            o[i] = __builtin_bit_cast(uint32_t, y);
+        }
+        *reinterpret_cast<u32x4_t *>(Xn + row + 8 * p) = o;
+    }
+}
+
+// H[m][j] = bf16(SiLU(gate) * up) from the fp32 output Y[M][N] of an interleaved gate/up weight:
+// gate = Y[m][8q + c], up = Y[m][8q + 4 + c] for j = 4q + c. One thread per output.
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float *Y, long long count, int N,
+                                                       uint16_t *H)
+{
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= count)
+        return;
+    const int I = N >> 1;
+    const long long m = idx / I;
+    const int j = (int)(idx - m * I);
+    const float gate = Y[m * N + 8 * (j >> 2) + (j & 3)];
+    const float up = Y[m * N + 8 * (j >> 2) + 4 + (j & 3)];
+    const float h = gate / (1.0f + __expf(-gate)) * up;
+    H[idx] = __builtin_bit_cast(uint16_t, (__bf16)h);
+}
+
+}  // namespace nvfp4
