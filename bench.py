@@ -23,7 +23,7 @@ Protocol
   * "lm_head_argmax": the lm_head (N = 151936) at M = 1, 16, 128, writing the logits
     (nvfp4_gemm) and folding them into the greedy token per row (nvfp4_gemm_argmax).
   * "fused_neighbours": q/k/v with the RMSNorm folded in and gate/up with RMSNorm and
-    SiLU(gate)*up folded in, at M = 1 and 16, beside the plain GEMMs.
+    SiLU(gate)*up folded in, at M = 1, 16 and 128, beside the plain GEMMs.
   * "moe_grouped": the grouped (mixture-of-experts) GEMM, 128 experts with 8 routed per token,
     at decode (1 token) and verification (16 tokens), per call over rotating routings.
   * "full_pass": 64 layers of those shapes plus an NVFP4 lm_head (N = 151936), 12.33 GB of
@@ -403,7 +403,7 @@ def moe_grouped(dev, launches, steps: int):
 def fused_neighbours(dev, launches, steps: int):
     """The layer's q/k/v projection with the input RMSNorm folded in, and its gate/up projection
     with the post-attention RMSNorm and SiLU(gate) * up folded in (weight columns interleaved),
-    at M = 1 and M = 16 (weights seed 13 drawn on the device, x and gamma seed 14), next to the
+    at M = 1, 16 and 128 (weights seed 13 drawn on the device, x and gamma seed 14), next to the
     plain GEMM of the same shape. Bytes of a fused call: weights, X, gamma and its output (fp32 Y
     for q/k/v, bf16 H for gate/up)."""
     import torch
@@ -424,7 +424,7 @@ def fused_neighbours(dev, launches, steps: int):
         del W
         copies = max(2, -(-COLD_BYTES // rl.weight_bytes(K, N)))
         packs = [p0] + [Layer._clone(p0) for _ in range(copies - 1)]
-        for M in (1, 16):
+        for M in (1, 16, 128):
             X = inputs.activations(xgen, M, K, outliers=4).to(dev)
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             O = torch.empty((M, N // 2) if silu else (M, N),

@@ -39,7 +39,11 @@ PACK_KERNELS = ("pack_clear_kernel", "pack_amax_kernel", "pack_scale_kernel",
                 "pack_quant_kernel")
 # Dispatches that finish a GEMM call started by the dispatch before them: the split-K reduce (plain
 # or folding into argmax keys) and the greedy-token finalize of nvfp4_gemm_argmax.
-FOLLOW_KERNELS = ("batch_reduce_kernel", "batch_reduce_argmax_kernel", "argmax_finalize_kernel")
+FOLLOW_KERNELS = ("batch_reduce_kernel", "batch_reduce_argmax_kernel", "argmax_finalize_kernel",
+                  "silu_mul_kernel")
+# Dispatches that open a GEMM call whose GEMM dispatch comes next: the row-wise RMSNorm of a
+# fused call above 16 rows.
+LEAD_KERNELS = ("rmsnorm_rows_kernel",)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -94,11 +98,34 @@ def is_follow(name: str) -> bool:
     return any(f"nvfp4::{k}" in name for k in FOLLOW_KERNELS)
 
 
+def is_lead(name: str) -> bool:
+    return any(f"nvfp4::{k}" in name for k in LEAD_KERNELS)
+
+
+def _merge(into, d):
+    """Adds dispatch d to the call `into`: the span covers both, counters are summed."""
+    if "start" in d and "start" in into:
+        into["start"] = min(into["start"], d["start"])
+        into["end"] = max(into["end"], d["end"])
+        into["ns"] = into["end"] - into["start"]
+    for k, v in d.items():
+        if k.isupper() and isinstance(v, float):
+            into[k] = into.get(k, 0.0) + v
+
+
 def fold_reductions(gemms):
-    """Folds each follow-on dispatch (split-K reduce, argmax finalize) into the GEMM dispatch
-    before it."""
+    """Folds each follow-on dispatch (split-K reduce, argmax finalize, SiLU * up) into the GEMM
+    dispatch before it, and each lead dispatch (RMSNorm) into the GEMM dispatch after it."""
     out = []
+    lead = None
     for d in gemms:
+        if is_lead(d["name"]):
+            lead = d
+            continue
+        if lead is not None and not is_follow(d["name"]):
+            _merge(d, lead)
+            d["fused"] = True
+            lead = None
         if is_follow(d["name"]):
             if not out:
                 raise ValueError("a follow-on dispatch with no GEMM dispatch before it")
@@ -113,8 +140,12 @@ def fold_reductions(gemms):
                 prev["argmax"] = True
             if "batch_reduce" in d["name"]:
                 prev["split_k"] = True
+            if "silu_mul" in d["name"]:
+                prev["fused"] = True
             continue
         out.append(d)
+    if lead is not None:
+        raise ValueError("a lead dispatch with no GEMM dispatch after it")
     return out
 
 
@@ -144,7 +175,8 @@ def trace_summary(trace_csv: str, labels_path: str) -> str:
         us = [d["ns"] / 1e3 for d in ds]
         d0 = ds[0]
         kname = (short_name(d0["name"]) + (" +reduce" if d0.get("split_k") else "") +
-                 (" +argmax" if d0.get("argmax") else ""))
+                 (" +argmax" if d0.get("argmax") else "") +
+                 (" +norm/silu" if d0.get("fused") else ""))
         lines.append(
             f"{lab:44s} {kname[:56]:56s} {len(us):4d} "
             f"{statistics.fmean(us):8.2f} {statistics.median(us):8.2f} {min(us):8.2f}  "

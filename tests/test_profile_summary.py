@@ -152,3 +152,19 @@ def test_calibration_is_the_first_copy_of_its_size(tmp_path):
     kf, kw, _ = ps.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
                                    str(tmp_path / "l.txt"), 1 << 20)
     assert kf == pytest.approx(2.0) and kw == pytest.approx(1.0)
+
+
+NORM = "nvfp4::rmsnorm_rows_kernel(unsigned short const*, unsigned short const*, float, int, unsigned short*)"
+SILU = "nvfp4::silu_mul_kernel(float const*, long long, int, unsigned short*)"
+
+
+def test_fused_lead_and_follow_dispatches_are_folded(tmp_path):
+    # fused call above 16 rows: RMSNorm 0..500, batch GEMM 600..2600, SiLU 2700..2900 (2.9 us);
+    # then a plain GEMM
+    _trace(tmp_path / "t.csv", [(NORM, 0, 500), (BATCH, 600, 2000), (SILU, 2700, 200),
+                                (GEMM, 5000, 1000)])
+    (tmp_path / "l.txt").write_text("f M=128 N=16 K=64\np M=1 N=16 K=64\n")
+    lines = ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt")).splitlines()
+    assert len(lines) == 3
+    assert "+norm/silu" in lines[1] and "    2.90" in lines[1]
+    assert "+norm/silu" not in lines[2] and "    1.00" in lines[2]
