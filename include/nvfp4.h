@@ -233,7 +233,8 @@ uint64_t nvfp4_argmax_workspace_bytes(int M);
  * part of this library); the kernel reads the row counts from `offsets` on the device and deals
  * the (row chunk, 4-column group) items evenly to every wavefront of the grid.
  *
- *   T        rows of X and Y (token-expert pairs); 0 is allowed and does nothing
+ *   T        rows of X and Y (token-expert pairs); 0 is allowed and does nothing (the pointers
+ *            are then not checked or used, so empty tensors' null pointers are fine)
  *   E        experts, 1 <= E <= 2048
  *   N, K     the shape of every expert's weight (K % 16 == 0, as for nvfp4_gemm)
  *   X        in:  bf16 bits [T][K], device, rows sorted by expert

@@ -159,6 +159,8 @@ nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
     if ((unsigned long long)E * per >= kMaxBytes ||
         (unsigned long long)T * (unsigned long long)nvfp4::num_groups(N) >= (1ULL << 40))
         return NVFP4_ERROR_INVALID_VALUE;
+    if (T == 0)
+        return NVFP4_SUCCESS;   // no rows: nothing to read or write (X and Y may be empty/null)
     if (!X || !offsets || !Wq || !Wscale || !gscale || !Y)
         return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(offsets, 4) ||

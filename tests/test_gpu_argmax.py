@@ -222,3 +222,17 @@ def test_graph_replays_match_eager(device):
         torch.cuda.synchronize()
         for n, ((_, _, i, v, _), (ei, ev)) in enumerate(zip(runs, eager)):
             assert torch.equal(i, ei) and torch.equal(v, ev), f"replay {rep}: call {n} differs"
+
+
+@pytest.mark.parametrize("N", [1, 2, 5])
+@pytest.mark.parametrize("M", [1, 16, 128])
+def test_tiny_and_ragged_vocabularies(device, N, M):
+    """One, two and five columns (fewer than a 4-column group): the fold still picks the first
+    maximum of the GEMM's own output."""
+    K = 64
+    X, Wq, Ws, g = random_case(9000 + 10 * N + M, M, N, K, FINITE_SCALES)
+    say(f"tiny argmax M={M} N={N}")
+    packed = to_device_packed(Wq, Ws, g, device)
+    Y, idx, val = _run(X, packed, device, nv.PATH_AUTO, 0)
+    _check_fused_equals_unfused(Y, idx, val, f"tiny M={M} N={N}")
+    assert idx.min() >= 0 and idx.max() < N

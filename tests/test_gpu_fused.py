@@ -176,3 +176,29 @@ def test_fused_graph_replays_match_eager(device):
         torch.cuda.synchronize()
         for H, E in zip(Hs, eager):
             assert torch.equal(H, E), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("M", [1, 5, 17])
+def test_smallest_shapes(device, M):
+    """N = 8 (one gate/up pair) and K = 16 (one scale block), every fuse mode."""
+    N, K = 8, 16
+    gen = inputs.generator(7070 + M)
+    Wq, Ws = inputs.random_packed(gen, N, K, FINITE_SCALES)
+    g = np.float32(0.02)
+    X = inputs.activations(gen, M, K)
+    gamma = inputs.norm_weight(gen, K)
+    p = to_device_packed(Wq, Ws, g, device)
+    for fuse in (1, 2, 3):
+        norm = bool(fuse & nv.FUSE_RMSNORM)
+        label = f"smallest fused={fuse} M={M}"
+        say(label)
+        Yref, tol = _ref_gemm(_bits_of(X), Wq.numpy(), Ws.numpy(), g,
+                              _bits_of(gamma) if norm else None)
+        out = nv.gemm_fused(X.to(device), p.Wq, p.Ws, p.g, N,
+                            gamma=gamma.to(device) if norm else None, eps=EPS,
+                            silu_mul=bool(fuse & nv.FUSE_SILU_MUL))
+        torch.cuda.synchronize()
+        if fuse & nv.FUSE_SILU_MUL:
+            _check_h(out.cpu().view(torch.int16).numpy().view(np.uint16), Yref, tol, label)
+        else:
+            _check_y(out.cpu().numpy(), Yref, tol, label)

@@ -172,3 +172,27 @@ def test_graph_replays_match_eager(device):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(Y, eager[rep % 3]), f"replay {rep} differs"
+
+
+def test_no_rows_and_most_experts(device):
+    """T = 0 launches nothing and leaves Y as it was; E = 2048 (the most the kernel takes) with a
+    handful of rows on scattered experts, the others empty."""
+    N, K = 24, 256
+    E = 2048
+    gen = inputs.generator(1212)
+    used = [3, 700, 701, 2047]
+    Wq, Ws, g = _random_experts(gen, E, N, K, used)
+    dev_w = _experts_to_device(Wq, Ws, g, N, K, device)
+    Y = torch.full((0, N), 7.0, dtype=torch.float32, device=device)
+    say("grouped T=0")
+    nv.gemm_grouped(torch.empty((0, K), dtype=torch.bfloat16, device=device),
+                    torch.zeros(E + 1, dtype=torch.int32, device=device), *dev_w, N, out=Y)
+    torch.cuda.synchronize()
+    counts = np.zeros(E, dtype=np.int64)
+    counts[used] = [2, 1, 3, 1]
+    offsets = _offsets(counts)
+    X = inputs.activations(gen, int(offsets[-1]), K)
+    say("grouped E=2048")
+    Y = _run(X, offsets, dev_w, N, device)
+    Yref, A = oracle.grouped_gemm(inputs.bf16_bits(X), offsets, Wq, Ws, g)
+    check_close(Y, Yref, A, "E=2048")
