@@ -289,13 +289,14 @@ nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
  *   eps      RMSNorm epsilon, finite and >= 0 (e.g. 1e-6)
  *   out      out: fp32 Y [M][N] (4-byte aligned) without NVFP4_FUSE_SILU_MUL, bf16 bits
  *            H [M][N / 2] (2-byte aligned) with it; device
- * Kernels: the dot-product kernel for M <= 4 (X normalised once in LDS), the 16-row matrix-core
- * kernel for M <= 16 (each X window normalised as it is staged), both with the epilogue inside;
- * above 16 rows, a row-wise RMSNorm kernel, the GEMM nvfp4_gemm runs (each weight read once per
- * 128 rows) and an elementwise SiLU(gate) * up kernel, through a library workspace of M*K*2 +
- * M*N*4 bytes per device (allocated by the first call that needs it, never freed; under stream
- * capture a call that would have to grow it returns NVFP4_ERROR_LAUNCH, so run one call per
- * shape eagerly first; calls above 16 rows must not overlap on different streams of a device).
+ * Kernels: up to 4 rows the dot-product kernel does everything (X normalised once in LDS, the
+ * epilogue on its column sums). Above, RMSNorm is a row-wise kernel of its own writing the bf16
+ * xhat to a library workspace; then the 16-row matrix-core kernel with the SiLU(gate) * up
+ * epilogue inside (M <= 16), or the GEMM nvfp4_gemm runs (each weight read once per 128 rows)
+ * followed by an elementwise SiLU(gate) * up kernel (M > 16). The workspace (M*K*2 + M*N*4
+ * bytes at most, per device) is allocated by the first call that needs it and never freed;
+ * under stream capture a call that would have to grow it returns NVFP4_ERROR_LAUNCH, so run one
+ * call per shape eagerly first; such calls must not overlap on different streams of a device.
  * Errors as for nvfp4_gemm.
  */
 enum { NVFP4_FUSE_RMSNORM = 1, NVFP4_FUSE_SILU_MUL = 2 };

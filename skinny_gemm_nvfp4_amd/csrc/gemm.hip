@@ -254,7 +254,7 @@ bool mfma_plan(int N, int K, int waves, MfmaPlan *P, bool pair = false)
     P->grid = G;
     P->tc_index = ti;
     P->lds = mfma_stream_lds_bytes(kMfmaTiles[ti], waves);
-    return P->lds + 256 <= kMaxLds;   // (plus the kernel's static RMSNorm array)
+    return P->lds <= kMaxLds;
 }
 
 // Wavefronts of the matrix-core kernel when the caller leaves it open: wide chunks keep more
@@ -664,62 +664,63 @@ int device_compute_units() { return compute_units(); }
 hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream)
 {
     const bool pair = a.H != nullptr;
-    if (a.M > 16) {
-        // The batch kernel reads each weight once for up to 128 rows; the neighbours run as
-        // kernels of their own around it, through a workspace (normalised X, fp32 gate/up).
-        const size_t xbytes = a.gamma ? ((size_t)a.M * a.K * 2 + 255) & ~(size_t)255 : 0;
-        const size_t ybytes = pair ? (size_t)a.M * a.N * 4 : 0;
-        uint8_t *ws = reinterpret_cast<uint8_t *>(batch_workspace(xbytes + ybytes, stream, 1));
-        if (ws == nullptr)
-            return hipErrorStreamCaptureUnsupported;   // (or out of memory)
-        (void)hipGetLastError();
-        GemmArgs b = a;
-        b.gamma = nullptr;
-        b.H = nullptr;
-        b.keys = nullptr;
-        b.key_slots = 0;
-        if (a.gamma) {
-            uint16_t *Xn = reinterpret_cast<uint16_t *>(ws);
-            hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3((unsigned)a.M), dim3(256), 0, stream, a.X,
-                               a.gamma, a.eps, a.K, Xn);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess)
-                return e;
-            b.X = Xn;
-        }
-        if (pair)
-            b.Y = reinterpret_cast<float *>(ws + xbytes);
-        int path = kPathAuto, split = 0;
-        if (!choose_config(a.M, a.N, a.K, &path, &split))
-            return hipErrorInvalidValue;
-        hipError_t e = launch_impl(path, split, b, nullptr, nullptr, stream);
-        if (e != hipSuccess || !pair)
-            return e;
-        const long long count = (long long)a.M * (a.N / 2);
-        hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                           stream, b.Y, count, a.N, a.H);
-        return hipGetLastError();
-    }
-    // The dot-product kernel for the smallest M when X fits in LDS, else the 16-row matrix-core
-    // kernel.
-    int path = kPathMfma, split = 0;
+    // Up to 4 rows the dot-product kernel does it all: X is staged in LDS anyway, so RMSNorm
+    // costs two barriers and a pass over LDS, and the SiLU(gate) * up epilogue runs on the
+    // column sums. Above, the RMSNorm is a row-wise kernel of its own (normalising each X window
+    // inside the 16-row kernel cost more than the launch); the SiLU(gate) * up epilogue stays in
+    // the 16-row kernel (M <= 16) or follows the batch kernel as an elementwise kernel (M > 16,
+    // the batch kernel reading each weight once per 128 rows).
     StreamLayout L;
     int grid;
-    if (a.M <= 4 && stream_plan(a.M, a.N, a.K, a.M, 16, &grid, &L, pair)) {
-        path = kPathDot;
-        split = 16;
-    } else {
+    const bool dot = a.M <= 4 && stream_plan(a.M, a.N, a.K, a.M, 16, &grid, &L, pair);
+    const bool split_silu = pair && a.M > 16;
+    const size_t xbytes = (!dot && a.gamma) ? ((size_t)a.M * a.K * 2 + 255) & ~(size_t)255 : 0;
+    const size_t ybytes = split_silu ? (size_t)a.M * a.N * 4 : 0;
+    uint8_t *ws = nullptr;
+    if (xbytes + ybytes > 0) {
+        ws = reinterpret_cast<uint8_t *>(batch_workspace(xbytes + ybytes, stream, 1));
+        if (ws == nullptr)
+            return hipErrorStreamCaptureUnsupported;   // (or out of memory)
+    }
+    (void)hipGetLastError();
+    GemmArgs b = a;
+    b.keys = nullptr;
+    b.key_slots = 0;
+    if (xbytes > 0) {
+        uint16_t *Xn = reinterpret_cast<uint16_t *>(ws);
+        hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3((unsigned)a.M), dim3(256), 0, stream, a.X,
+                           a.gamma, a.eps, a.K, Xn);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        b.X = Xn;
+        b.gamma = nullptr;
+    }
+    if (dot)
+        return launch_impl(kPathDot, 16, b, nullptr, nullptr, stream);
+    if (a.M <= 16) {
         MfmaPlan P;
-        split = 8;
+        int split = 8;
         if (!mfma_plan(a.N, a.K, 8, &P, pair) || kMfmaTiles[P.tc_index] >= 6)
             split = 4;
         if (!mfma_plan(a.N, a.K, split, &P, pair))
             return hipErrorInvalidValue;
+        return launch_impl(kPathMfma, split, b, nullptr, nullptr, stream);
     }
-    GemmArgs b = a;
-    b.keys = nullptr;
-    b.key_slots = 0;
-    return launch_impl(path, split, b, nullptr, nullptr, stream);
+    if (split_silu) {
+        b.H = nullptr;
+        b.Y = reinterpret_cast<float *>(ws + xbytes);
+    }
+    int path = kPathAuto, split = 0;
+    if (!choose_config(a.M, a.N, a.K, &path, &split))
+        return hipErrorInvalidValue;
+    hipError_t e = launch_impl(path, split, b, nullptr, nullptr, stream);
+    if (e != hipSuccess || !split_silu)
+        return e;
+    const long long count = (long long)a.M * (a.N / 2);
+    hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                       stream, b.Y, count, a.N, a.H);
+    return hipGetLastError();
 }
 
 }  // namespace nvfp4

@@ -50,7 +50,6 @@ struct MfmaWindow {
     u32x4_t x[4];      // X pieces in load order: row 4 p + l / 16, k = 8 (l % 16)
     u32x4_t c[TC];     // the lane's 16 code bytes of each tile
     uint32_t s[TC];    // the word holding the lane's 2 scale bytes of each tile
-    u32x4_t gm;        // RMSNorm: gamma at the lane's 8 k (zero when not normalising)
 
     // lq/ls: the lane's code/scale offset within a tile-window at window 0; tq/ts: bytes per
     // tile; wq/ws: bytes per window; xo: the lane's X offset at window 0.
@@ -58,13 +57,8 @@ struct MfmaWindow {
     __device__ __forceinline__ void load(rsrc_t rq, rsrc_t rs, rsrc_t rx, uint32_t lq,
                                          uint32_t ls, uint32_t tq, uint32_t ts, uint32_t xo,
                                          int xk, int w, bool live, int tc0, int ngroups,
-                                         int gr, int q, int CH, int K, rsrc_t rg, bool norm)
+                                         int gr, int q, int CH, int K)
     {
-        gm = u32x4_t{0u, 0u, 0u, 0u};
-        if (norm)
-            gm = __builtin_amdgcn_raw_buffer_load_b128(
-                rg, off_if(live && kMfmaWindow * w + xk < K, (uint32_t)(kMfmaWindow * w + xk) * 2u),
-                0, kAuxNormal);
 #pragma unroll
         for (int p = 0; p < 4; p++)
             x[p] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -92,27 +86,6 @@ struct MfmaWindow {
         for (int p = 0; p < 4; p++)
             *reinterpret_cast<u32x4_t *>(buf + (4 * p + (lane >> 4)) * kXRowBytes +
                                          16 * (lane & 15)) = x[p];
-    }
-
-    // RMSNorm: X pieces as bf16((x * r) * gamma) into the wavefront's LDS buffer; rr[p] is r of
-    // the piece's row.
-    __device__ __forceinline__ void stage_norm(uint8_t *buf, int lane, const float rr[4]) const
-    {
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            u32x4_t o;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float x0 = __uint_as_float(x[p][i] << 16) * rr[p];
-                const float x1 = __uint_as_float(x[p][i] & 0xFFFF0000u) * rr[p];
-                bf16x2_t y;
-                y[0] = (__bf16)(x0 * __uint_as_float(gm[i] << 16));
-                y[1] = (__bf16)(x1 * __uint_as_float(gm[i] & 0xFFFF0000u));
-                o[i] = __builtin_bit_cast(uint32_t, y);
-            }
-            *reinterpret_cast<u32x4_t *>(buf + (4 * p + (lane >> 4)) * kXRowBytes +
-                                         16 * (lane & 15)) = o;
-        }
     }
 
     __device__ __forceinline__ void mul(f32x4_t (&acc)[TC], const uint8_t *buf, int r, int q,
@@ -185,48 +158,6 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     // This wavefront's windows: wave, wave + W, ...; window i of the wavefront is wave + i W.
     const int nmine = (nwin - wave + W - 1) / W;
 
-    // RMSNorm: r of each of the block's rows (wavefront w takes rows w, w + W, ...: lane sums of
-    // x^2 over k = 8 lane + 512 i in order, loads issued eight at a time, then a fixed butterfly;
-    // relative error below (K / 64 + 32) 2^-24), then each lane keeps r of its 4 staging rows.
-    // Done once, after the first weight windows are in flight.
-    const bool norm = a.gamma != nullptr;
-    const rsrc_t rg = make_rsrc(a.gamma, norm ? (uint32_t)K * 2u : 0u);
-    float rr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    __shared__ float nr[16];
-    auto row_norms = [&]() {
-        for (int m = wave; m < 16; m += W) {
-            float t = 0.0f;
-            for (int k0 = 8 * lane; k0 < K; k0 += 8 * 8 * kWave) {
-                u32x4_t v[8];
-#pragma unroll
-                for (int b = 0; b < 8; b++) {
-                    const int k = k0 + 8 * kWave * b;
-                    v[b] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rx, off_if(m < mrows && k < K, ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u),
-                        0, kAuxNormal);
-                }
-#pragma unroll
-                for (int b = 0; b < 8; b++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float lo = __uint_as_float(v[b][i] << 16);
-                        const float hi = __uint_as_float(v[b][i] & 0xFFFF0000u);
-                        t = __builtin_fmaf(lo, lo, t);
-                        t = __builtin_fmaf(hi, hi, t);
-                    }
-            }
-#pragma unroll
-            for (int d = kWave / 2; d >= 1; d >>= 1)
-                t += __shfl_xor(t, d);
-            if (lane == 0)
-                nr[m] = 1.0f / __builtin_sqrtf(t / (float)K + a.eps);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < 4; p++)
-            rr[p] = nr[4 * p + (lane >> 4)];
-    };
-
     // Argmax mode: every output this thread adds up below is in row 4 q + wave % 4 of the block
     // (W is a multiple of 4), so one key per thread.
     argkey_t best = 0;
@@ -244,17 +175,12 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
         auto load = [&](int i, MfmaWindow<TC> &win) {
             const int w = wave + i * W;
             win.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w, i < nmine, tc0,
-                                    ngroups, gr, q, CH, K, rg, norm);
+                                    ngroups, gr, q, CH, K);
         };
 #pragma unroll
         for (int i = 0; i < D - 1; i++)
             load(i, ring[i]);
-        if (norm && tc0 == 0)
-            row_norms();   // once, with the first windows of weights already requested
-        if (norm)
-            ring[0].stage_norm(xbuf[0], lane, rr);
-        else
-            ring[0].stage(xbuf[0], lane);
+        ring[0].stage(xbuf[0], lane);
         for (int i0 = 0; i0 < nmine; i0 += D) {
 #pragma unroll
             for (int u = 0; u < D; u++) {
@@ -264,12 +190,8 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
                     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
                     ring[u].mul(acc, xbuf[i & 1], r, q, nt, sshift);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (i + 1 < nmine) {
-                        if (norm)
-                            ring[(u + 1) % D].stage_norm(xbuf[(i + 1) & 1], lane, rr);
-                        else
-                            ring[(u + 1) % D].stage(xbuf[(i + 1) & 1], lane);
-                    }
+                    if (i + 1 < nmine)
+                        ring[(u + 1) % D].stage(xbuf[(i + 1) & 1], lane);
                 }
             }
         }
