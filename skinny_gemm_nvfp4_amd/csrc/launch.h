@@ -18,10 +18,11 @@ struct GemmArgs {
     // owns into one argmax key per row (argmax.h) and stores it at keys[m * key_slots + slot].
     unsigned long long *keys = nullptr;
     int key_slots = 0;
-    // Layer neighbours (nvfp4_gemm_fused). gamma set: X is replaced by its RMSNorm, rounded to
-    // bf16, xhat = bf16((x * r) * gamma[k]) with r = 1 / sqrt(mean_k x^2 + eps) per row. H set:
-    // instead of Y, H[m][j] = bf16(SiLU(gate) * up) from the column pairs of the interleaved
-    // gate/up weight (columns 8q + c and 8q + 4 + c, c < 4, give j = 4q + c); N % 8 == 0.
+    // Layer neighbours (nvfp4_gemm_fused). gamma set (dot-product kernel only): X is replaced by
+    // its RMSNorm, rounded to bf16, xhat = bf16((x * r) * gamma[k]) with r = 1 / sqrt(mean_k x^2
+    // + eps) per row. H set (dot-product and 16-row kernels): instead of Y, H[m][j] =
+    // bf16(SiLU(gate) * up) from the column pairs of the interleaved gate/up weight (columns
+    // 8q + c and 8q + 4 + c, c < 4, give j = 4q + c); N % 8 == 0.
     const uint16_t *gamma = nullptr;   // bf16 [K]
     float eps = 0.0f;
     uint16_t *H = nullptr;             // bf16 [M][N / 2]

@@ -1,8 +1,8 @@
 // neighbours.h -- the decode layer's neighbours of the GEMM as kernels of their own, for the
-// fused entry point at M > 16 (nvfp4_gemm_fused), where the batch kernel reads each weight once
-// for up to 128 rows but has no prologue or epilogue: RMSNorm of X before it, SiLU(gate) * up of
-// its interleaved gate/up output after it ("SparkInfer" README, section "Layout & scoring":
-// RMSNorm and fused FFN kernels). At M <= 16 the same steps run inside the GEMM kernels.
+// fused entry point (nvfp4_gemm_fused): the RMSNorm of X before the GEMM above 4 rows (up to 4
+// the dot-product kernel normalises X in LDS itself), and SiLU(gate) * up of the interleaved
+// gate/up output after the batch kernel above 16 rows (up to 16 the GEMM kernels' epilogues do
+// it) ("SparkInfer" README, section "Layout & scoring": RMSNorm and fused FFN kernels).
 #pragma once
 
 #include "device.h"
