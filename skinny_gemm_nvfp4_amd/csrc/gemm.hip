@@ -33,6 +33,13 @@ typedef void (*StreamFn)(GemmArgs, StreamLayout);
 // ahead of the first bytes every wavefront waits for (one row: 3 vs 4 saves 0.3-0.45 us on qkv and
 // o_proj and is even on gate_up and down; four rows: 2 vs 4 saves 1-1.8 us).
 constexpr int stream_depth(int rows) { return rows == 1 ? 3 : 2; }
+
+// Wavefronts per workgroup of the dot-product kernel when the caller leaves it open: 16, or 8
+// for one row when a workgroup has at most 128 units (512-k windows of a 4-column group) to
+// stream. Measured on the layer shapes with cold weights: q/k/v and o_proj (50-70 units) are
+// 0.2-0.4 us faster with 8; gate_up (340) and the lm_head (1480) 0.5-3 us slower; 4 is slower
+// everywhere.
+int dot_default_waves(int rows, int N, int K);
 constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 constexpr int kDefaultLds = 64 * 1024;      // above this a kernel must opt in
 
@@ -230,6 +237,13 @@ bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L,
     L->rnwin = 1.0f / (float)L->nwin;
     *grid = G;
     return true;
+}
+
+int dot_default_waves(int rows, int N, int K)
+{
+    const long long G = group_grid(N);
+    const long long units = (num_groups(N) + G - 1) / G * ((K + kStreamWindow - 1) / kStreamWindow);
+    return rows == 1 && units <= 128 ? 8 : 16;
 }
 
 // Workgroups, column-tile chunk and LDS bytes of the matrix-core kernel.
@@ -474,7 +488,7 @@ bool choose_config(int M, int N, int K, int *path, int *split)
         if (M > kDotMaxM)
             return false;
         if (*split == 0)
-            *split = 16;
+            *split = dot_default_waves(M, N, K);
         StreamLayout L;
         int grid;
         if (wave_index(*split) < 0)
@@ -672,7 +686,8 @@ hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream)
     // the batch kernel reading each weight once per 128 rows).
     StreamLayout L;
     int grid;
-    const bool dot = a.M <= 4 && stream_plan(a.M, a.N, a.K, a.M, 16, &grid, &L, pair);
+    const int dw = dot_default_waves(a.M, a.N, a.K);
+    const bool dot = a.M <= 4 && stream_plan(a.M, a.N, a.K, a.M, dw, &grid, &L, pair);
     const bool split_silu = pair && a.M > 16;
     const size_t xbytes = (!dot && a.gamma) ? ((size_t)a.M * a.K * 2 + 255) & ~(size_t)255 : 0;
     const size_t ybytes = split_silu ? (size_t)a.M * a.N * 4 : 0;
@@ -697,7 +712,7 @@ hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream)
         b.gamma = nullptr;
     }
     if (dot)
-        return launch_impl(kPathDot, 16, b, nullptr, nullptr, stream);
+        return launch_impl(kPathDot, dw, b, nullptr, nullptr, stream);
     if (a.M <= 16) {
         MfmaPlan P;
         int split = 8;
