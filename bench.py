@@ -195,11 +195,34 @@ def cpu_baseline(workload, seconds: float):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    cores = oracle.num_threads()
     rec = {"value": round(bytes_per_pass * passes / dt / 1e9, 4), "unit": "GB/s",
-           "cores": oracle.num_threads(), "kind": "oracle",
+           "cores": cores, "kind": "oracle",
            "sample": f"whole layer (4 GEMMs) at M=1, {passes} pass(es) in {dt:.1f} s, "
-                     "double accumulation, OpenMP over output columns"}
+                     "double accumulation, OpenMP over output columns",
+           "cpu": cpu_model()}
+    # The same oracle on one core: one pass of the layer.
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    for x, p in zip(xbits, packed):
+        oracle.gemm(x, *p)
+    d1 = time.perf_counter() - t1
+    oracle.set_num_threads(cores)
+    rec["single_core"] = {"value": round(bytes_per_pass / d1 / 1e9, 4), "unit": "GB/s",
+                          "cores": 1, "sample": f"one pass of the layer in {d1:.1f} s"}
     return rec, refs
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the record of the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def full_pass(dev, launches, reps: int):

@@ -63,6 +63,8 @@ def lib():
     L.oracle_gemm.restype = ctypes.c_int
     L.oracle_num_threads.argtypes = []
     L.oracle_num_threads.restype = ctypes.c_int
+    L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    L.oracle_set_num_threads.restype = None
     _lib = L
     return L
 
@@ -262,6 +264,11 @@ def argmax_rows(Y: np.ndarray) -> np.ndarray:
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops run on."""
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on (for timing it on one core)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def tolerance(A: np.ndarray) -> np.ndarray:

@@ -296,3 +296,14 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the OpenMP loops from now on (the benchmark times the oracle on all host cores and
+ * on one); n < 1 is taken as 1. No effect without OpenMP. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}
