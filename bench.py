@@ -26,6 +26,8 @@ Protocol
     SiLU(gate)*up folded in, at M = 1, 16 and 128, beside the plain GEMMs.
   * "moe_grouped": the grouped (mixture-of-experts) GEMM, 128 experts with 8 routed per token,
     at decode (1 token) and verification (16 tokens), per call over rotating routings.
+  * "tp8_shard": one GPU's share of the layer under 8-way tensor parallelism (q/k/v, gate/up
+    split N; o_proj, down split K) at M = 1, 16, 128.
   * "full_pass": 64 layers of those shapes plus an NVFP4 lm_head (N = 151936), 12.33 GB of
     packed weights (weights seed 9 drawn on the device one tensor at a time and packed, x seed
     10), at M = 1 and M = 16: the 257 GEMMs captured as one HIP graph per M, replays timed with
@@ -480,6 +482,36 @@ def fused_neighbours(dev, launches, steps: int):
     return out
 
 
+def tp8_shard(dev, launches, steps: int):
+    """One GPU's share of the dense layer under 8-way tensor parallelism (q/k/v and gate/up split
+    N, o_proj and down split K) at M = 1, 16 and 128, per GEMM, as the other legs (the
+    collective of the row-parallel halves is not part of a one-GPU run)."""
+    import torch
+    import skinny_gemm_nvfp4_amd as nv
+    from skinny_gemm_nvfp4_amd import inputs, roofline as rl
+    wgen = torch.Generator(device=dev).manual_seed(15)
+    xgen = inputs.generator(16)
+    out = {"tp": inputs.TP,
+           "timing": "HIP events around graph replays of 32 calls rotating over cold copies"}
+    for name, (K, N) in inputs.TP8_SHARD_SHAPES.items():
+        p0 = nv.pack(inputs.weights_on_device(wgen, K, N, dev))
+        copies = max(2, -(-COLD_BYTES // rl.weight_bytes(K, N)))
+        packs = [p0] + [Layer._clone(p0) for _ in range(copies - 1)]
+        for M in (1, 16, 128):
+            X = inputs.activations(xgen, M, K).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+            def call(c, X=X, Y=Y, packs=packs):
+                nv.gemm(X, *packs[c], out=Y)
+
+            lab = f"tp8.{name} M={M} N={N} K={K}"
+            us = graph_time_us(call, copies, max(64, steps), lab, launches)
+            out[f"{name}_m{M}"] = gemm_report((M, N, K), us)
+        del packs
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -492,6 +524,8 @@ def main() -> int:
     ap.add_argument("--no-full-pass", action="store_true",
                     help="skip the 64-layer + lm_head weight pass at M=1 and M=16")
     ap.add_argument("--full-pass-reps", type=int, default=20)
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the 8-way tensor-parallel shard shapes")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the RMSNorm / SiLU(gate)*up fused-neighbour timing")
     ap.add_argument("--no-moe", action="store_true",
@@ -642,6 +676,11 @@ def main() -> int:
         log("timing the grouped (mixture-of-experts) GEMM: decode and verify routings")
         moe = moe_grouped(dev, launches, args.steps)
 
+    shard = None
+    if not args.no_shard:
+        log("timing one GPU's share of the layer under 8-way tensor parallelism")
+        shard = tp8_shard(dev, launches, args.steps)
+
     fp = None
     if not args.no_full_pass:
         log("generating, packing and timing the full weight pass (64 layers + lm_head)")
@@ -669,6 +708,7 @@ def main() -> int:
         "lm_head_argmax": lmh,
         "moe_grouped": moe,
         "fused_neighbours": fused,
+        "tp8_shard": shard,
         "full_pass": fp,
         "source_hash": ps.source_hash(),
     }

@@ -208,3 +208,14 @@ RMSNORM_EPS = 1e-6
 def norm_weight(gen: torch.Generator, K: int) -> torch.Tensor:
     """bf16 RMSNorm gain gamma[K] = 1 + 0.1 N(0, 1) (a trained norm's gains sit around 1)."""
     return (1.0 + 0.1 * torch.randn(K, generator=gen, dtype=torch.float32)).to(torch.bfloat16)
+
+
+# ---- one GPU's share of an 8-way tensor-parallel layer ----
+TP = 8
+# name -> (K, N): column-parallel projections split N, row-parallel ones split K.
+TP8_SHARD_SHAPES: Dict[str, Tuple[int, int]] = {
+    "qkv": (HIDDEN, (HIDDEN + 2 * KV_DIM) // TP),
+    "o_proj": (HIDDEN // TP, HIDDEN),
+    "gate_up": (HIDDEN, 2 * INTERMEDIATE // TP),
+    "down": (INTERMEDIATE // TP, HIDDEN),
+}
