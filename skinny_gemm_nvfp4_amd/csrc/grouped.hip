@@ -21,6 +21,14 @@ const GroupedFn kGrouped[2][2][3] = {{NVFP4_GROUPED(false, false), NVFP4_GROUPED
                                      {NVFP4_GROUPED(true, false), NVFP4_GROUPED(true, true)}};
 const int kGroupedWaves[3] = {16, 8, 8};
 
+// One row per item and at most 16 rows in all (decode: a token's routed experts): 8 wavefronts
+// with 4 windows in flight each. A wavefront then has about one item and streams it in one round
+// trip instead of two (measured: 3-8% faster on the decode calls, slower on 128 rows). [LDSX][FAST]
+const GroupedFn kGroupedFew[2][2] = {
+    {&grouped_gemv_kernel<1, 8, 4, false, false>, &grouped_gemv_kernel<1, 8, 4, true, false>},
+    {&grouped_gemv_kernel<1, 8, 4, false, true>, &grouped_gemv_kernel<1, 8, 4, true, true>}};
+constexpr int kGroupedFewRows = 16;
+
 // Dynamic LDS for the staged X rows (within the 64 KB every kernel may use without opting in,
 // next to the 24 KB of the expert tables).
 constexpr int kGroupedXLds = 32 * 1024;
@@ -60,9 +68,11 @@ hipError_t launch_grouped(const GroupedArgs &a, int rows_per_item, hipStream_t s
     const int row_bytes = nwin * (kGroupedWindow / kChunkK) * kGroupedSlot;
     const int ldsx = need * (row_bytes + 4) <= kGroupedXLds ? 1 : 0;
     const int xrows = ldsx ? (int)need : 0;
-    hipLaunchKernelGGL(kGrouped[ldsx][fast][mi], dim3((unsigned)cus),
-                       dim3(kWave * kGroupedWaves[mi]), (size_t)xrows * (row_bytes + 4), stream,
-                       a, xrows);
+    const bool few = MR == 1 && a.T <= kGroupedFewRows;
+    const GroupedFn fn = few ? kGroupedFew[ldsx][fast] : kGrouped[ldsx][fast][mi];
+    const int waves = few ? 8 : kGroupedWaves[mi];
+    hipLaunchKernelGGL(fn, dim3((unsigned)cus), dim3(kWave * waves),
+                       (size_t)xrows * (row_bytes + 4), stream, a, xrows);
     return hipGetLastError();
 }
 
