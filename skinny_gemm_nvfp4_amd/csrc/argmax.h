@@ -84,8 +84,16 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const argkey_t *ke
     const int m = blockIdx.x;
     const argkey_t *row = keys + (size_t)m * (size_t)slots;
     argkey_t k = 0;
-    for (int s = threadIdx.x; s < slots; s += 256)
-        k = key_max(k, row[s]);
+    // Eight loads in flight per thread (a row holds up to 16 keys per compute unit).
+    for (int s0 = threadIdx.x; s0 < slots; s0 += 8 * 256) {
+        argkey_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = s0 + 256 * i < slots ? row[s0 + 256 * i] : 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            k = key_max(k, v[i]);
+    }
     k = key_max_64(k);
     if ((threadIdx.x & (kWave - 1)) == 0)
         best[threadIdx.x / kWave] = k;
