@@ -66,16 +66,21 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a, i
     const size_t cb = (size_t)NG * gq;                      // code bytes per expert
     const size_t sb = (size_t)NG * gs;                      // scale bytes per expert
 
+    // The offsets, clamped to [0, T], into cum[] first: one load per thread, all in flight at
+    // once (the scan below reads them from LDS and overwrites cum[] only after its last read).
+    for (int e = threadIdx.x; e <= E; e += kWave * W)
+        cum[e] = min(max(a.offsets[e], 0), T);
+    __syncthreads();
+
     // Prefix sums of the row chunks, by wavefront 0: lane l takes a contiguous run of experts.
-    // Boundaries: offsets clamped to [0, T], then a running maximum (prefix max over the lanes'
-    // runs), so expert e owns rows [b_e, b_{e+1}) with b non-decreasing.
+    // Boundaries: the clamped offsets, then a running maximum (prefix max over the lanes' runs),
+    // so expert e owns rows [b_e, b_{e+1}) with b non-decreasing.
     if (wave == 0) {
         const int per = (E + kWave - 1) / kWave;
         const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
-        auto clampT = [&](int v) { return min(max(v, 0), T); };
         int lmax = 0;
         for (int e = e0; e < e1; e++)
-            lmax = max(lmax, clampT(a.offsets[e]));
+            lmax = max(lmax, cum[e]);
         int pmax = lmax;   // inclusive prefix max over lanes
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -88,8 +93,8 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a, i
             bnd = 0;
         int local = 0;
         for (int e = e0; e < e1; e++) {
-            const int r0 = max(bnd, clampT(a.offsets[e]));
-            bnd = max(r0, clampT(a.offsets[e + 1]));
+            const int r0 = max(bnd, cum[e]);
+            bnd = max(r0, cum[e + 1]);
             const int n = bnd - r0;
             rstart[e] = r0;
             rcount[e] = n;
