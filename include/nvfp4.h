@@ -216,7 +216,8 @@ nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
                                       void *stream);
 
 /* Workspace bytes nvfp4_gemm_argmax needs for M rows on the current device:
- * 8 * 16 * (compute units) per row (one 8-byte key per wavefront of the widest kernel);
+ * 8 * 16 * (compute units) per row (room for 16 8-byte keys per compute unit; the kernels write
+ * at most 4 per compute unit, or 256 per row after a K-split reduce);
  * 0 if M < 1. */
 uint64_t nvfp4_argmax_workspace_bytes(int M);
 

@@ -15,10 +15,10 @@
 // is associative and commutative: any fold order gives the same winner, so results are exact and
 // reproducible however the writers split the columns.
 //
-// Fold. Each writer (a wavefront or a group of lanes) folds the outputs it owns into per-row
-// keys, reduces them across its lanes and stores one key per row in its slot of the workspace;
-// argmax_finalize_kernel then takes the maximum over a row's slots and writes the column and the
-// fp32 value.
+// Fold. Each writer (a workgroup of the dot-product kernel, or a group of wavefronts of the
+// matrix-core kernels) folds the outputs it owns into per-row keys, reduces them across its lanes
+// and stores one key per row in its slot of the workspace; argmax_finalize_kernel then takes the
+// maximum over a row's slots and writes the column and the fp32 value.
 #pragma once
 
 #include "device.h"

@@ -541,7 +541,7 @@ hipError_t launch_impl(int path, int split, const GemmArgs &a0, int32_t *index, 
         if (e != hipSuccess)
             return e;
         if (argmax)
-            a.key_slots = grid * split;   // one key per wavefront
+            a.key_slots = grid;   // one key per workgroup
         if (a.key_slots > cap)
             return hipErrorInvalidValue;
         hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * split), lds, stream, a, L);

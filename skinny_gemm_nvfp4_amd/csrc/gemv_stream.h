@@ -360,10 +360,20 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
                 best = key_max(best, argmax_key(sum * g, c0 + c));
         }
         if (a.keys != nullptr) {
-            // Argmax mode: one key per row and wavefront, slot b W + wave of the row.
+            // Argmax mode: one key per row and workgroup (slot b of the row): the wavefronts'
+            // keys meet in LDS, so the finalize kernel reads one key per compute unit.
+            __shared__ argkey_t wkeys[W];
             best = key_max_64(best);
             if (lane == 0)
-                a.keys[(size_t)m * a.key_slots + b * W + wave] = best;
+                wkeys[wave] = best;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                argkey_t k = wkeys[0];
+                for (int w = 1; w < W; w++)
+                    k = key_max(k, wkeys[w]);
+                a.keys[(size_t)m * a.key_slots + b] = k;
+            }
+            __syncthreads();   // wkeys is reused by the next row
         }
     }
 }
