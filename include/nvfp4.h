@@ -160,7 +160,8 @@ typedef enum {
  *
  * Same operation, arguments, rules and results as nvfp4_gemm. `path` is an nvfp4_path_t.
  * `split` tunes the kernel (0 picks it like nvfp4_gemm):
- *   NVFP4_PATH_DOT: wavefronts per workgroup, 4, 8 or 16; M <= 8, else NVFP4_ERROR_INVALID_VALUE.
+ *   NVFP4_PATH_DOT: wavefronts per workgroup, 4, 8, 12 or 16; M <= 8, else
+ *     NVFP4_ERROR_INVALID_VALUE.
  *     If X does not fit in LDS (M * K too large) the call runs NVFP4_PATH_MFMA with its own split.
  *   NVFP4_PATH_MFMA: wavefronts per workgroup, 4 or 8.
  *   NVFP4_PATH_BATCH: 1, 2 or 4, the number of consumer wavefronts that share the K steps of one

@@ -63,7 +63,8 @@ nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const u
         return NVFP4_ERROR_INVALID_VALUE;
     if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_INVARIANT)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 16)
+    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 12 &&
+        split != 16)
         return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
         !aligned(Y, 4))
@@ -109,7 +110,8 @@ nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
         return NVFP4_ERROR_INVALID_VALUE;
     if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_INVARIANT)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 16)
+    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 12 &&
+        split != 16)
         return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
         !aligned(index, 4) || !aligned(value, 4) || !aligned(workspace, 8))

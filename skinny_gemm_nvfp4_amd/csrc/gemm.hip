@@ -34,21 +34,21 @@ typedef void (*StreamFn)(GemmArgs, StreamLayout);
 // o_proj and is even on gate_up and down; four rows: 2 vs 4 saves 1-1.8 us).
 constexpr int stream_depth(int rows) { return rows == 1 ? 3 : 2; }
 
-// Wavefronts per workgroup of the dot-product kernel when the caller leaves it open: 16, or 8
-// for one row when a workgroup has at most 128 units (512-k windows of a 4-column group) to
-// stream. Measured on the layer shapes with cold weights: q/k/v and o_proj (50-70 units) are
-// 0.2-0.4 us faster with 8; gate_up (340) and the lm_head (1480) 0.5-3 us slower; 4 is slower
-// everywhere.
+// Wavefronts per workgroup of the dot-product kernel when the caller leaves it open: 12 for one
+// row, 16 for more. Measured on the layer shapes and the lm_head at M = 1 with cold weights,
+// 12 against 16: gate_up 19.3 vs 20.5 us, down 11.5 vs 12.4, lm_head 72.1 vs 73.6, q/k/v and
+// o_proj 0.3 us faster (and within 0.1 us of 8); 4 is slower everywhere.
 int dot_default_waves(int rows, int N, int K);
 constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 constexpr int kDefaultLds = 64 * 1024;      // above this a kernel must opt in
 
-// ---- dot-product kernels: [FAST][MR - 1][wave index] ----
+// ---- dot-product kernels: [FAST][MR - 1][wave index: 4, 8, 16, 12] ----
 #define NVFP4_STREAM_WAVES(R, FAST)                                                        \
     {                                                                                      \
         &gemv_stream_kernel<R, 4, stream_depth(R), FAST>,                                  \
             &gemv_stream_kernel<R, 8, stream_depth(R), FAST>,                              \
-            &gemv_stream_kernel<R, 16, stream_depth(R), FAST>                              \
+            &gemv_stream_kernel<R, 16, stream_depth(R), FAST>,                             \
+            &gemv_stream_kernel<R, 12, stream_depth(R), FAST>                              \
     }
 #define NVFP4_STREAM_TABLE(FAST)                                                           \
     {                                                                                      \
@@ -57,7 +57,7 @@ constexpr int kDefaultLds = 64 * 1024;      // above this a kernel must opt in
             NVFP4_STREAM_WAVES(5, FAST), NVFP4_STREAM_WAVES(6, FAST),                      \
             NVFP4_STREAM_WAVES(7, FAST), NVFP4_STREAM_WAVES(8, FAST)                       \
     }
-const StreamFn kStream[2][8][3] = {NVFP4_STREAM_TABLE(false), NVFP4_STREAM_TABLE(true)};
+const StreamFn kStream[2][8][4] = {NVFP4_STREAM_TABLE(false), NVFP4_STREAM_TABLE(true)};
 
 // ---- matrix-core kernels: [FAST][TC index][wave index] ----
 // TC column tiles of 16 are processed together; the smallest TC >= the workgroup's tile count is
@@ -135,6 +135,7 @@ int wave_index(int waves)
     case 4: return 0;
     case 8: return 1;
     case 16: return 2;
+    case 12: return 3;
     default: return -1;
     }
 }
@@ -241,9 +242,9 @@ bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L,
 
 int dot_default_waves(int rows, int N, int K)
 {
-    const long long G = group_grid(N);
-    const long long units = (num_groups(N) + G - 1) / G * ((K + kStreamWindow - 1) / kStreamWindow);
-    return rows == 1 && units <= 128 ? 8 : 16;
+    (void)N;
+    (void)K;
+    return rows == 1 ? 12 : 16;
 }
 
 // Workgroups, column-tile chunk and LDS bytes of the matrix-core kernel.

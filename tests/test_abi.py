@@ -107,11 +107,14 @@ def test_gemm_path_rejects_bad_options(lib):
         assert nv.nvfp4_gemm_path(nv.PATH_INVARIANT, split, 16, 16, 256, *ptrs, None) == \
             nv.ERROR_INVALID_VALUE
     # the wave counts of the other kernels are 4, 8 or 16
-    for split in (1, 2):
+    for split in (1, 2, 12):
         assert nv.nvfp4_gemm_path(nv.PATH_MFMA, split, 16, 16, 256, *ptrs, None) == \
             nv.ERROR_INVALID_VALUE
-        assert nv.nvfp4_gemm_path(nv.PATH_DOT, split, 1, 16, 256, *ptrs, None) == \
-            nv.ERROR_INVALID_VALUE
+        if split != 12:   # 12 wavefronts is a dot-product kernel size
+            assert nv.nvfp4_gemm_path(nv.PATH_DOT, split, 1, 16, 256, *ptrs, None) == \
+                nv.ERROR_INVALID_VALUE
+    assert nv.nvfp4_gemm_path(nv.PATH_BATCH, 12, 128, 16, 256, *ptrs, None) == \
+        nv.ERROR_INVALID_VALUE
 
 
 def test_gemm_rejects_overflowing_sizes(lib):

@@ -15,7 +15,7 @@ from parity import (FINITE_SCALES, check_close, gpu_gemm, random_case, say, to_d
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [(nv.PATH_DOT, 4), (nv.PATH_DOT, 8), (nv.PATH_DOT, 16),
+PATHS = [(nv.PATH_DOT, 4), (nv.PATH_DOT, 8), (nv.PATH_DOT, 12), (nv.PATH_DOT, 16),
          (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
          (nv.PATH_BATCH, 1), (nv.PATH_BATCH, 2), (nv.PATH_BATCH, 4), (nv.PATH_AUTO, 0)]
 VALU_PATHS = (nv.PATH_DOT,)   # the dot-product kernel: M <= 8
