@@ -35,9 +35,11 @@ typedef void (*StreamFn)(GemmArgs, StreamLayout);
 constexpr int stream_depth(int rows) { return rows == 1 ? 3 : 2; }
 
 // Wavefronts per workgroup of the dot-product kernel when the caller leaves it open: 12 for one
-// row, 16 for more. Measured on the layer shapes and the lm_head at M = 1 with cold weights,
-// 12 against 16: gate_up 19.3 vs 20.5 us, down 11.5 vs 12.4, lm_head 72.1 vs 73.6, q/k/v and
-// o_proj 0.3 us faster (and within 0.1 us of 8); 4 is slower everywhere.
+// row, 16 for more. Measured on the layer shapes and the lm_head at M = 1 with cold weights
+// (medians of five interleaved runs), 12 against 16: gate_up 18.8 vs 19.5 us, down 11.2 vs 12.0,
+// lm_head 72.4 vs 73.0, q/k/v 6.7 vs 7.0, o_proj 6.2 vs 6.5 (8: within 0.1 us on the last two,
+// slower on the others); 4 is slower everywhere. Four units in flight instead of three gained
+// nothing at 12 wavefronts.
 int dot_default_waves(int rows, int N, int K);
 constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 constexpr int kDefaultLds = 64 * 1024;      // above this a kernel must opt in
