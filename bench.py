@@ -13,8 +13,9 @@ Protocol
   * The step is captured once per copy in a HIP graph; warmup replays, then exactly `steps`
     replays bracketed by torch.cuda.synchronize(), timed on the host clock.
   * Per-kernel durations: per GEMM, HIP graphs of back-to-back launches rotating over enough
-    cold copies (> 512 MB of weights), bracketed by HIP events on the stream the graphs run on;
-    the dominant kernel (gate/up) gives the roofline object.
+    cold copies (> 512 MB of weights), bracketed by HIP events on the stream the graphs run on,
+    the median of five such timed blocks; the dominant kernel (gate/up) gives the roofline
+    object.
   * The GPU output is checked against the oracle, and the oracle itself is timed on the host
     cores on the same layer (cpu_baseline).
   * "also": the verify shapes at M = 16 and M = 128, timed the same way (per-kernel events).
@@ -52,6 +53,25 @@ EQUIV_MODEL_GB = 17.9     # the page's checkpoint size, for the tokens/s-equival
 CALIBRATION_BYTES = 256 << 20
 COLD_BYTES = 512 << 20      # rotated weight bytes per timed GEMM: twice the Infinity Cache
 LAUNCHES_PER_GRAPH = 32
+TIMED_BLOCKS = 5            # per-call figures: median of this many timed blocks of replays
+
+
+def timed_replays(graph, replays: int, stream) -> float:
+    """Median over TIMED_BLOCKS blocks of the milliseconds per replay of `graph`, each block
+    `replays` replays bracketed by HIP events on `stream` (a single block can catch a slow
+    stretch: the first timing of a process runs slow, and blocks scatter by a few percent)."""
+    import torch
+    times = []
+    for _ in range(TIMED_BLOCKS):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / replays)
+    return sorted(times)[len(times) // 2]
 
 
 def log(msg: str) -> None:
@@ -155,15 +175,10 @@ class Layer:
             replays = max(1, -(-launches // LAUNCHES_PER_GRAPH))
             graph.replay()                     # warm
             torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(replays):
-                graph.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            out.append(1e3 * e0.elapsed_time(e1) / (replays * LAUNCHES_PER_GRAPH))
-            self.launches.extend([self.label(i)] * ((replays + 1) * LAUNCHES_PER_GRAPH))
+            ms = timed_replays(graph, replays, stream)
+            out.append(1e3 * ms / LAUNCHES_PER_GRAPH)
+            self.launches.extend([self.label(i)] *
+                                 ((TIMED_BLOCKS * replays + 1) * LAUNCHES_PER_GRAPH))
             del graph
         return out
 
@@ -286,8 +301,9 @@ def full_pass(dev, launches, reps: int):
 
 def graph_time_us(call, copies: int, launches: int, label: str, log_list) -> float:
     """Average duration of one call(c): a HIP graph of LAUNCHES_PER_GRAPH back-to-back calls
-    rotating over `copies` cold weight copies, replayed until about `launches` calls ran, HIP
-    events on the stream the graph runs on around the replays (as Layer.kernel_times_us)."""
+    rotating over `copies` cold weight copies, replayed in blocks of about `launches` calls, HIP
+    events on the stream the graph runs on around each block, the median block (as
+    Layer.kernel_times_us)."""
     import torch
     stream = torch.cuda.current_stream()
     call(0)                                    # eager first call: one-time set-up
@@ -299,16 +315,10 @@ def graph_time_us(call, copies: int, launches: int, label: str, log_list) -> flo
     replays = max(1, -(-launches // LAUNCHES_PER_GRAPH))
     graph.replay()                             # warm
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(replays):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    log_list.extend([label] * (1 + (replays + 1) * LAUNCHES_PER_GRAPH))
+    ms = timed_replays(graph, replays, stream)
+    log_list.extend([label] * (1 + (TIMED_BLOCKS * replays + 1) * LAUNCHES_PER_GRAPH))
     del graph
-    return 1e3 * e0.elapsed_time(e1) / (replays * LAUNCHES_PER_GRAPH)
+    return 1e3 * ms / LAUNCHES_PER_GRAPH
 
 
 def lm_head_argmax(dev, launches, steps: int):

@@ -205,10 +205,27 @@ bool bytes_fit(int N, int K, int grid, bool pair = false)
     return gmax * (long long)num_chunks(K) * kChunkCodeBytes < (1LL << 31);
 }
 
+// Workgroups per compute unit of the dot-product kernel: two for one row when a compute unit has
+// more than 128 units (512-k windows of a 4-column group) to stream, else one. Measured at M = 1
+// with 12 wavefronts per workgroup (medians of five interleaved runs), two against one: gate_up
+// 18.1 vs 18.8 us, down 10.9 vs 11.2, lm_head 71.9 vs 72.3; q/k/v and o_proj (50-70 units)
+// are slower with two (7.1 vs 6.7, 6.9 vs 6.1).
+constexpr int kStreamTwoWgUnits = 128;
+
+int stream_wg_per_cu(int M, int N, int K, bool pair)
+{
+    if (M != 1 || pair)
+        return 1;
+    const long long G = group_grid(N);
+    const long long units = (num_groups(N) + G - 1) / G * ((K + kStreamWindow - 1) / kStreamWindow);
+    return units > kStreamTwoWgUnits ? 2 : 1;
+}
+
 // Workgroups and LDS layout of the dot-product kernel; false if X does not fit in LDS.
 bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L, bool pair = false)
 {
-    const int G = group_grid(N, pair);
+    const int G = std::max(1, std::min(compute_units() * stream_wg_per_cu(M, N, K, pair),
+                                       num_groups(N) / (pair ? 2 : 1)));
     const int u = pair ? 2 : 1;   // groups are dealt in units of u
     L->nwin = (K + kStreamWindow - 1) / kStreamWindow;
     L->row_bytes = L->nwin * (kStreamWindow / 32) * kStreamSlot;

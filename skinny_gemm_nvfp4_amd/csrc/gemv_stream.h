@@ -5,7 +5,8 @@
 // reaches the HBM roof only if every compute unit keeps the same number of bytes in flight until
 // the very end, so the work is split evenly by construction instead of by tile count:
 //
-//   * One workgroup of W wavefronts per compute unit. With NG = q G + r 4-column groups,
+//   * One workgroup of W wavefronts per compute unit (two for one row of a large weight: the
+//     launcher's choice). With NG = q G + r 4-column groups,
 //     workgroup b owns q + (b < r) consecutive groups from b q + min(b, r), so all hold the same
 //     number of weight bytes (to within one group).
 //   * A unit is one (group, 512-k window) pair: 16 chunks of 32 k x 4 columns, 1 KB of codes in
