@@ -523,6 +523,7 @@ def tp8_shard(dev, launches, steps: int):
 
 
 def main() -> int:
+    global TIMED_BLOCKS
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -547,7 +548,11 @@ def main() -> int:
     ap.add_argument("--launch-log", default=None,
                     help="write the label of every GEMM dispatch, in order, to this file (for "
                          "matching a rocprofv3 kernel trace to the GEMMs)")
+    ap.add_argument("--timed-blocks", type=int, default=TIMED_BLOCKS,
+                    help="timed blocks per per-call figure (the median is reported); counter "
+                         "passes under a profiler use 1 to keep the dispatch count down")
     args = ap.parse_args()
+    TIMED_BLOCKS = max(1, args.timed_blocks)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
