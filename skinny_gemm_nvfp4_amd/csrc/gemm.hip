@@ -34,12 +34,14 @@ typedef void (*StreamFn)(GemmArgs, StreamLayout);
 // o_proj and is even on gate_up and down; four rows: 2 vs 4 saves 1-1.8 us).
 constexpr int stream_depth(int rows) { return rows == 1 ? 3 : 2; }
 
-// Wavefronts per workgroup of the dot-product kernel when the caller leaves it open: 12 for one
-// row, 16 for more. Measured on the layer shapes and the lm_head at M = 1 with cold weights
-// (medians of five interleaved runs), 12 against 16: gate_up 18.8 vs 19.5 us, down 11.2 vs 12.0,
-// lm_head 72.4 vs 73.0, q/k/v 6.7 vs 7.0, o_proj 6.2 vs 6.5 (8: within 0.1 us on the last two,
-// slower on the others); 4 is slower everywhere. Four units in flight instead of three gained
-// nothing at 12 wavefronts.
+// Wavefronts per workgroup of the dot-product kernel when the caller leaves it open: 12 for up to
+// four rows, 16 for two to four rows of an lm_head-sized weight (more than 1024 units per compute
+// unit) and for more rows. Measured with cold weights (medians of five interleaved runs), 12
+// against 16 at M = 1: gate_up 18.8 vs 19.5 us, down 11.2 vs 12.0, lm_head 72.4 vs 73.0, q/k/v
+// 6.7 vs 7.0, o_proj 6.2 vs 6.5 (8: within 0.1 us on the last two, slower on the others); at
+// M = 2 and 4: q/k/v 7.8 vs 8.0 and 10.5 vs 10.7, o_proj 6.9 vs 7.2 and 9.0 vs 9.4, gate_up and
+// down even, lm_head (two workgroups per CU) 75.8 vs 75.3 and 108.1 vs 105.1. 4 is slower
+// everywhere. Four units in flight instead of three gained nothing at 12 wavefronts.
 int dot_default_waves(int rows, int N, int K);
 constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 constexpr int kDefaultLds = 64 * 1024;      // above this a kernel must opt in
@@ -205,20 +207,29 @@ bool bytes_fit(int N, int K, int grid, bool pair = false)
     return gmax * (long long)num_chunks(K) * kChunkCodeBytes < (1LL << 31);
 }
 
+// Units (512-k windows of a 4-column group) a compute unit streams with one workgroup per CU.
+long long stream_units_per_cu(int N, int K)
+{
+    const long long G = group_grid(N);
+    return (num_groups(N) + G - 1) / G * ((K + kStreamWindow - 1) / kStreamWindow);
+}
+
 // Workgroups per compute unit of the dot-product kernel: two for one row when a compute unit has
-// more than 128 units (512-k windows of a 4-column group) to stream, else one. Measured at M = 1
-// with 12 wavefronts per workgroup (medians of five interleaved runs), two against one: gate_up
-// 18.1 vs 18.8 us, down 10.9 vs 11.2, lm_head 71.9 vs 72.3; q/k/v and o_proj (50-70 units)
-// are slower with two (7.1 vs 6.7, 6.9 vs 6.1).
+// more than 128 units to stream, two for two to four rows above 1024 units (the lm_head), else
+// one. Measured (medians of five interleaved runs), two against one: at M = 1 with 12 wavefronts
+// gate_up 18.1 vs 18.8 us, down 10.9 vs 11.2, lm_head 71.9 vs 72.3, while q/k/v and o_proj
+// (50-70 units) are slower with two (7.1 vs 6.7, 6.9 vs 6.1); at M = 2 and 4 with 16 wavefronts
+// lm_head 75.3 vs 76.8 and 105.1 vs 110.5, while gate_up is even and down (whose X fills more
+// than half the LDS) slower (17.0 vs 13.6 at M = 2).
 constexpr int kStreamTwoWgUnits = 128;
+constexpr int kStreamLargeUnits = 1024;
 
 int stream_wg_per_cu(int M, int N, int K, bool pair)
 {
-    if (M != 1 || pair)
+    if (pair || M > 4)
         return 1;
-    const long long G = group_grid(N);
-    const long long units = (num_groups(N) + G - 1) / G * ((K + kStreamWindow - 1) / kStreamWindow);
-    return units > kStreamTwoWgUnits ? 2 : 1;
+    const long long units = stream_units_per_cu(N, K);
+    return units > (M == 1 ? kStreamTwoWgUnits : kStreamLargeUnits) ? 2 : 1;
 }
 
 // Workgroups and LDS layout of the dot-product kernel; false if X does not fit in LDS.
@@ -261,9 +272,11 @@ bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L,
 
 int dot_default_waves(int rows, int N, int K)
 {
-    (void)N;
-    (void)K;
-    return rows == 1 ? 12 : 16;
+    if (rows == 1)
+        return 12;
+    if (rows > 4 || stream_units_per_cu(N, K) > kStreamLargeUnits)
+        return 16;
+    return 12;
 }
 
 // Workgroups, column-tile chunk and LDS bytes of the matrix-core kernel.
