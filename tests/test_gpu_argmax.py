@@ -169,10 +169,11 @@ def lm_head(device):
     return p, (Wq_o, Ws_o, g_o), gen
 
 
-@pytest.mark.parametrize("M", [1, 16, 128])
+@pytest.mark.parametrize("M", [1, 3, 16, 128])
 def test_lm_head_shape(device, lm_head, M):
-    """nvfp4_gemm_argmax's automatic path at the lm_head shape; the oracle on every column for
-    the first 8 rows."""
+    """nvfp4_gemm_argmax's automatic path at the lm_head shape (M = 3: the dot-product kernel
+    with two workgroups per compute unit; M = 16: the 16-row kernel's chunks of unequal tiles);
+    the oracle on every column for the first 8 rows."""
     p, (Wq_o, Ws_o, g_o), gen = lm_head
     X = inputs.activations(gen, M, inputs.LM_HEAD_SHAPE[0])
     say(f"lm_head argmax M={M}")
