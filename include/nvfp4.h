@@ -141,10 +141,13 @@ typedef enum {
                              workgroups: partial sums go to a workspace, a second kernel adds
                              them in slice order and applies g */
     NVFP4_PATH_INVARIANT = 5 /* batch-invariant mode: row m of Y is the same bits for every M
-                             and whatever the other rows of X hold, so a request verified
-                             alone or with others gets exactly what M = 1 decode gives it
-                             ("SparkInfer" README, speculative decoding sections: a request
-                             speculating alone is bit-identical to speculation off). The
+                             and whatever the other rows of X hold. A request verified alone
+                             or with others then gets exactly the bits its own M = 1 call in
+                             this mode gives it, which is what lets speculation leave the
+                             greedy tokens unchanged ("SparkInfer" README, speculative decoding
+                             sections). Every call that must agree, plain decode included, has
+                             to use this mode: nvfp4_gemm at M = 1 picks another kernel and
+                             other bits, and nvfp4_gemm_fused has no invariant mode. The
                              batch kernel with one plan per (N, K) for all M, the plan
                              nvfp4_gemm takes for 128 rows, K slices included; slower than
                              NVFP4_PATH_AUTO at small M. A split plan needs the workspace

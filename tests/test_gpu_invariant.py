@@ -1,8 +1,8 @@
 """Batch-invariant mode (NVFP4_PATH_INVARIANT) through the C ABI.
 
-The property ("SparkInfer" README, speculative decoding sections: a request speculating alone is
-bit-identical to speculation off): row m of Y is the same bits whatever M is and whatever the
-other rows of X hold. Checked bit for bit between calls of the HIP path on the same seeded
+The property (the "SparkInfer" README's speculative decoding sections promise that a request which
+speculates alone produces exactly the tokens it would produce with speculation disabled): row m of
+Y is the same bits whatever M is and whatever the other rows of X hold. Checked bit for bit between calls of the HIP path on the same seeded
 inputs (any number of rows, rows at any offset, 128-row slab boundaries, other rows replaced), and
 every call against the oracle within |Y - Y_ref| <= 2e-3 * sum|x*w| + 1e-6.
 """
