@@ -468,10 +468,13 @@ def fused_neighbours(dev, launches, steps: int):
             def plain(c, X=X, Y=Y, packs=packs):
                 nv.gemm(X, *packs[c], out=Y)
 
-            def fused(c, X=X, O=O, packs=packs, N=N, silu=silu):
+            ws = nv.fused_workspace(nv.FUSE_RMSNORM | (nv.FUSE_SILU_MUL if silu else 0), M, N,
+                                    K, dev)
+
+            def fused(c, X=X, O=O, packs=packs, N=N, silu=silu, ws=ws):
                 p = packs[c]
                 nv.gemm_fused(X, p.Wq, p.Ws, p.g, N, gamma=gamma, eps=inputs.RMSNORM_EPS,
-                              silu_mul=silu, out=O)
+                              silu_mul=silu, out=O, workspace=ws)
 
             lab = f"fused.{name} M={M} N={N} K={K}"
             pus = graph_time_us(plain, copies, max(64, steps), f"{lab} plain", launches)
@@ -484,9 +487,11 @@ def fused_neighbours(dev, launches, steps: int):
                 "M": M, "N": N, "K": K, "fused_us": round(fus, 3), "plain_gemm_us": round(pus, 3),
                 "fused_bytes": fbytes, "fused_GB_s": round(gbs, 1),
                 "fused_pct_hbm_peak": round(100 * gbs / rl.HBM_PEAK_GBS, 2),
-                # the round trips a separate RMSNorm (bf16 xhat) and SiLU * up (fp32 gate/up)
-                # kernel would add
-                "bytes_not_moved": (8 * M * N + 4 * M * K) if silu else 4 * M * K}
+                # the round trips a separate SiLU * up kernel (fp32 gate/up) would add, and a
+                # separate RMSNorm kernel's bf16 xhat where the call normalises X in LDS
+                "bytes_not_moved": (8 * M * N if silu else 0) +
+                                   (4 * M * K if ws is None else 0),
+                "workspace_bytes": 0 if ws is None else ws.numel()}
         del packs
         torch.cuda.empty_cache()
     return out

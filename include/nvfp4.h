@@ -43,13 +43,10 @@
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer owned by the caller; the library keeps none of them past
  *     the call.
- *   - Device memory of the library's own: only the split-K workspace of the batch kernel (K cut
- *     across workgroups for narrow shapes at M > 16): one buffer per device, allocated by the
- *     first call that needs it, grown when a call needs more, never freed before the process ends
- *     (a captured graph may still use it). A call that would have to allocate while its stream is
- *     being captured runs without split K instead; run one such call eagerly first.
- *     Because the workspace is shared, calls that may split K (M > 16, NVFP4_PATH_BATCH_SPLITK or
- *     NVFP4_PATH_INVARIANT) must not run concurrently on different streams of the same device.
+ *   - The library owns no device memory: every partial sum stays inside a workgroup (in
+ *     registers and LDS), and the entry points that need scratch memory take it from the caller
+ *     (nvfp4_gemm_argmax, nvfp4_gemm_fused), so a call never allocates, and calls on different
+ *     streams or host threads never share memory unless the caller gives them the same buffers.
  *   - Sizes: 1 <= M, 1 <= N, 16 <= K <= 4194304 (2^22), K % 16 == 0, and every array must have
  *     fewer than 2^62 bytes. Anything else returns NVFP4_ERROR_INVALID_VALUE.
  *   - Alignment: X, Wq, Wscale and W must be 16-byte aligned, Y and gscale 4-byte aligned;
@@ -60,11 +57,11 @@
  *   - Calls are stream-ordered on `stream` (a hipStream_t; NULL is the null stream) and never
  *     synchronise. A failed kernel launch returns NVFP4_ERROR_LAUNCH; faults during execution
  *     surface at the caller's next synchronisation, as for any HIP kernel.
- *   - Results are deterministic: the same inputs give the same bits on every call. (The one
- *     exception: a call that runs without split K for want of a workspace under capture, as
- *     above, may differ from the split-K result in the last bits.)
- *   - Calls are re-entrant and thread-safe on the host. The only mutable global state is the
- *     workspace table, behind a mutex.
+ *   - Results are deterministic: the same inputs give the same bits on every call, on any
+ *     stream, eagerly or inside a captured graph.
+ *   - Calls are re-entrant and thread-safe on the host. The only mutable global state is a
+ *     per-device cache of the compute-unit count and of which kernels were allowed more LDS,
+ *     both behind atomics or a mutex.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -124,22 +121,20 @@ nvfp4_status_t nvfp4_gemm(int M, int N, int K, const uint16_t *X, const uint8_t 
                           const uint8_t *Wscale, const float *gscale, float *Y, void *stream);
 
 /* Kernel families nvfp4_gemm chooses between (for nvfp4_gemm_path). All are persistent: one
- * workgroup per compute unit (and per 16-row block of X for NVFP4_PATH_MFMA), each with an equal
- * share of the 4-column groups. nvfp4_gemm takes DOT for M <= 4, MFMA for M <= 16 and BATCH
- * above. */
+ * workgroup per compute unit (per 16-row block of X for NVFP4_PATH_MFMA; per row group and tile
+ * set for NVFP4_PATH_BATCH), each with an equal share of the 4-column groups. nvfp4_gemm takes
+ * DOT for M <= 4, MFMA for M <= 16 (and narrow weights up to M = 48) and BATCH above. */
 typedef enum {
     NVFP4_PATH_AUTO = 0,  /* what nvfp4_gemm does */
     NVFP4_PATH_DOT = 1,   /* VALU: E2M1->bf16 decode, v_dot2_f32_bf16 against X staged in LDS,
                              fp32 partial * s; M <= 8 */
     NVFP4_PATH_MFMA = 2,  /* matrix cores: E2M1*s decoded to bf16, v_mfma_f32_16x16x32_bf16 on
                              one 16-row block of X per workgroup; any M */
-    NVFP4_PATH_BATCH = 3, /* matrix cores, every weight decoded once per 128-row slab of X:
-                             loader wavefronts stage X and the weights in LDS, four consumer
-                             wavefronts decode and multiply; any M, meant for M > 16. It may cut
-                             K across workgroups (see below) */
-    NVFP4_PATH_BATCH_SPLITK = 4, /* NVFP4_PATH_BATCH with K cut into `split` slices across
-                             workgroups: partial sums go to a workspace, a second kernel adds
-                             them in slice order and applies g */
+    NVFP4_PATH_BATCH = 3, /* matrix cores, every weight decoded once per workgroup for slabs of
+                             up to 128 rows of X: X, codes and scales staged in LDS by
+                             direct-to-LDS loads, four wavefronts splitting each tile's k-steps;
+                             narrow weights cut the rows into row groups. Any M, meant for
+                             M > 16. (Value 4 is not a path.) */
     NVFP4_PATH_INVARIANT = 5 /* batch-invariant mode: row m of Y is the same bits for every M
                              and whatever the other rows of X hold. A request verified alone
                              or with others then gets exactly the bits its own M = 1 call in
@@ -147,15 +142,10 @@ typedef enum {
                              greedy tokens unchanged ("SparkInfer" README, speculative decoding
                              sections). Every call that must agree, plain decode included, has
                              to use this mode: nvfp4_gemm at M = 1 picks another kernel and
-                             other bits, and nvfp4_gemm_fused has no invariant mode. The
-                             batch kernel with one plan per (N, K) for all M, the plan
-                             nvfp4_gemm takes for 128 rows, K slices included; slower than
-                             NVFP4_PATH_AUTO at small M. A split plan needs the workspace
-                             (above) sized for 128 rows: a call under stream capture that
-                             would have to grow it returns NVFP4_ERROR_LAUNCH and launches
-                             nothing (there is no unsplit fallback, which would change the
-                             bits), so run one call per shape before capturing. split must be
-                             0. */
+                             other bits, and nvfp4_gemm_fused has no invariant mode. The slab
+                             kernel with one plan per (N, K) for all M, the plan nvfp4_gemm
+                             takes for 128 rows; slower than NVFP4_PATH_AUTO at small M.
+                             split must be 0. */
 } nvfp4_path_t;
 
 /*
@@ -167,9 +157,8 @@ typedef enum {
  *     NVFP4_ERROR_INVALID_VALUE.
  *     If X does not fit in LDS (M * K too large) the call runs NVFP4_PATH_MFMA with its own split.
  *   NVFP4_PATH_MFMA: wavefronts per workgroup, 4 or 8.
- *   NVFP4_PATH_BATCH: 1, 2 or 4, the number of consumer wavefronts that share the K steps of one
- *     column tile (4 / split tiles are processed side by side).
- *   NVFP4_PATH_BATCH_SPLITK: 2, 4 or 8 K slices (at most one per 128 k).
+ *   NVFP4_PATH_BATCH: rows per row group, 16, 32, 64 or 128 (the rows of a 128-row slab are
+ *     cut into groups of that many, each with its own workgroups).
  *   NVFP4_PATH_INVARIANT: 0 only.
  * Any other value returns NVFP4_ERROR_INVALID_VALUE.
  */
@@ -204,7 +193,7 @@ nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const u
  *              undefined. Calls that overlap in time must not share a workspace.
  *   workspace_bytes  its size; smaller than required returns NVFP4_ERROR_INVALID_VALUE
  *   stream     hipStream_t
- * Errors as for nvfp4_gemm. The split-K workspace rules of the batch kernel (above) apply too.
+ * Errors as for nvfp4_gemm.
  */
 nvfp4_status_t nvfp4_gemm_argmax(int M, int N, int K, const uint16_t *X, const uint8_t *Wq,
                                  const uint8_t *Wscale, const float *gscale, int32_t *index,
@@ -221,8 +210,7 @@ nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
 
 /* Workspace bytes nvfp4_gemm_argmax needs for M rows on the current device:
  * 8 * 16 * (compute units) per row (room for 16 8-byte keys per compute unit; the kernels write
- * at most 4 per compute unit, or 256 per row after a K-split reduce);
- * 0 if M < 1. */
+ * at most 4 per compute unit); 0 if M < 1. */
 uint64_t nvfp4_argmax_workspace_bytes(int M);
 
 /*
@@ -294,22 +282,29 @@ nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
  *   eps      RMSNorm epsilon, finite and >= 0 (e.g. 1e-6)
  *   out      out: fp32 Y [M][N] (4-byte aligned) without NVFP4_FUSE_SILU_MUL, bf16 bits
  *            H [M][N / 2] (2-byte aligned) with it; device
+ *   workspace  scratch owned by the caller: at least nvfp4_fused_workspace_bytes(fuse, M, N, K)
+ *              bytes of device memory, 16-byte aligned (NULL when that is 0); its contents on
+ *              entry do not matter and are left undefined. Calls that overlap in time must not
+ *              share a workspace.
+ *   workspace_bytes  its size; smaller than required returns NVFP4_ERROR_INVALID_VALUE
  * Kernels: up to 4 rows the dot-product kernel does everything (X normalised once in LDS, the
- * epilogue on its column sums). Above, RMSNorm is a row-wise kernel of its own writing the bf16
- * xhat to a library workspace; then the 16-row matrix-core kernel with the SiLU(gate) * up
- * epilogue inside (M <= 16), or the GEMM nvfp4_gemm runs (each weight read once per 128 rows)
- * followed by an elementwise SiLU(gate) * up kernel (M > 16). The workspace (M*K*2 + M*N*4
- * bytes at most, per device) is allocated by the first call that needs it and never freed;
- * under stream capture a call that would have to grow it returns NVFP4_ERROR_LAUNCH, so run one
- * call per shape eagerly first; such calls must not overlap on different streams of a device.
- * Errors as for nvfp4_gemm.
+ * epilogue on its column sums; no workspace). Above, RMSNorm is a row-wise kernel of its own
+ * writing the bf16 xhat to the workspace (normalising X inside the matrix-core kernels would
+ * repeat it in every workgroup); then the 16-row matrix-core kernel (M <= 16) or the slab kernel
+ * (M > 16), each with the SiLU(gate) * up epilogue inside, so the fp32 gate/up output is never
+ * written. Errors as for nvfp4_gemm.
  */
 enum { NVFP4_FUSE_RMSNORM = 1, NVFP4_FUSE_SILU_MUL = 2 };
 
 nvfp4_status_t nvfp4_gemm_fused(int fuse, int M, int N, int K, const uint16_t *X,
                                 const uint16_t *gamma, float eps, const uint8_t *Wq,
                                 const uint8_t *Wscale, const float *gscale, void *out,
-                                void *stream);
+                                void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* Workspace bytes nvfp4_gemm_fused needs for these arguments on the current device: 0 when one
+ * kernel does everything (no RMSNorm, or up to 4 rows whose X fits in LDS), else the normalised
+ * X, M * K * 2 bytes rounded up to 256. 0 for arguments nvfp4_gemm_fused would reject. */
+uint64_t nvfp4_fused_workspace_bytes(int fuse, int M, int N, int K);
 
 /* Bytes of Wq for an N x K weight: 64 * ceil(N/4) * ceil(K/32); 0 if N < 1 or K < 1. */
 uint64_t nvfp4_codes_bytes(int N, int K);
@@ -321,7 +316,7 @@ uint64_t nvfp4_scales_bytes(int N, int K);
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define NVFP4_ABI_VERSION 5
+#define NVFP4_ABI_VERSION 6
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

@@ -22,8 +22,7 @@ ERROR_LAUNCH = 3
 PATH_AUTO = 0
 PATH_DOT = 1
 PATH_MFMA = 2
-PATH_BATCH = 3
-PATH_BATCH_SPLITK = 4
+PATH_BATCH = 3       # split: rows per row group, 16, 32, 64 or 128 (0: chosen)
 PATH_INVARIANT = 5   # row m of Y is the same bits for every M
 
 FUSE_RMSNORM = 1     # nvfp4_gemm_fused: RMSNorm of X before the GEMM
@@ -70,8 +69,11 @@ def load_library() -> ctypes.CDLL:
     L.nvfp4_argmax_workspace_bytes.restype = ctypes.c_uint64
     L.nvfp4_gemm_grouped.argtypes = [ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, ci, vp]
     L.nvfp4_gemm_grouped.restype = ci
-    L.nvfp4_gemm_fused.argtypes = [ci, ci, ci, ci, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp]
+    L.nvfp4_gemm_fused.argtypes = [ci, ci, ci, ci, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+                                   ctypes.c_uint64, vp]
     L.nvfp4_gemm_fused.restype = ci
+    L.nvfp4_fused_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    L.nvfp4_fused_workspace_bytes.restype = ctypes.c_uint64
     L.nvfp4_status_string.argtypes = [ci]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_abi_version.argtypes = []
@@ -135,9 +137,14 @@ def nvfp4_gemm_grouped(T: int, E: int, N: int, K: int, X: int, offsets: int, Wq:
 
 
 def nvfp4_gemm_fused(fuse: int, M: int, N: int, K: int, X: int, gamma: int, eps: float,
-                     Wq: int, Wscale: int, gscale: int, out: int, stream: Optional[int]) -> int:
+                     Wq: int, Wscale: int, gscale: int, out: int, workspace: int,
+                     workspace_bytes: int, stream: Optional[int]) -> int:
     return load_library().nvfp4_gemm_fused(fuse, M, N, K, X, gamma, eps, Wq, Wscale, gscale,
-                                           out, stream)
+                                           out, workspace, workspace_bytes, stream)
+
+
+def nvfp4_fused_workspace_bytes(fuse: int, M: int, N: int, K: int) -> int:
+    return load_library().nvfp4_fused_workspace_bytes(fuse, M, N, K)
 
 
 def nvfp4_codes_bytes(N: int, K: int) -> int:
@@ -328,12 +335,22 @@ def interleave_gate_up(W: torch.Tensor) -> torch.Tensor:
     return torch.stack([g, u], dim=2).reshape(K, N2).contiguous()
 
 
+def fused_workspace(fuse: int, M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
+    """A device buffer of nvfp4_fused_workspace_bytes (None when the call needs none)."""
+    n = nvfp4_fused_workspace_bytes(fuse, M, N, K)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def gemm_fused(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Tensor, N: int,
                gamma: Optional[torch.Tensor] = None, eps: float = 1e-6, silu_mul: bool = False,
-               stream=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               stream=None, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The GEMM with its layer neighbours: RMSNorm(X; gamma, eps) first when gamma is given, and
     SiLU(gate) * up of an interleaved gate/up weight (interleave_gate_up) when silu_mul. Returns
-    fp32 Y [M, N], or bf16 H [M, N/2] with silu_mul."""
+    fp32 Y [M, N], or bf16 H [M, N/2] with silu_mul. `workspace` (device bytes) is allocated here
+    when the call needs one and none is given."""
     M, K = X.shape
     _check_device(X, "X", torch.bfloat16, (M, K))
     _check_device(Wq, "Wq", torch.uint8, codes_shape(N, K))
@@ -352,9 +369,16 @@ def gemm_fused(X: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor, g: torch.Ten
         out = torch.empty(shape, dtype=dtype, device=X.device)
     else:
         _check_device(out, "out", dtype, shape)
+    if workspace is None:
+        workspace = fused_workspace(fuse, M, N, K, X.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = nvfp4_gemm_fused(fuse, M, N, K, X.data_ptr(), 0 if gamma is None else gamma.data_ptr(),
                           float(eps), Wq.data_ptr(), Ws.data_ptr(), g.data_ptr(), out.data_ptr(),
-                          _stream(stream))
+                          ws_ptr, ws_bytes, _stream(stream))
     if st != SUCCESS:
         raise NVFP4Error(st, "nvfp4_gemm_fused")
     return out

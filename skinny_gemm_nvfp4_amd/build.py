@@ -11,6 +11,9 @@ Flags that matter for results:
         recipe rounds every fp32 step on its own.
   -fhip-fp32-correctly-rounded-divide-sqrt
         fp32 division is correctly rounded (the recipe divides twice).
+  -mllvm -amdgpu-mfma-vgpr-form
+        matrix-core accumulators in ordinary VGPRs: without it the compiler moves the 16x16
+        accumulators through AGPRs with copies around every MFMA of the unrolled tile loops.
 """
 from __future__ import annotations
 
@@ -41,6 +44,7 @@ def compile_flags() -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

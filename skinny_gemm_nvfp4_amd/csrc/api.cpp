@@ -31,6 +31,15 @@ bool sizes_ok(long long M, long long N, long long K)
     return m * k * 2ULL < kMaxBytes && n * k * 4ULL < kMaxBytes && m * n * 4ULL < kMaxBytes;
 }
 
+// Values `split` may take for any path (each path accepts a subset, checked when it is chosen).
+bool split_ok(int split)
+{
+    switch (split) {
+    case 0: case 4: case 8: case 12: case 16: case 32: case 64: case 128: return true;
+    default: return false;
+    }
+}
+
 nvfp4_status_t from_hip(hipError_t e)
 {
     return e == hipSuccess ? NVFP4_SUCCESS : NVFP4_ERROR_LAUNCH;
@@ -63,8 +72,7 @@ nvfp4_status_t nvfp4_gemm_path(int path, int split, int M, int N, int K, const u
         return NVFP4_ERROR_INVALID_VALUE;
     if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_INVARIANT)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 12 &&
-        split != 16)
+    if (!split_ok(split))
         return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
         !aligned(Y, 4))
@@ -110,8 +118,7 @@ nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
         return NVFP4_ERROR_INVALID_VALUE;
     if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_INVARIANT)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (split != 0 && split != 1 && split != 2 && split != 4 && split != 8 && split != 12 &&
-        split != 16)
+    if (!split_ok(split))
         return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
         !aligned(index, 4) || !aligned(value, 4) || !aligned(workspace, 8))
@@ -183,10 +190,18 @@ nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
     return from_hip(nvfp4::launch_grouped(a, mr, static_cast<hipStream_t>(stream)));
 }
 
+uint64_t nvfp4_fused_workspace_bytes(int fuse, int M, int N, int K)
+{
+    if (fuse < 1 || fuse > (NVFP4_FUSE_RMSNORM | NVFP4_FUSE_SILU_MUL) || !sizes_ok(M, N, K))
+        return 0;
+    return nvfp4::fused_workspace_bytes((fuse & NVFP4_FUSE_RMSNORM) != 0,
+                                        (fuse & NVFP4_FUSE_SILU_MUL) != 0, M, N, K);
+}
+
 nvfp4_status_t nvfp4_gemm_fused(int fuse, int M, int N, int K, const uint16_t *X,
                                 const uint16_t *gamma, float eps, const uint8_t *Wq,
                                 const uint8_t *Wscale, const float *gscale, void *out,
-                                void *stream)
+                                void *workspace, uint64_t workspace_bytes, void *stream)
 {
     if (fuse < 1 || fuse > (NVFP4_FUSE_RMSNORM | NVFP4_FUSE_SILU_MUL))
         return NVFP4_ERROR_INVALID_VALUE;
@@ -198,8 +213,12 @@ nvfp4_status_t nvfp4_gemm_fused(int fuse, int M, int N, int K, const uint16_t *X
         return NVFP4_ERROR_INVALID_VALUE;
     if (!X || !Wq || !Wscale || !gscale || !out || (norm && !gamma))
         return NVFP4_ERROR_INVALID_VALUE;
+    const uint64_t need = nvfp4_fused_workspace_bytes(fuse, M, N, K);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return NVFP4_ERROR_INVALID_VALUE;
     if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
-        (norm && !aligned(gamma, 16)) || !aligned(out, silu ? 2 : 4))
+        (norm && !aligned(gamma, 16)) || !aligned(out, silu ? 2 : 4) ||
+        (need > 0 && !aligned(workspace, 16)))
         return NVFP4_ERROR_MISALIGNED;
     nvfp4::GemmArgs a;
     a.X = X;
@@ -213,6 +232,8 @@ nvfp4_status_t nvfp4_gemm_fused(int fuse, int M, int N, int K, const uint16_t *X
     a.M = M;
     a.N = N;
     a.K = K;
+    a.workspace = need > 0 ? workspace : nullptr;
+    a.workspace_bytes = need > 0 ? (size_t)workspace_bytes : 0;
     return from_hip(nvfp4::launch_gemm_fused(a, static_cast<hipStream_t>(stream)));
 }
 

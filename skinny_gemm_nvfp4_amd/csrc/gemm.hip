@@ -6,18 +6,18 @@
 //     the smallest M.
 //   * mfma_stream.h (NVFP4_PATH_MFMA): bf16 matrix cores on 16-row blocks of X (speculative
 //     verification of one request), and every shape whose X does not fit in LDS.
-//   * mfma_batch.h (NVFP4_PATH_BATCH): bf16 matrix cores, each weight decoded once for up to 128
-//     rows of X (verification of several requests together).
+//   * mfma_slab.h (NVFP4_PATH_BATCH): bf16 matrix cores, each weight decoded once per workgroup
+//     for slabs of up to 128 rows of X (verification of several requests together).
+// None of them needs memory beyond the caller's arrays: every partial sum stays in a workgroup.
 #include <algorithm>
 #include <atomic>
-#include <map>
 #include <mutex>
 #include <set>
 #include <utility>
 
 #include "gemv_stream.h"
 #include "launch.h"
-#include "mfma_batch.h"
+#include "mfma_slab.h"
 #include "mfma_stream.h"
 #include "neighbours.h"
 
@@ -78,60 +78,36 @@ const int kMfmaTiles[6] = {1, 2, 3, 4, 6, 9};
     }
 const KernelFn kMfma[2][6][2] = {NVFP4_MFMA_TABLE(false), NVFP4_MFMA_TABLE(true)};
 
-// ---- batch kernels: [TCW - 1][MB index: 1, 2, 4, 8 row blocks][KS index: 1, 2, 4] ----
-// (second index of kBatchAll: 0 stores Y, 1 folds it into argmax keys)
-#define NVFP4_BATCH_KS(TCW, MB, A)                                                         \
-    {                                                                                      \
-        &mfma_batch_kernel<TCW, MB, 1, 0, A>, &mfma_batch_kernel<TCW, MB, 2, 0, A>,        \
-            &mfma_batch_kernel<TCW, MB, 4, 0, A>                                           \
+// ---- slab kernels: [MODE][RB index: 1, 2, 4, 8 row blocks][HT - 1][NR] ----
+constexpr int kSlabMaxHT = 4;   // at most 2 * 4 + 1 = 9 tiles per pass
+#define NVFP4_SLAB_NR(RB, HT, MODE)                                                         \
+    {                                                                                       \
+        &mfma_slab_kernel<RB, HT, 0, MODE>, &mfma_slab_kernel<RB, HT, 1, MODE>              \
     }
-#define NVFP4_BATCH_MB(TCW, A)                                                             \
-    {                                                                                      \
-        NVFP4_BATCH_KS(TCW, 1, A), NVFP4_BATCH_KS(TCW, 2, A), NVFP4_BATCH_KS(TCW, 4, A),   \
-            NVFP4_BATCH_KS(TCW, 8, A)                                                      \
+#define NVFP4_SLAB_HT(RB, MODE)                                                             \
+    {                                                                                       \
+        NVFP4_SLAB_NR(RB, 1, MODE), NVFP4_SLAB_NR(RB, 2, MODE), NVFP4_SLAB_NR(RB, 3, MODE),  \
+            NVFP4_SLAB_NR(RB, 4, MODE)                                                      \
     }
-const KernelFn kBatchAll[2][3][4][3] = {
-    {NVFP4_BATCH_MB(1, false), NVFP4_BATCH_MB(2, false), NVFP4_BATCH_MB(3, false)},
-    {NVFP4_BATCH_MB(1, true), NVFP4_BATCH_MB(2, true), NVFP4_BATCH_MB(3, true)}};
-
-template <int TCW, int MB, int KS>
-constexpr int batch_lds()
-{
-    return BatchShape<TCW, MB, KS>::LDS;
-}
-#define NVFP4_BATCH_LDS_KS(TCW, MB)                                                        \
-    {                                                                                      \
-        batch_lds<TCW, MB, 1>(), batch_lds<TCW, MB, 2>(), batch_lds<TCW, MB, 4>()          \
+#define NVFP4_SLAB_RB(MODE)                                                                 \
+    {                                                                                       \
+        NVFP4_SLAB_HT(1, MODE), NVFP4_SLAB_HT(2, MODE), NVFP4_SLAB_HT(4, MODE),             \
+            NVFP4_SLAB_HT(8, MODE)                                                          \
     }
-#define NVFP4_BATCH_LDS_MB(TCW)                                                            \
-    {                                                                                      \
-        NVFP4_BATCH_LDS_KS(TCW, 1), NVFP4_BATCH_LDS_KS(TCW, 2), NVFP4_BATCH_LDS_KS(TCW, 4), \
-            NVFP4_BATCH_LDS_KS(TCW, 8)                                                     \
+typedef void (*SlabFn)(GemmArgs, SlabLayout);
+const SlabFn kSlab[3][4][kSlabMaxHT][2] = {NVFP4_SLAB_RB(kSlabStore), NVFP4_SLAB_RB(kSlabArgmax),
+                                           NVFP4_SLAB_RB(kSlabSilu)};
+#define NVFP4_SLAB_LDS_HT(RB, HT)                                                           \
+    {                                                                                       \
+        SlabShape<RB, HT, 0>::LDS, SlabShape<RB, HT, 1>::LDS                                \
     }
-constexpr int kBatchLds[3][4][3] = {NVFP4_BATCH_LDS_MB(1), NVFP4_BATCH_LDS_MB(2),
-                                    NVFP4_BATCH_LDS_MB(3)};
-
-// ---- batch kernels with remainder tiles (KS = 1): [(TCW, NR) index][MB index] ----
-constexpr int kBatchNrCombos = 3;
-constexpr int kBatchNrTcw[kBatchNrCombos] = {1, 1, 2};
-constexpr int kBatchNrNr[kBatchNrCombos] = {1, 2, 1};
-#define NVFP4_BATCH_NR_MB(TCW, NR, A)                                                      \
-    {                                                                                      \
-        &mfma_batch_kernel<TCW, 1, 1, NR, A>, &mfma_batch_kernel<TCW, 2, 1, NR, A>,        \
-            &mfma_batch_kernel<TCW, 4, 1, NR, A>, &mfma_batch_kernel<TCW, 8, 1, NR, A>     \
+#define NVFP4_SLAB_LDS_RB(RB)                                                               \
+    {                                                                                       \
+        NVFP4_SLAB_LDS_HT(RB, 1), NVFP4_SLAB_LDS_HT(RB, 2), NVFP4_SLAB_LDS_HT(RB, 3),       \
+            NVFP4_SLAB_LDS_HT(RB, 4)                                                        \
     }
-const KernelFn kBatchNrAll[2][kBatchNrCombos][4] = {
-    {NVFP4_BATCH_NR_MB(1, 1, false), NVFP4_BATCH_NR_MB(1, 2, false),
-     NVFP4_BATCH_NR_MB(2, 1, false)},
-    {NVFP4_BATCH_NR_MB(1, 1, true), NVFP4_BATCH_NR_MB(1, 2, true),
-     NVFP4_BATCH_NR_MB(2, 1, true)}};
-#define NVFP4_BATCH_NR_LDS(TCW, NR)                                                        \
-    {                                                                                      \
-        BatchShape<TCW, 1, 1, NR>::LDS, BatchShape<TCW, 2, 1, NR>::LDS,                    \
-            BatchShape<TCW, 4, 1, NR>::LDS, BatchShape<TCW, 8, 1, NR>::LDS                 \
-    }
-constexpr int kBatchNrLds[kBatchNrCombos][4] = {NVFP4_BATCH_NR_LDS(1, 1), NVFP4_BATCH_NR_LDS(1, 2),
-                                                NVFP4_BATCH_NR_LDS(2, 1)};
+constexpr int kSlabLds[4][kSlabMaxHT][2] = {NVFP4_SLAB_LDS_RB(1), NVFP4_SLAB_LDS_RB(2),
+                                            NVFP4_SLAB_LDS_RB(4), NVFP4_SLAB_LDS_RB(8)};
 
 int wave_index(int waves)
 {
@@ -314,168 +290,123 @@ int mfma_default_waves(int N, int K)
     return kMfmaTiles[P.tc_index] >= 6 ? 4 : 8;
 }
 
-// Batch kernel for one slab of `rows` <= 128 rows: row blocks MB (1, 2, 4 or 8), tiles per
-// consumer TCW and step split KS (ks_req unless 0), from a cycle estimate per compute unit. A
-// window costs the slowest of: the busiest consumer's MFMAs (16 cycles each) or decode (about 80
-// VALU cycles per tile and step); the X bytes from L2 (64 bytes per cycle); the LDS traffic (128
-// bytes per cycle); the weight bytes at the compute unit's share of HBM (13 bytes per cycle); and
-// the load latency spread over the windows in flight (about 4000 cycles / 4). Every pass also
-// pays one latency to fill the pipeline.
-constexpr double kLoadLatency = 4000.0;
-
-struct BatchPlan {
-    int tcw, mbi, ksi, mb, grid, lds;
-    int nr;       // remainder tiles per pass (KS = 1 only), 0 for none
-    int nri;      // index into kBatchNr when nr > 0
-    int nslice;   // K slices across workgroups (split K), 1 for none
+// Slab kernel plan for a slab of `rows` <= 128 rows: row groups of RG = 16 RB rows, tile sets,
+// tiles per pass (TW = 2 HT + NR) and passes, from a cycle estimate per compute unit and window
+// (128 k). A window costs the slowest of: a consumer's MFMAs (about 17 cycles each, plus a fifth
+// for the decode of its B fragments, measured with interleaved decode on gfx950); the X and weight
+// bytes through the compute unit's L2 port (64 bytes per cycle); the LDS traffic (128 bytes per
+// cycle: the staged window, plus every consumer's A fragments of its two k-steps); the weight
+// bytes at the compute unit's share of HBM (13 bytes per cycle, counting each weight once per
+// tile set: the row groups of a set share an XCD and its L2). Each pass also pays one pipeline
+// fill (about 4000 cycles).
+struct SlabPlan {
+    int rbi, rb;    // row blocks of a row group: index into 1, 2, 4, 8, and the count
+    int rg;         // rows per row group: 16 * (the plan's row blocks), before trimming to the slab
+    int P, S;       // row groups, tile sets
+    int ht, nr;     // tiles per pass: 2 ht + nr
+    int passes;
+    int lds;
+    int gunit;
 };
 
-// Cycle estimate of one pass window (see batch_plan) for `units` tile-steps per consumer.
-double batch_window_cost(int units, int MB, int KS, int pt)
+constexpr double kSlabFill = 4000.0;
+
+int rb_index(int rb) { return rb <= 1 ? 0 : rb <= 2 ? 1 : rb <= 4 ? 2 : 3; }
+
+// Row blocks the kernel takes for a group of `rows` rows: the next power of two of rows / 16.
+int rb_for_rows(int rows)
 {
-    // X arrives from L2 about 1400 cycles after it is requested, XRING - 1 windows ahead.
-    const int xring = MB >= 8 ? 2 : MB >= 4 ? 3 : 4;
-    const double x_lat = 1400.0 / (xring - 1);
-    const double mfma = 16.0 * units * MB;
-    const double valu = 80.0 * units;
-    const double x_l2 = 16.0 * MB * kBatchRowBytes / 64.0;
-    const double lds = (16.0 * MB * kBatchRowBytes * (1 + kBatchConsumers / KS) +
-                        2.0 * pt * (kBatchTileBytes + kWave * 4)) /
-                       128.0;
-    const double hbm = pt * (kBatchTileBytes + kWave * 4) / 13.0;
-    const double lat = kLoadLatency / (kBatchWRing - 1);
-    // (plus a tenth of the consumer's own work, which breaks ties toward spreading it)
-    return std::max(std::max(std::max(mfma, valu), std::max(x_l2, lds)),
-                    std::max(std::max(hbm, lat), x_lat)) +
-           0.1 * std::max(mfma, valu);
+    const int blocks = (rows + 15) / 16;
+    return blocks <= 1 ? 1 : blocks <= 2 ? 2 : blocks <= 4 ? 4 : 8;
 }
 
-bool batch_plan(int rows, int N, int K, int ks_req, int s_req, BatchPlan *P)
+// Tiles per pass and passes for T tiles per set: at most 9 tiles per pass, the passes equal.
+void slab_passes(int T, int *ht, int *nr, int *passes)
 {
-    // The Y descriptor covers rows * N floats with 32-bit offsets.
-    if ((long long)rows * N * 4 >= (1LL << 31))
+    const int maxtw = 2 * kSlabMaxHT + 1;
+    *passes = std::max(1, (T + maxtw - 1) / maxtw);
+    const int tw = std::max(2, (T + *passes - 1) / *passes);
+    *ht = tw / 2;
+    *nr = tw % 2;
+}
+
+// The plan for `rows` rows with row groups of rg rows (rg = 16, 32, 64 or 128; 0: best).
+bool slab_plan(int rows, int N, int K, bool pair, int rg_req, SlabPlan *P)
+{
+    if (rows < 1 || rows > 16 * 8)
         return false;
-    const int nwin = (K + kBatchWindow - 1) / kBatchWindow;
-    const int mbi = rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 64 ? 2 : 3;
-    const int MB = 1 << mbi;
     const int cus = compute_units();
-    double best = 0.0;
-    bool found = false;
-    for (int si = 0; si < 4; si++) {
-        const int S = 1 << si;   // K slices
-        if ((s_req != 0 && S != s_req) || S > nwin)
-            continue;
-        const int G = std::max(1, std::min(num_groups(N), cus / S));
-        if (!bytes_fit(N, K, G))
-            continue;
-        const int T = ((num_groups(N) + G - 1) / G + 3) / 4;
-        const int nw = (nwin + S - 1) / S;   // windows of the longest slice
-        // Split K adds the S partial slices' round trip and a second launch.
-        const double reduce =
-            S > 1 ? (S + 1.0) * rows * N * 4.0 / 2400.0 + kLoadLatency : 0.0;
-        auto consider = [&](double cost, int tcw, int ksi, int nr, int nri) {
-            cost += reduce;
-            if (!found || cost < best - 1e-9) {
-                best = cost;
-                found = true;
-                P->tcw = tcw;
-                P->ksi = ksi;
-                P->nr = nr;
-                P->nri = nri;
-                P->nslice = S;
-                P->grid = G;
-            }
-        };
-        for (int ksi = 0; ksi < 3; ksi++) {
-            const int KS = 1 << ksi;
-            if (ks_req != 0 && KS != ks_req)
-                continue;
-            const int TS = kBatchConsumers / KS;
-            const int NSTEP = 4 / KS;
-            for (int tcw = 1; tcw <= 3; tcw++) {
-                if (kBatchLds[tcw - 1][mbi][ksi] > kMaxLds)
-                    continue;
-                const int PT = TS * tcw;
-                double cost = 0.0;
-                for (int t0 = 0; t0 < T; t0 += PT) {
-                    const int pt = std::min(PT, T - t0);   // tiles of this pass
-                    const int live = std::min(tcw, (pt + TS - 1) / TS);
-                    cost += nw * batch_window_cost(live * NSTEP, MB, KS, pt) + kLoadLatency;
-                }
-                consider(cost, tcw, ksi, 0, 0);
-            }
-        }
-        // Remainder variants (KS = 1): passes of 4 TCW + NR tiles, every consumer 4 TCW + NR
-        // steps.
-        if (ks_req == 0 || ks_req == 1) {
-            for (int ci = 0; ci < kBatchNrCombos; ci++) {
-                const int tcw = kBatchNrTcw[ci], nr = kBatchNrNr[ci];
-                if (kBatchNrLds[ci][mbi] > kMaxLds)
-                    continue;
-                const int PT = kBatchConsumers * tcw + nr;
-                double cost = 0.0;
-                for (int t0 = 0; t0 < T; t0 += PT)
-                    cost += nw * batch_window_cost(4 * tcw + nr, MB, 1, std::min(PT, T - t0)) +
-                            kLoadLatency;
-                consider(cost, tcw, 0, nr, ci);
-            }
-        }
-    }
-    if (!found)
+    const int unit = pair ? 2 : 1;
+    const int units = num_groups(N) / unit;
+    if (units < 1)
         return false;
-    P->mbi = mbi;
-    P->mb = MB;
-    P->lds = P->nr > 0 ? kBatchNrLds[P->nri][mbi] : kBatchLds[P->tcw - 1][mbi][P->ksi];
-    return true;
-}
-
-// Library workspaces: one per device and kind (kind 0: the split-K partial sums; kind 1: the
-// normalised X and the gate/up output of a fused call at M > 16), grown (never shrunk or freed:
-// a captured graph may still hold an older one) on first need. Returns null when it would have
-// to grow while the stream is being captured, or when the allocation fails.
-float *batch_workspace(size_t bytes, hipStream_t stream, int kind = 0)
-{
-    static std::mutex mu;
-    static std::map<std::pair<int, int>, std::pair<void *, size_t>> ws;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    auto &e = ws[{dev, kind}];
-    if (e.first != nullptr && e.second >= bytes)
-        return static_cast<float *>(e.first);
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) {
-        (void)hipGetLastError();
-        return nullptr;
+    const double nwin = (K + kSlabWindow - 1) / kSlabWindow;
+    bool found = false;
+    double best = 0.0;
+    for (int rg = 16; rg <= 128; rg *= 2) {
+        if (rg_req != 0 && rg != rg_req)
+            continue;
+        const int Pg = (rows + rg - 1) / rg;
+        if (Pg > cus)
+            continue;
+        int S = cus / Pg;
+        if (S >= 8)
+            S -= S % 8;
+        S = std::max(1, std::min(S, units));
+        const int gmax = unit * ((units + S - 1) / S);
+        if (!bytes_fit(N, K, S, pair))
+            continue;
+        const int T = (gmax + 3) / 4;
+        int ht, nr, passes;
+        slab_passes(T, &ht, &nr, &passes);
+        const int rb = rb_for_rows(std::min(rows, rg));
+        const int lds = kSlabLds[rb_index(rb)][ht - 1][nr];
+        if (lds > kMaxLds)
+            continue;
+        const int tw = 2 * ht + nr;
+        const double mfma = 17.0 * 1.2 * tw * rb;                 // per consumer and window
+        const double wbytes = tw * (kSlabTileBytes + 128.0);
+        const double xbytes = 16.0 * rb * kSlabRowBytes;
+        const double l2 = (wbytes + xbytes) / 64.0;
+        const double ldsc = (wbytes + xbytes + kSlabWaves * 2.0 * rb * 1024.0) / 128.0;
+        const double hbm = wbytes / Pg / 13.0 * (double)(Pg * S) / cus;
+        const double win = std::max(std::max(mfma, l2), std::max(ldsc, hbm));
+        const double cost = passes * (nwin * win + kSlabFill);
+        if (!found || cost < best - 1e-9) {
+            found = true;
+            best = cost;
+            P->rg = rg;
+            P->rb = rb;
+            P->rbi = rb_index(rb);
+            P->P = Pg;
+            P->S = S;
+            P->ht = ht;
+            P->nr = nr;
+            P->passes = passes;
+            P->lds = lds;
+            P->gunit = unit;
+        }
     }
-    void *p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    e = {p, bytes};
-    return static_cast<float *>(p);
+    return found;
 }
 
-// Batch-invariant mode: one plan per (N, K), the plan of a full 128-row slab (K slices included),
-// used for every slab whatever its rows. Only the row-block count MB follows the rows, and a row's
-// arithmetic does not depend on it: each row block has its own accumulators, the weight fragment
-// it multiplies is the same, and the steps, the step split, the remainder partials and the K
-// slices are added in the same order. So row m of Y is the same bits for any M. The workspace of
-// a split plan is sized for a full slab on every call, so one call outside stream capture covers
-// every later M.
-bool invariant_plan(int N, int K, BatchPlan *P)
+// Batch-invariant mode: one plan per (N, K), the plan of a full 128-row slab, used for every
+// slab whatever its rows. A slab with fewer rows runs fewer row groups (and fewer row blocks
+// in the last), but every row's arithmetic stays the same: its tile set, the k-steps each
+// consumer multiplies, the remainder split and the order the partial sums meet in are fixed
+// by (S, ht, nr, passes), and each row block has accumulators of its own.
+bool invariant_plan(int N, int K, bool pair, SlabPlan *P)
 {
-    return batch_plan(16 * kBatchMaxBlocks, N, K, 0, 0, P);
+    return slab_plan(16 * 8, N, K, pair, 0, P);
 }
 
-// The invariant plan adapted to a slab of `rows` rows: the row-block count and LDS bytes only.
-void plan_for_rows(BatchPlan *P, int rows)
+// The invariant plan adapted to a slab of `rows` rows: row groups and row blocks only.
+void plan_for_rows(SlabPlan *P, int rows)
 {
-    P->mbi = rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 64 ? 2 : 3;
-    P->mb = 1 << P->mbi;
-    P->lds = P->nr > 0 ? kBatchNrLds[P->nri][P->mbi] : kBatchLds[P->tcw - 1][P->mbi][P->ksi];
+    P->P = (rows + P->rg - 1) / P->rg;
+    P->rb = rb_for_rows(std::min(rows, P->rg));
+    P->rbi = rb_index(P->rb);
+    P->lds = kSlabLds[P->rbi][P->ht - 1][P->nr];
 }
 
 // Tiles of 16 columns per workgroup when every compute unit takes an equal share of the groups.
@@ -492,30 +423,20 @@ bool choose_config(int M, int N, int K, int *path, int *split)
     // Automatic choice (measured on the layer shapes): the dot-product kernel for the smallest M;
     // the 16-row matrix-core kernel up to M = 16 and, up to M = 48, for narrow shapes (a few
     // tiles per compute unit) of moderate K, whose weights it reads once per row block; above
-    // that the batch kernel, which decodes each weight once per 128 rows (and cuts K across
-    // workgroups for narrow shapes).
+    // that the slab kernel, which decodes each weight once per workgroup for up to 128 rows.
     if (*path == kPathAuto) {
         const bool narrow = tiles_per_workgroup(N) < 6 && K <= 8192;
         *path = (M <= 4) ? kPathDot : (M <= 16 || (M <= 48 && narrow)) ? kPathMfma : kPathBatch;
     }
     if (*path == kPathBatch) {
-        if (*split != 0 && *split != 1 && *split != 2 && *split != 4)
+        if (*split != 0 && *split != 16 && *split != 32 && *split != 64 && *split != 128)
             return false;
-        BatchPlan P;
-        if (!batch_plan(std::min(M, 16 * kBatchMaxBlocks), N, K, *split, 0, &P))
-            return false;
-        *split = 1 << P.ksi;
-        return true;
+        SlabPlan P;
+        return slab_plan(std::min(M, 128), N, K, false, *split, &P);
     }
     if (*path == kPathInvariant) {
-        BatchPlan P;
-        return *split == 0 && invariant_plan(N, K, &P);
-    }
-    if (*path == kPathBatchSplit) {
-        if (*split != 2 && *split != 4 && *split != 8)
-            return false;
-        BatchPlan P;
-        return batch_plan(std::min(M, 16 * kBatchMaxBlocks), N, K, 0, *split, &P);
+        SlabPlan P;
+        return *split == 0 && invariant_plan(N, K, false, &P);
     }
     if (*path == kPathDot) {
         if (M > kDotMaxM)
@@ -583,82 +504,48 @@ hipError_t launch_impl(int path, int split, const GemmArgs &a0, int32_t *index, 
             return le;
         return launch_finalize(a.keys, a.key_slots, a.M, index, value, stream);
     }
-    if (path == kPathBatch || path == kPathBatchSplit || path == kPathInvariant) {
-        const int ks_req = path == kPathBatch ? split : 0;
-        const int s_req = path == kPathBatch ? 0 : split;
-        BatchPlan fixed = {};
-        if (path == kPathInvariant && !invariant_plan(a.N, a.K, &fixed))
-            return hipErrorInvalidValue;
+    if (path == kPathBatch || path == kPathInvariant) {
         // Slabs of 128 rows, one launch each (the last one may be smaller).
-        constexpr int kSlab = 16 * kBatchMaxBlocks;
-        for (int m0 = 0; m0 < a.M; m0 += kSlab) {
-            const int rows = std::min(kSlab, a.M - m0);
-            BatchPlan P = fixed;
+        const bool pair = a.H != nullptr;
+        SlabPlan fixed = {};
+        if (path == kPathInvariant && !invariant_plan(a.N, a.K, pair, &fixed))
+            return hipErrorInvalidValue;
+        const int mode = argmax ? kSlabArgmax : pair ? kSlabSilu : kSlabStore;
+        constexpr int kSlabRows = 128;
+        for (int m0 = 0; m0 < a.M; m0 += kSlabRows) {
+            const int rows = std::min(kSlabRows, a.M - m0);
+            SlabPlan P = fixed;
             if (path == kPathInvariant)
                 plan_for_rows(&P, rows);
-            else if (!batch_plan(rows, a.N, a.K, ks_req, s_req, &P))
+            else if (!slab_plan(rows, a.N, a.K, pair, split, &P))
                 return hipErrorInvalidValue;
-            GemmArgs b = a;
-            b.X = a.X + (size_t)m0 * (size_t)a.K;
-            b.Y = a.Y != nullptr ? a.Y + (size_t)m0 * (size_t)a.N : nullptr;
-            b.M = rows;
-            float *ws = nullptr;
-            const size_t stride = batch_slice_stride(rows, a.N);
-            if (P.nslice > 1 && path == kPathInvariant) {
-                // The slices are part of the invariant arithmetic: no unsplit fallback.
-                ws = batch_workspace(
-                    (size_t)P.nslice * batch_slice_stride(kSlab, a.N) * sizeof(float), stream);
-                if (ws == nullptr)
-                    return hipErrorStreamCaptureUnsupported;
-            } else if (P.nslice > 1) {
-                ws = batch_workspace((size_t)P.nslice * stride * sizeof(float), stream);
-                if (ws == nullptr && !batch_plan(rows, a.N, a.K, ks_req, 1, &P))
-                    return hipErrorInvalidValue;   // no workspace: run unsplit
-            }
-            // Argmax mode: the kernel folds Y into keys itself unless K is split, in which case
-            // the partials go to the workspace as usual and the reduce kernel folds the sums.
-            const int fold = (argmax && P.nslice == 1) ? 1 : 0;
-            const KernelFn fn = P.nr > 0 ? kBatchNrAll[fold][P.nri][P.mbi]
-                                         : kBatchAll[fold][P.tcw - 1][P.mbi][P.ksi];
+            const SlabFn fn = kSlab[mode][P.rbi][P.ht - 1][P.nr];
             const hipError_t e = allow_lds(reinterpret_cast<const void *>(fn), P.lds);
             if (e != hipSuccess)
                 return e;
-            GemmArgs kb = b;
-            kb.keys = nullptr;
-            if (P.nslice > 1)
-                kb.Y = ws;   // unscaled partial sums, slice by slice
+            GemmArgs b = a;
+            b.X = a.X + (size_t)m0 * (size_t)a.K;
+            b.Y = a.Y != nullptr ? a.Y + (size_t)m0 * (size_t)a.N : nullptr;
+            b.H = a.H != nullptr ? a.H + (size_t)m0 * (size_t)(a.N / 2) : nullptr;
+            b.M = rows;
+            SlabLayout L;
+            L.sets = P.S;
+            L.rgroups = P.P;
+            L.gunit = P.gunit;
+            L.xcd = (P.S % 8 == 0 && P.P > 1) ? 1 : 0;
+            L.passes = P.passes;
+            L.key_slots = kSlabWaves * P.S;   // one key per consumer wavefront and tile set
             argkey_t *slab_keys = argmax ? a.keys + (size_t)m0 * (size_t)cap : nullptr;
-            if (fold) {
-                kb.keys = slab_keys;
-                kb.key_slots = kBatchConsumers * P.grid;   // one key per consumer wavefront
-                if (kb.key_slots > cap)
-                    return hipErrorInvalidValue;
-            }
-            hipLaunchKernelGGL(fn, dim3((unsigned)P.grid, (unsigned)P.nslice),
-                               dim3(kWave * kBatchWaves), P.lds, stream, kb);
+            b.keys = slab_keys;
+            if (argmax && L.key_slots > cap)
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL(fn, dim3((unsigned)(P.S * P.P)), dim3(kWave * kSlabWaves), P.lds,
+                               stream, b, L);
             hipError_t le = hipGetLastError();
             if (le != hipSuccess)
                 return le;
-            int slots = kb.key_slots;
-            if (P.nslice > 1 && argmax) {
-                slots = std::min(cap, std::max(1, std::min((a.N + 255) / 256, 256)));
-                hipLaunchKernelGGL(batch_reduce_argmax_kernel, dim3((unsigned)slots, (unsigned)rows),
-                                   dim3(256), 0, stream, ws, P.nslice, a.N, (long long)stride,
-                                   a.gscale, slab_keys, slots);
-                le = hipGetLastError();
-                if (le != hipSuccess)
-                    return le;
-            } else if (P.nslice > 1) {
-                const long long count = (long long)rows * a.N;
-                const unsigned blocks = (unsigned)((count + 4 * 256 - 1) / (4 * 256));
-                hipLaunchKernelGGL(batch_reduce_kernel, dim3(blocks), dim3(256), 0, stream, ws,
-                                   P.nslice, count, (long long)stride, a.gscale, b.Y);
-                le = hipGetLastError();
-                if (le != hipSuccess)
-                    return le;
-            }
             if (argmax) {
-                le = launch_finalize(slab_keys, slots, rows, index + m0, value + m0, stream);
+                le = launch_finalize(slab_keys, L.key_slots, rows, index + m0, value + m0, stream);
                 if (le != hipSuccess)
                     return le;
             }
@@ -708,34 +595,47 @@ hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *i
 
 int device_compute_units() { return compute_units(); }
 
+namespace {
+
+// Whether nvfp4_gemm_fused runs everything inside the dot-product kernel (up to 4 rows, X in LDS).
+bool fused_in_dot(int M, int N, int K, bool pair, int *waves, StreamLayout *L, int *grid)
+{
+    *waves = dot_default_waves(M, N, K);
+    return M <= 4 && stream_plan(M, N, K, M, *waves, grid, L, pair);
+}
+
+}  // namespace
+
+size_t fused_workspace_bytes(bool norm, bool pair, int M, int N, int K)
+{
+    StreamLayout L;
+    int grid, waves;
+    if (!norm || fused_in_dot(M, N, K, pair, &waves, &L, &grid))
+        return 0;
+    return ((size_t)M * (size_t)K * 2 + 255) & ~(size_t)255;
+}
+
 hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream)
 {
     const bool pair = a.H != nullptr;
     // Up to 4 rows the dot-product kernel does it all: X is staged in LDS anyway, so RMSNorm
     // costs two barriers and a pass over LDS, and the SiLU(gate) * up epilogue runs on the
-    // column sums. Above, the RMSNorm is a row-wise kernel of its own (normalising each X window
-    // inside the 16-row kernel cost more than the launch); the SiLU(gate) * up epilogue stays in
-    // the 16-row kernel (M <= 16) or follows the batch kernel as an elementwise kernel (M > 16,
-    // the batch kernel reading each weight once per 128 rows).
+    // column sums. Above, the RMSNorm is a row-wise kernel of its own writing the normalised X
+    // to the caller's workspace (normalising X inside the matrix-core kernels repeats the work in
+    // every workgroup: at 128 rows as much VALU work per window as decoding the weights); the
+    // SiLU(gate) * up epilogue is inside the 16-row kernel (M <= 16) and the slab kernel.
     StreamLayout L;
-    int grid;
-    const int dw = dot_default_waves(a.M, a.N, a.K);
-    const bool dot = a.M <= 4 && stream_plan(a.M, a.N, a.K, a.M, dw, &grid, &L, pair);
-    const bool split_silu = pair && a.M > 16;
-    const size_t xbytes = (!dot && a.gamma) ? ((size_t)a.M * a.K * 2 + 255) & ~(size_t)255 : 0;
-    const size_t ybytes = split_silu ? (size_t)a.M * a.N * 4 : 0;
-    uint8_t *ws = nullptr;
-    if (xbytes + ybytes > 0) {
-        ws = reinterpret_cast<uint8_t *>(batch_workspace(xbytes + ybytes, stream, 1));
-        if (ws == nullptr)
-            return hipErrorStreamCaptureUnsupported;   // (or out of memory)
-    }
+    int grid, dw;
+    const bool dot = fused_in_dot(a.M, a.N, a.K, pair, &dw, &L, &grid);
+    const size_t xbytes = fused_workspace_bytes(a.gamma != nullptr, pair, a.M, a.N, a.K);
+    if (xbytes > a.workspace_bytes || (xbytes > 0 && a.workspace == nullptr))
+        return hipErrorInvalidValue;
     (void)hipGetLastError();
     GemmArgs b = a;
     b.keys = nullptr;
     b.key_slots = 0;
     if (xbytes > 0) {
-        uint16_t *Xn = reinterpret_cast<uint16_t *>(ws);
+        uint16_t *Xn = reinterpret_cast<uint16_t *>(a.workspace);
         hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3((unsigned)a.M), dim3(256), 0, stream, a.X,
                            a.gamma, a.eps, a.K, Xn);
         const hipError_t e = hipGetLastError();
@@ -755,20 +655,7 @@ hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream)
             return hipErrorInvalidValue;
         return launch_impl(kPathMfma, split, b, nullptr, nullptr, stream);
     }
-    if (split_silu) {
-        b.H = nullptr;
-        b.Y = reinterpret_cast<float *>(ws + xbytes);
-    }
-    int path = kPathAuto, split = 0;
-    if (!choose_config(a.M, a.N, a.K, &path, &split))
-        return hipErrorInvalidValue;
-    hipError_t e = launch_impl(path, split, b, nullptr, nullptr, stream);
-    if (e != hipSuccess || !split_silu)
-        return e;
-    const long long count = (long long)a.M * (a.N / 2);
-    hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                       stream, b.Y, count, a.N, a.H);
-    return hipGetLastError();
+    return launch_impl(kPathBatch, 0, b, nullptr, nullptr, stream);
 }
 
 }  // namespace nvfp4

@@ -26,6 +26,10 @@ struct GemmArgs {
     const uint16_t *gamma = nullptr;   // bf16 [K]
     float eps = 0.0f;
     uint16_t *H = nullptr;             // bf16 [M][N / 2]
+    // Caller-owned device scratch of nvfp4_gemm_fused (the normalised X when a kernel of its own
+    // computes the RMSNorm).
+    void *workspace = nullptr;
+    size_t workspace_bytes = 0;
 };
 
 // Packed layout: 4-column groups, 32-k chunks. One chunk of one group is 4 x 16 code bytes
@@ -77,7 +81,6 @@ enum Path {
     kPathDot = 1,
     kPathMfma = 2,
     kPathBatch = 3,
-    kPathBatchSplit = 4,
     kPathInvariant = 5
 };
 
@@ -106,7 +109,11 @@ hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *i
                               float *value, hipStream_t stream);
 
 // Launch of nvfp4_gemm_fused: RMSNorm prologue (a.gamma) and/or SiLU(gate) * up epilogue (a.H).
+// The normalised X goes to a.workspace when fused_workspace_bytes() is not zero.
 hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream);
+
+// Workspace bytes nvfp4_gemm_fused needs (0 when one kernel does everything).
+size_t fused_workspace_bytes(bool norm, bool pair, int M, int N, int K);
 
 // Compute units of the current device (cached per device).
 int device_compute_units();

@@ -1,8 +1,7 @@
-// neighbours.h -- the decode layer's neighbours of the GEMM as kernels of their own, for the
-// fused entry point (nvfp4_gemm_fused): the RMSNorm of X before the GEMM above 4 rows (up to 4
-// the dot-product kernel normalises X in LDS itself), and SiLU(gate) * up of the interleaved
-// gate/up output after the batch kernel above 16 rows (up to 16 the GEMM kernels' epilogues do
-// it) ("SparkInfer" README, section "Layout & scoring": RMSNorm and fused FFN kernels).
+// neighbours.h -- the RMSNorm before the GEMM as a kernel of its own, for the fused entry point
+// (nvfp4_gemm_fused) above 4 rows (up to 4 the dot-product kernel normalises X in LDS itself;
+// SiLU(gate) * up is always inside the GEMM kernels' epilogues) ("SparkInfer" README, section
+// "Layout & scoring": RMSNorm and fused FFN kernels).
 #pragma once
 
 #include "device.h"
@@ -76,23 +75,6 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *X, co
             *reinterpret_cast<u32x4_t *>(Xn + row + 8 * p) = o;
         }
     }
-}
-
-// H[m][j] = bf16(SiLU(gate) * up) from the fp32 output Y[M][N] of an interleaved gate/up weight:
-// gate = Y[m][8q + c], up = Y[m][8q + 4 + c] for j = 4q + c. One thread per output.
-__global__ __launch_bounds__(256) void silu_mul_kernel(const float *Y, long long count, int N,
-                                                       uint16_t *H)
-{
-    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= count)
-        return;
-    const int I = N >> 1;
-    const long long m = idx / I;
-    const int j = (int)(idx - m * I);
-    const float gate = Y[m * N + 8 * (j >> 2) + (j & 3)];
-    const float up = Y[m * N + 8 * (j >> 2) + 4 + (j & 3)];
-    const float h = gate / (1.0f + __expf(-gate)) * up;
-    H[idx] = __builtin_bit_cast(uint16_t, (__bf16)h);
 }
 
 }  // namespace nvfp4

@@ -23,6 +23,7 @@ A16B = 0x7F0000100000
 A16C = 0x7F0000200000
 A16D = 0x7F0000300000
 A16E = 0x7F0000400000
+A16F = 0x7F0000600000   # workspace
 
 
 @pytest.fixture(scope="module")
@@ -53,7 +54,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert nv.abi_version() == 5
+    assert nv.abi_version() == 6
     for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH):
         assert nv.status_string(st)
     assert nv.status_string(99) == "unknown status"
@@ -94,13 +95,13 @@ def test_gemm_path_rejects_bad_options(lib):
     # the matrix-core kernel runs 4 or 8 waves per workgroup
     assert nv.nvfp4_gemm_path(nv.PATH_MFMA, 16, 16, 16, 256, *ptrs, None) == \
         nv.ERROR_INVALID_VALUE
-    # the batch kernel's split is the step split 1, 2 or 4
-    for split in (8, 16):
+    # the slab kernel's split is the rows of a row group: 16, 32, 64 or 128 (0: chosen)
+    for split in (1, 2, 4, 8, 12, 256):
         assert nv.nvfp4_gemm_path(nv.PATH_BATCH, split, 128, 16, 256, *ptrs, None) == \
             nv.ERROR_INVALID_VALUE
-    # the split-K batch path takes 2, 4 or 8 slices, at most one per 128 k (K = 256: 2 windows)
-    for split in (0, 1, 4, 16):
-        assert nv.nvfp4_gemm_path(nv.PATH_BATCH_SPLITK, split, 128, 16, 256, *ptrs, None) == \
+    # path 4 (K cut across workgroups through a library workspace) no longer exists
+    for split in (0, 2, 4, 8):
+        assert nv.nvfp4_gemm_path(4, split, 128, 16, 256, *ptrs, None) == \
             nv.ERROR_INVALID_VALUE
     # the batch-invariant mode has no split to choose
     for split in (1, 2, 4, 8):
@@ -247,9 +248,10 @@ def test_grouped_with_no_rows_does_nothing(lib):
 
 # ---- nvfp4_gemm_fused: fuse flags, sizes, eps, pointers, alignment ----
 
-def _fused(fuse, M, N, K, ptrs=None, eps=1e-6):
+def _fused(fuse, M, N, K, ptrs=None, eps=1e-6, ws=0, ws_bytes=0):
     p = ptrs or [A16, A16B, A16C, A16D, A16E, A8F]     # X, gamma, Wq, Wscale, gscale, out
-    return nv.nvfp4_gemm_fused(fuse, M, N, K, p[0], p[1], eps, p[2], p[3], p[4], p[5], None)
+    return nv.nvfp4_gemm_fused(fuse, M, N, K, p[0], p[1], eps, p[2], p[3], p[4], p[5], ws,
+                               ws_bytes, None)
 
 
 def test_fused_rejects_bad_arguments(lib):
@@ -276,3 +278,24 @@ def test_fused_rejects_bad_arguments(lib):
     assert _fused(nv.FUSE_RMSNORM, 1, 16, 256, bad) == nv.ERROR_MISALIGNED
     bad[5] = good[5] + 1
     assert _fused(nv.FUSE_SILU_MUL, 1, 16, 256, bad) == nv.ERROR_MISALIGNED
+
+
+def test_fused_workspace_rules(lib):
+    """The fused call's workspace: none needed where one kernel does everything (up to 4 rows
+    with X in LDS, or no RMSNorm); otherwise the normalised X, M * K * 2 bytes rounded up to
+    256; a call with less, or a null or misaligned workspace, is rejected before any HIP call."""
+    assert nv.nvfp4_fused_workspace_bytes(nv.FUSE_SILU_MUL, 128, 16, 256) == 0
+    assert nv.nvfp4_fused_workspace_bytes(nv.FUSE_RMSNORM, 1, 16, 256) == 0
+    assert nv.nvfp4_fused_workspace_bytes(nv.FUSE_RMSNORM, 5, 16, 256) == 2560
+    assert nv.nvfp4_fused_workspace_bytes(nv.FUSE_RMSNORM, 5, 16, 272) == 2816   # 2720 -> 2816
+    need = nv.nvfp4_fused_workspace_bytes(nv.FUSE_RMSNORM | nv.FUSE_SILU_MUL, 128, 16, 5120)
+    assert need == 128 * 5120 * 2
+    assert nv.nvfp4_fused_workspace_bytes(0, 128, 16, 5120) == 0
+    assert nv.nvfp4_fused_workspace_bytes(nv.FUSE_RMSNORM, 0, 16, 5120) == 0
+    assert _fused(nv.FUSE_RMSNORM, 128, 16, 5120) == nv.ERROR_INVALID_VALUE            # none
+    assert _fused(nv.FUSE_RMSNORM, 128, 16, 5120, ws=A16F, ws_bytes=need - 1) == \
+        nv.ERROR_INVALID_VALUE                                                          # short
+    assert _fused(nv.FUSE_RMSNORM, 128, 16, 5120, ws=0, ws_bytes=need) == \
+        nv.ERROR_INVALID_VALUE                                                          # null
+    assert _fused(nv.FUSE_RMSNORM, 128, 16, 5120, ws=A16F + 8, ws_bytes=need) == \
+        nv.ERROR_MISALIGNED

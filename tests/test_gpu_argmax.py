@@ -26,8 +26,8 @@ pytestmark = pytest.mark.gpu
 # (path, split, M): every kernel family and its argmax writer, ragged M across row blocks/slabs.
 CASES = [(nv.PATH_DOT, 16, 1), (nv.PATH_DOT, 4, 3), (nv.PATH_DOT, 8, 8),
          (nv.PATH_MFMA, 4, 5), (nv.PATH_MFMA, 8, 16), (nv.PATH_MFMA, 8, 33),
-         (nv.PATH_BATCH, 1, 40), (nv.PATH_BATCH, 2, 128), (nv.PATH_BATCH, 4, 130),
-         (nv.PATH_BATCH_SPLITK, 4, 64), (nv.PATH_BATCH_SPLITK, 8, 129),
+         (nv.PATH_BATCH, 0, 40), (nv.PATH_BATCH, 32, 128), (nv.PATH_BATCH, 64, 130),
+         (nv.PATH_BATCH, 16, 64), (nv.PATH_BATCH, 128, 129),
          (nv.PATH_INVARIANT, 0, 1), (nv.PATH_INVARIANT, 0, 17),
          (nv.PATH_AUTO, 0, 1), (nv.PATH_AUTO, 0, 16), (nv.PATH_AUTO, 0, 128)]
 
@@ -72,8 +72,6 @@ def _check_against_oracle(idx, val, Yref, A, label):
 @pytest.mark.parametrize("path,split,M", CASES)
 def test_argmax_matches_gemm_and_oracle(device, path, split, M):
     for N, K in [(1003, 1024), (4099, 272), (65, 5120)]:
-        if path == nv.PATH_BATCH_SPLITK and split > -(-K // 128):
-            continue                      # at most one K slice per 128 k
         X, Wq, Ws, g = random_case(11 * M + N + K, M, N, K, FINITE_SCALES)
         label = f"argmax path={path} split={split} M={M} N={N} K={K}"
         say(label)
@@ -115,8 +113,8 @@ def test_constructed_ties_at_the_maximum(device):
         Wq[n] = 0x77                                          # 6.0 everywhere
     X = torch.ones(M, K, dtype=torch.bfloat16)
     packed = to_device_packed(torch.from_numpy(Wq), torch.from_numpy(Ws), 1.0, device)
-    for path, split in [(nv.PATH_DOT, 16), (nv.PATH_MFMA, 8), (nv.PATH_BATCH, 1),
-                        (nv.PATH_BATCH_SPLITK, 2)]:
+    for path, split in [(nv.PATH_DOT, 16), (nv.PATH_MFMA, 8), (nv.PATH_BATCH, 0),
+                        (nv.PATH_BATCH, 32)]:
         say(f"constructed ties path={path}")
         _, idx, val = _run(X, packed, device, path, split)
         assert idx.tolist() == [77] * M, (path, idx)
@@ -135,7 +133,7 @@ def test_all_negative_and_zero_rows(device):
     X[1] = 0.5
     Yref, _ = oracle.gemm(inputs.bf16_bits(X), Wq, np.asarray(Ws), 1.0)
     packed = to_device_packed(torch.from_numpy(Wq), Ws, 1.0, device)
-    for path, split in [(nv.PATH_DOT, 16), (nv.PATH_MFMA, 4), (nv.PATH_BATCH, 1)]:
+    for path, split in [(nv.PATH_DOT, 16), (nv.PATH_MFMA, 4), (nv.PATH_BATCH, 0)]:
         say(f"negative rows path={path}")
         Y, idx, val = _run(X, packed, device, path, split)
         assert np.array_equal(idx, oracle.argmax_rows(Yref)), (path, idx)

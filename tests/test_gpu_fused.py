@@ -145,8 +145,9 @@ def test_layer_shapes(device, M):
 
 
 def test_fused_graph_replays_match_eager(device):
-    """Fused calls (M = 1 in one kernel, M = 64 as RMSNorm, batch GEMM and SiLU * up kernels
-    through the library workspace) captured in a HIP graph reproduce the eager bits."""
+    """Fused calls (M = 1 in one kernel; M = 64 as an RMSNorm kernel writing the caller's
+    workspace, then the slab kernel with the SiLU * up epilogue) captured in a HIP graph reproduce
+    the eager bits on every replay, with the workspace clobbered between replays."""
     K, N = 1024, 2048
     gen = inputs.generator(6060)
     W = nv.interleave_gate_up(inputs.weights(gen, K, N))
@@ -154,10 +155,14 @@ def test_fused_graph_replays_match_eager(device):
     gamma = inputs.norm_weight(gen, K).to(device)
     Xs = [inputs.activations(gen, M, K).to(device) for M in (1, 64)]
     Hs = [torch.empty((X.shape[0], N // 2), dtype=torch.bfloat16, device=device) for X in Xs]
+    fuse = nv.FUSE_RMSNORM | nv.FUSE_SILU_MUL
+    Ws = [nv.fused_workspace(fuse, X.shape[0], N, K, device) for X in Xs]
+    assert Ws[0] is None and Ws[1] is not None
 
     def step():
-        for X, H in zip(Xs, Hs):
-            nv.gemm_fused(X, p.Wq, p.Ws, p.g, N, gamma=gamma, eps=EPS, silu_mul=True, out=H)
+        for X, H, ws in zip(Xs, Hs, Ws):
+            nv.gemm_fused(X, p.Wq, p.Ws, p.g, N, gamma=gamma, eps=EPS, silu_mul=True, out=H,
+                          workspace=ws)
 
     step()
     torch.cuda.synchronize()
@@ -168,6 +173,7 @@ def test_fused_graph_replays_match_eager(device):
     for rep in range(3):
         for H in Hs:
             H.fill_(0)
+        Ws[1].fill_(0x5A)
         torch.cuda.synchronize()
         say(f"fused graph replay {rep}")
         graph.replay()

@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 
 PATHS = [(nv.PATH_DOT, 4), (nv.PATH_DOT, 8), (nv.PATH_DOT, 12), (nv.PATH_DOT, 16),
          (nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
-         (nv.PATH_BATCH, 1), (nv.PATH_BATCH, 2), (nv.PATH_BATCH, 4), (nv.PATH_AUTO, 0)]
+         (nv.PATH_BATCH, 0), (nv.PATH_BATCH, 16), (nv.PATH_BATCH, 32), (nv.PATH_BATCH, 64),
+         (nv.PATH_BATCH, 128), (nv.PATH_AUTO, 0)]
 VALU_PATHS = (nv.PATH_DOT,)   # the dot-product kernel: M <= 8
 SMALL_M = [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 130]
 SMALL_N = [1, 15, 16, 17, 65]
@@ -122,7 +123,7 @@ def test_deterministic(device):
 
 
 @pytest.mark.parametrize("path,split", [(nv.PATH_MFMA, 4), (nv.PATH_MFMA, 8),
-                                        (nv.PATH_BATCH, 1), (nv.PATH_BATCH, 4),
+                                        (nv.PATH_BATCH, 128), (nv.PATH_BATCH, 32),
                                         (nv.PATH_DOT, 16)])
 def test_many_columns_per_workgroup(device, path, split):
     """Enough columns that a persistent workgroup owns more column tiles than one pass takes
@@ -136,12 +137,13 @@ def test_many_columns_per_workgroup(device, path, split):
     check_close(Y, Yref, A, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,split", [(16, 34813, 0), (100, 34813, 0), (128, 34813, 1),
-                                       (33, 18431, 0), (128, 22521, 1), (16, 22521, 1)])
+@pytest.mark.parametrize("M,N,split", [(16, 34813, 0), (100, 34813, 0), (128, 34813, 128),
+                                       (33, 18431, 0), (128, 22521, 128), (16, 22521, 16),
+                                       (128, 1795, 32), (70, 4099, 64)])
 def test_batch_remainder_tiles(device, M, N, split):
-    """Column shares of 5, 6 and 9 tiles of 16 per compute unit (256 CUs), where the batch kernel
-    splits the last 1 or 2 tiles of a pass by MFMA step across its four consumers and adds their
-    partial sums in LDS; ragged N, ragged last window (K = 272) and ragged row blocks."""
+    """Column shares that leave an odd tile per workgroup (9, 7, 5, ... tiles of 16), whose four
+    MFMA k-steps are split across the four consumer wavefronts and meet in LDS; ragged N, ragged
+    last window (K = 272), ragged row blocks and row groups."""
     K = 272
     X, Wq, Ws, g = random_case(500 + M + N, M, N, K, FINITE_SCALES)
     Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
@@ -150,24 +152,25 @@ def test_batch_remainder_tiles(device, M, N, split):
     check_close(Y, Yref, A, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K,S", [(128, 1000, 2048, 2), (128, 1000, 2048, 8), (33, 520, 1040, 4),
-                                     (131, 300, 512, 4), (16, 257, 272, 2)])
-def test_batch_split_k(device, M, N, K, S):
-    """K cut into S slices across workgroups: partial sums in the workspace, added in slice order
-    by the reduce kernel (ragged K slices, ragged rows, two 128-row slabs)."""
-    X, Wq, Ws, g = random_case(700 + M + N + S, M, N, K, FINITE_SCALES)
+@pytest.mark.parametrize("M,N,K,rg", [(128, 1000, 2048, 16), (128, 1000, 2048, 32),
+                                      (33, 520, 1040, 64), (131, 300, 512, 32),
+                                      (128, 5120, 17408, 32), (16, 257, 272, 16)])
+def test_batch_row_groups(device, M, N, K, rg):
+    """Rows cut into row groups of rg rows, each with its own workgroups (tile sets on one XCD);
+    ragged K, ragged rows, two 128-row slabs; reproducible bit for bit."""
+    X, Wq, Ws, g = random_case(700 + M + N + rg, M, N, K, FINITE_SCALES)
     Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
-    say(f"split-k S={S} M={M} N={N} K={K}")
+    say(f"row groups rg={rg} M={M} N={N} K={K}")
     packed = to_device_packed(Wq, Ws, g, device)
-    Y = gpu_gemm(X, packed, device, nv.PATH_BATCH_SPLITK, S)
-    check_close(Y, Yref, A, f"S={S} M={M} N={N} K={K}")
-    Y2 = gpu_gemm(X, packed, device, nv.PATH_BATCH_SPLITK, S)
-    assert np.array_equal(Y, Y2), "split K not reproducible"
+    Y = gpu_gemm(X, packed, device, nv.PATH_BATCH, rg)
+    check_close(Y, Yref, A, f"rg={rg} M={M} N={N} K={K}")
+    Y2 = gpu_gemm(X, packed, device, nv.PATH_BATCH, rg)
+    assert np.array_equal(Y, Y2), "row-group plan not reproducible"
 
 
-def test_auto_narrow_m128_splits_k(device):
+def test_auto_narrow_m128(device):
     """nvfp4_gemm on a narrow shape at M = 128 (few column tiles per compute unit), where the
-    planner cuts K across workgroups."""
+    planner cuts the rows into row groups."""
     M, N, K = 128, 2048, 4096
     X, Wq, Ws, g = random_case(811, M, N, K, FINITE_SCALES)
     Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)

@@ -1,15 +1,20 @@
 """Exact scaling invariants of the HIP GEMM, per kernel family, through the C ABI.
 
-The GEMM is linear in X and in the tensor scale g, and multiplying every input of an fp32 sum by
--1 or 2 multiplies every rounded partial sum by the same factor (no overflow or underflow at these
-magnitudes). So for any fixed summation order, which every kernel has:
-  * Y(-X) = -Y,
+The GEMM is linear in X and in the tensor scale g. Multiplying every input of a floating-point sum
+by 2 multiplies every rounded partial sum by 2 (no overflow or underflow at these magnitudes), in
+IEEE arithmetic and in the matrix cores' accumulation alike, so for the fixed summation order
+every kernel has:
   * Y(2X) = 2Y,
   * Y(2g) = 2Y (g multiplies the finished sum once),
-bit for bit (+0 and -0 compare equal). A kernel that mixed rows, dropped a term, or let one row's
-arithmetic depend on another's magnitude in a non-homogeneous way breaks one of them. These hold
-without any reference value; the oracle is still checked once per case so the invariants are not
-satisfied by a degenerate output.
+bit for bit. Negation commutes with round-to-nearest, so the VALU kernels (dot product, grouped)
+also give Y(-X) = -Y bit for bit. The bf16 matrix-core instruction does not: adding its products
+to a non-zero accumulator it truncates the aligned addends instead of rounding them to nearest
+(measured on gfx950 for v_mfma_f32_16x16x32_bf16: about 3% of outputs differ in the last bits
+between D(A, C) and -D(-A, -C), while D(A, 0) is sign-symmetric), so on the matrix-core kernels
+Y(-X) is held to the oracle's tolerance around -Y_ref instead. A kernel that mixed rows, dropped a
+term, or let a row's arithmetic depend on another row breaks one of these checks; the oracle is
+checked once per case as well, so a degenerate output cannot satisfy them.
++0 and -0 compare equal.
 """
 import numpy as np
 import pytest
@@ -49,7 +54,10 @@ def test_sign_and_scale_invariants(device, path, split, M, N, K):
     check_close(Y.astype(np.float64), Yref, A, label)
     assert np.count_nonzero(Y) > Y.size // 2, f"{label}: degenerate output"
     Yneg = _gemm(-X, p, N, path, split, device)
-    assert np.array_equal(Yneg, -Y), f"{label}: Y(-X) != -Y"
+    if path == nv.PATH_DOT or (path == nv.PATH_AUTO and M <= 4):
+        assert np.array_equal(Yneg, -Y), f"{label}: Y(-X) != -Y"
+    else:
+        check_close(Yneg.astype(np.float64), -Yref, A, f"{label}: Y(-X)")
     Y2x = _gemm(2 * X, p, N, path, split, device)
     assert np.array_equal(Y2x, np.float32(2) * Y), f"{label}: Y(2X) != 2Y"
     Y2g = _gemm(X, p2, N, path, split, device)
