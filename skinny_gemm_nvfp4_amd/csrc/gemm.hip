@@ -534,7 +534,12 @@ hipError_t launch_impl(int path, int split, const GemmArgs &a0, int32_t *index, 
             L.gunit = P.gunit;
             L.xcd = (P.S % 8 == 0 && P.P > 1) ? 1 : 0;
             L.passes = P.passes;
-            L.key_slots = kSlabWaves * P.S;   // one key per consumer wavefront and tile set
+            L.key_slots = P.S;   // one key per row and tile set
+            L.vec = pair ? (reinterpret_cast<uintptr_t>(b.H) % 8 == 0 ? 1 : 0)
+                         : (b.Y != nullptr && reinterpret_cast<uintptr_t>(b.Y) % 16 == 0 &&
+                            a.N % 4 == 0)
+                               ? 1
+                               : 0;
             argkey_t *slab_keys = argmax ? a.keys + (size_t)m0 * (size_t)cap : nullptr;
             b.keys = slab_keys;
             if (argmax && L.key_slots > cap)

@@ -17,26 +17,29 @@
 //     dispatcher places on the same XCD, so the weights they share are fetched from HBM once and
 //     served to the others by that XCD's L2.
 //   * Workgroup of 4 wavefronts, one per SIMD. Consumer c = 2 ts + ks takes the main tiles ts,
-//     ts + 2, ... (HT of them) and, of every 128-k window, the MFMA k-steps 2 ks and 2 ks + 1;
-//     with NR = 1 the last tile's four k-steps go one to each consumer (step 2 ks + ts). Every
-//     consumer thus multiplies the same number of tile-steps, and each weight is decoded once.
+//     ts + 2, ... (HT of them) and, of every 128-k window, the MFMA k-steps 2 ks and 2 ks + 1
+//     (in the order 2 ks + ts, 2 ks + 1 - ts); with NR = 1 the last tile's four k-steps go one to
+//     each consumer (step 2 ks + ts, its first). Every consumer thus multiplies the same number
+//     of tile-steps, and each weight is decoded once. The B fragment of the next tile is decoded
+//     while the MFMAs of the current one run.
 //   * Per 128-k window the whole workgroup stages X (16 RB rows x 256 bytes), the codes (1 KB
 //     per tile) and the scales (128 bytes per tile) in LDS through direct-to-LDS buffer loads
-//     (16 bytes per lane, no registers), D windows deep, with one barrier per window. The loads
-//     of a window are dealt round robin to the four wavefronts, the same number to each; loads
-//     past the end of a row, of K or of the workgroup's groups read zeros.
+//     (16 bytes per lane, no registers), with one barrier per window: X in a ring of 3
+//     windows loaded by wavefronts 0 and 1, the weights (from HBM, higher latency) in a ring of up
+//     to 6 loaded by wavefronts 2 and 3. Loads past the end of a row, of K or of the workgroup's
+//     groups read zeros.
 //   * Step d of lane (r, q) covers k = 32 q + 8 d .. + 7 of the window: dword d of the lane's 16
 //     code bytes of column r, chunk q is its B fragment (decoded to bf16 with its block scale,
 //     exact), and row 16 b + r of X at those k its A fragment of row block b
 //     (v_mfma_f32_16x16x32_bf16). X rows sit in LDS with piece kp of row m at slot kp ^ (m & 15),
 //     so the 16 rows of an A fragment hit 16 different bank groups.
 //   * At the end of a pass the ks = 1 consumers' partial sums (and all four of the remainder
-//     tile) meet the others' in LDS in a fixed order; Y = sum * g. Results are reproducible.
+//     tile) meet the others' in LDS, in a fixed order, as a row-major tile of Y; then all 256
+//     threads write whole rows of it (16-byte stores), Y = sum * g. Results are reproducible.
 //     Weights with more tiles per workgroup than TW are done in several passes, each streaming
 //     X again.
-//   * MODE 0 stores Y; MODE 1 folds Y into argmax keys (argmax.h), one slot per consumer and
-//     tile set; MODE 2 writes H = bf16(SiLU(gate) * up) of an interleaved gate/up weight (the
-//     gate column's partner is 4 lanes away in the same tile).
+//   * MODE 0 stores Y; MODE 1 folds Y into argmax keys (argmax.h), one slot per row and tile
+//     set; MODE 2 writes H = bf16(SiLU(gate) * up) of an interleaved gate/up weight.
 #pragma once
 
 #include "argmax.h"
@@ -61,19 +64,29 @@ struct SlabShape {
     static constexpr int XBYTES = 16 * RB * kSlabRowBytes;     // X of one window
     static constexpr int CBYTES = TW * kSlabTileBytes;
     static constexpr int NSC = (TW + 7) / 8;                   // scale loads per window
-    static constexpr int BUF = XBYTES + CBYTES + NSC * 1024;
+    static constexpr int WBYTES = CBYTES + NSC * 1024;         // weights of one window
     static constexpr int SINK = 1024;                          // target of padding loads
-    static constexpr int DMAX = (kSlabMaxLds - SINK) / BUF;
-    static constexpr int D = DMAX >= 4 ? 4 : DMAX;             // windows in LDS
-    static_assert(D >= 2, "slab buffers do not fit in LDS");
-    static constexpr int NWL = TW + NSC;                       // code and scale loads
-    static constexpr int NWPW = (NWL + kSlabWaves - 1) / kSlabWaves;
-    static constexpr int LOADS = RB + NWPW;                    // loads per wavefront and window
-    // End-of-pass exchange: ks = 1 partials [2][HT][RB][4][64], remainder [4][RB][4][64].
-    static constexpr int RED_MAIN = 2 * HT * RB * 4 * kWave * 4;
-    static constexpr int RED = RED_MAIN + (NR ? 4 * RB * 4 * kWave * 4 : 0);
-    static constexpr int RING = D * BUF + SINK;
-    static constexpr int LDS = (RING > RED) ? RING : RED;
+    // X comes from L2 (every workgroup of a row group reads it), the weights from HBM: the
+    // weight ring is deeper. Three X windows and as many weight windows (up to 6) as fit.
+    static constexpr int DX = 3;
+    static constexpr int DWMAX = (kSlabMaxLds - SINK - DX * XBYTES) / WBYTES;
+    static constexpr int DW = DWMAX >= 6 ? 6 : DWMAX;
+    static_assert(DW >= 3, "slab buffers do not fit in LDS");
+    static constexpr int XOFF = 0;
+    static constexpr int WOFF = DX * XBYTES;
+    static constexpr int SINKOFF = WOFF + DW * WBYTES;
+    // Waves 0 and 1 issue the X loads (2 RB each per window), waves 2 and 3 the weight loads
+    // (codes then scales, the same count each, padded).
+    static constexpr int XL = 2 * RB;
+    static constexpr int NWL = TW + NSC;
+    static constexpr int WL = (NWL + 1) / 2;
+    // End of a pass: Y as a row-major tile [16 RB][YST] (the row padding keeps the four rows a
+    // fragment writes on different banks), and the remainder tile's four parts [4][16 RB][20].
+    static constexpr int YST = 16 * TW + 4;
+    static constexpr int YBYTES = 16 * RB * YST * 4;
+    static constexpr int EPI = YBYTES + (NR ? 4 * 16 * RB * 20 * 4 : 0);
+    static constexpr int RING = SINKOFF + SINK;
+    static constexpr int LDS = (RING > EPI) ? RING : EPI;
 };
 
 struct SlabLayout {
@@ -82,7 +95,8 @@ struct SlabLayout {
     int gunit;      // column groups dealt together (2: whole gate/up pairs)
     int xcd;        // 1: row groups of a set share an XCD (S % 8 == 0)
     int passes;     // tile passes of up to TW tiles
-    int key_slots;  // argmax: keys per row of the workspace
+    int key_slots;  // argmax: keys per row of the workspace (one per tile set)
+    int vec;        // 1: Y (or H) rows may be written 16 (8) bytes at a time
 };
 
 // Wait until at most N vector memory operations of this wavefront are outstanding.
@@ -122,7 +136,6 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
 {
     using S = SlabShape<RB, HT, NR>;
     constexpr int TW = S::TW;
-    constexpr int D = S::D;
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
@@ -167,50 +180,81 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
     const float g = *a.gscale;
 
     // ---- load side ----
-    // Loads of window w of pass `pass` into ring buffer `buf`; every wavefront issues LOADS of
-    // them per window whatever the window (past the pass's last window, past K, past the rows or
-    // the groups they read zeros; padding loads write zeros into the sink), so waiting for a
-    // window is a fixed count of outstanding loads.
-    //   X: load i of this wavefront covers rows 4 u .. 4 u + 3 of the window, u = wave + 4 i;
-    //      lane l fetches piece (l % 16) ^ (row & 15) of row 4 u + l / 16 into LDS slot l % 16.
-    //   W: load v = wave + 4 j of the window's list: v < TW the codes of tile v (lane l: group
-    //      l / 16 of the tile, 16-byte piece l % 16 of its 256 bytes, = LDS order); then the
-    //      scales of tiles 8 (v - TW) .. + 7 (lane l: tile 8 (v - TW) + l / 8, group (l / 2) % 4,
-    //      16-byte half l % 2 of its 32 bytes: chunks 2 (l % 2), 2 (l % 2) + 1 of the window).
-    auto issue = [&](int pass, int w, int buf) {
+    // Waves 0 and 1 load X windows into the X ring, waves 2 and 3 weight windows into the
+    // weight ring (each load kind in waves of its own, so that waiting for a fast X load never
+    // waits for older weight loads: loads complete in issue order). Every call issues the same
+    // number of loads whatever the window (past the pass's last window they read zeros; padding
+    // loads write zeros into the sink), so waiting for a window is a fixed count of outstanding
+    // loads. A load's lane offset is a loop-invariant register plus a scalar part; rows past the
+    // group and column groups past the workgroup's lie beyond the descriptors' ranges and read
+    // zeros by themselves, so only the window holding the end of K masks lanes.
+    //   X: load i of X wave xw covers rows 4 u .. 4 u + 3 of the window, u = xw + 2 i; lane l
+    //      fetches piece (l % 16) ^ (row & 15) of row 4 u + l / 16 into LDS slot l % 16 (the
+    //      piece depends on u only through u % 4, i.e. on xw and i % 2).
+    //   W: load v = (wave - 2) + 2 j of the window's list: v < TW the codes of tile v (lane l:
+    //      group l / 16 of the tile, 16-byte piece l % 16 of its 256 bytes, = LDS order); then
+    //      the scales of tiles 8 (v - TW) .. + 7 (lane l: tile 8 (v - TW) + l / 8, group
+    //      (l / 2) % 4, 16-byte half l % 2 of its 32 bytes: chunks 2 (l % 2), 2 (l % 2) + 1).
+    const bool xwave = wave < 2;
+    const int xw = wave & 1;
+    const int xrow0 = 4 * xw + (lane >> 4);                   // row of load 0 (u = xw)
+    const int xrow1 = 4 * (xw + 2) + (lane >> 4);             // row of load 1 (u = xw + 2)
+    const int xkp0 = (lane & 15) ^ (xrow0 & 15);
+    const int xkp1 = (lane & 15) ^ (xrow1 & 15);
+    const uint32_t xlane0 = (uint32_t)xrow0 * (uint32_t)K * 2u + (uint32_t)xkp0 * 16u;
+    const uint32_t xlane1 = (uint32_t)xrow1 * (uint32_t)K * 2u + (uint32_t)xkp1 * 16u;
+    const uint32_t xstep = 16u * (uint32_t)K * 2u;            // 16 rows: load i to i + 2
+    const uint32_t clane = (uint32_t)(lane >> 4) * gq + (uint32_t)(lane & 15) * 16u;
+    const uint32_t slane = (uint32_t)(4 * (lane >> 3) + ((lane >> 1) & 3)) * gs +
+                           (uint32_t)(lane & 1) * 16u;
+    const int nfull = K / kSlabWindow;                        // windows with no K tail
+    auto issue_x = [&](int w, int slot) {
+        uint8_t *base = lds + S::XOFF + slot * S::XBYTES;
+        const bool full = w < nfull;
         const bool live = w < nwin;
-        uint8_t *base = lds + buf * S::BUF;
+        const uint32_t xwo = (uint32_t)w * (kSlabWindow * 2);
+        const bool ok0 = full || (live && kSlabWindow * w + 8 * xkp0 < K);
+        const bool ok1 = full || (live && kSlabWindow * w + 8 * xkp1 < K);
 #pragma unroll
-        for (int i = 0; i < RB; i++) {
-            const int u = wave + kSlabWaves * i;
-            const int m = 4 * u + (lane >> 4);
-            const int kp = (lane & 15) ^ (m & 15);
-            const bool v = live && kSlabWindow * w + 8 * kp < K;
-            slab_lds_load16(rx, base + u * 1024,
-                            off_if(v, (uint32_t)m * (uint32_t)K * 2u +
-                                          (uint32_t)w * (kSlabWindow * 2) + (uint32_t)kp * 16u));
+        for (int i = 0; i < S::XL; i++) {
+            const int u = xw + 2 * i;
+            const bool ok = (i & 1) ? ok1 : ok0;
+            const uint32_t lo = ((i & 1) ? xlane1 : xlane0) + xwo + (uint32_t)(i >> 1) * xstep;
+            slab_lds_load16(rx, base + u * 1024, ok ? lo : kOutOfRange);
         }
+    };
+    auto issue_w = [&](int pass, int w, int slot) {
+        uint8_t *base = lds + S::WOFF + slot * S::WBYTES;
+        const bool full = w < nfull;
+        const bool live = w < nwin;
 #pragma unroll
-        for (int j = 0; j < S::NWPW; j++) {
-            const int v = wave + kSlabWaves * j;
+        for (int j = 0; j < S::WL; j++) {
+            const int v = (wave - 2) + 2 * j;
             if (v < TW) {
-                const int grp = 4 * (pass * TW + v) + (lane >> 4);
-                const int chunk = 4 * w + ((lane & 15) >> 2);
-                const bool ok = live && grp < ngroups && chunk < CH;
-                slab_lds_load16(rq, base + S::XBYTES + v * kSlabTileBytes,
-                                off_if(ok, (uint32_t)grp * gq + (uint32_t)w * 256u +
-                                               (uint32_t)(lane & 15) * 16u));
+                const bool ok = full || (live && 4 * w + ((lane & 15) >> 2) < CH);
+                const uint32_t sc = (uint32_t)(4 * (pass * TW + v)) * gq + (uint32_t)w * 256u;
+                slab_lds_load16(rq, base + v * kSlabTileBytes, ok ? clane + sc : kOutOfRange);
             } else if (v < S::NWL) {
-                const int tl = 8 * (v - TW) + (lane >> 3);
-                const int grp = 4 * (pass * TW + tl) + ((lane >> 1) & 3);
-                const int chunk = 4 * w + 2 * (lane & 1);
-                const bool ok = live && tl < TW && grp < ngroups && chunk < CH;
-                slab_lds_load16(rs, base + S::XBYTES + S::CBYTES + (v - TW) * 1024,
-                                off_if(ok, (uint32_t)grp * gs + (uint32_t)w * 32u +
-                                               (uint32_t)(lane & 1) * 16u));
+                const bool ok = full || (live && 4 * w + 2 * (lane & 1) < CH);
+                const uint32_t sc =
+                    (uint32_t)(4 * (pass * TW + 8 * (v - TW))) * gs + (uint32_t)w * 32u;
+                slab_lds_load16(rs, base + S::CBYTES + (v - TW) * 1024,
+                                ok ? slane + sc : kOutOfRange);
             } else {
-                slab_lds_load16(rq, lds + S::D * S::BUF, kOutOfRange);
+                slab_lds_load16(rq, lds + S::SINKOFF, kOutOfRange);
             }
+        }
+    };
+    // The first windows of a pass: D - 1 windows ahead of their use, in each ring.
+    auto prologue = [&](int pass) {
+        if (xwave) {
+#pragma unroll
+            for (int i = 0; i < S::DX - 1; i++)
+                issue_x(i, i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < S::DW - 1; i++)
+                issue_w(pass, i, i);
         }
     };
 
@@ -219,16 +263,9 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
     const uint32_t scale_lane = (uint32_t)(r >> 2) * 32u + (uint32_t)q * 8u + (uint32_t)(r & 2) * 2u;
     const uint32_t sshift = 16u * (uint32_t)(r & 1) + 8u * (uint32_t)ks;
 
-#pragma unroll
-    for (int i = 0; i < D - 1; i++)
-        issue(0, i, i);
+    prologue(0);
 
-    argkey_t best[MODE == kSlabArgmax ? RB : 1][4];
-#pragma unroll
-    for (int b = 0; b < (MODE == kSlabArgmax ? RB : 1); b++)
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-            best[b][e] = 0;
+    argkey_t best = 0;   // greedy token: the key of this thread's row (see the epilogue)
 
     for (int pass = 0; pass < L.passes; pass++) {
         f32x4_t acc[HT][RB];
@@ -243,25 +280,34 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
             racc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
         for (int w = 0; w < nwin; w++) {
-            slab_wait_vm<(D - 2) * S::LOADS>();   // this wavefront's loads of window w landed
-            slab_barrier();                      // ... everyone's; buffer (w - 1) % D is free
-            issue(pass, w + D - 1, (w + D - 1) % D);
-            const uint8_t *xb = lds + (w % D) * S::BUF;
-            const uint8_t *cb = xb + S::XBYTES;
-            const uint8_t *sb = cb + S::CBYTES;
+            if (xwave)
+                slab_wait_vm<(S::DX - 2) * S::XL>();   // this wave's X loads of window w landed
+            else
+                slab_wait_vm<(S::DW - 2) * S::WL>();   // this wave's weight loads of window w
+            slab_barrier();   // ... everyone's; the slots of window w - 1 are free
+            if (xwave)
+                issue_x(w + S::DX - 1, (w + S::DX - 1) % S::DX);
+            else
+                issue_w(pass, w + S::DW - 1, (w + S::DW - 1) % S::DW);
+            const uint8_t *xb = lds + S::XOFF + (w % S::DX) * S::XBYTES;
+            const uint8_t *wb = lds + S::WOFF + (w % S::DW) * S::WBYTES;
+            const uint8_t *cb = wb;
+            const uint8_t *sb = wb + S::CBYTES;
             // Scale bytes of chunks past K may hold the next group's scales (a 16-byte load
             // spans two chunks); their codes are zero, and the scale is zeroed so that a NaN
             // scale there cannot reach the sum.
             const bool kvalid = 4 * w + q < CH;
+            // Step s of this consumer is k-step d_s = 2 ks + (s ^ ts) of the window (consumers
+            // with ts = 1 take their two steps in the other order), so that the remainder
+            // tile's step, 2 ks + ts, is every consumer's first.
             uint32_t code[HT][2];
             float sc[HT];
 #pragma unroll
             for (int j = 0; j < HT; j++) {
                 const int t = 2 * j + ts;
-                const u32x2_t c2 = *reinterpret_cast<const u32x2_t *>(
-                    cb + t * kSlabTileBytes + code_lane + 8 * ks);
-                code[j][0] = c2[0];
-                code[j][1] = c2[1];
+                const uint8_t *cp = cb + t * kSlabTileBytes + code_lane + 8 * ks;
+                code[j][0] = *reinterpret_cast<const uint32_t *>(cp + 4 * ts);
+                code[j][1] = *reinterpret_cast<const uint32_t *>(cp + 4 * (1 - ts));
                 const uint32_t sw = *reinterpret_cast<const uint32_t *>(
                     sb + (t >> 3) * 1024 + (t & 7) * 128 + scale_lane);
                 sc[j] = kvalid ? e4m3_to_f32<0>(sw >> sshift) : 0.0f;
@@ -276,51 +322,77 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                     sb + (t >> 3) * 1024 + (t & 7) * 128 + scale_lane);
                 rsc = kvalid ? e4m3_to_f32<0>(sw >> sshift) : 0.0f;
             }
+            // A fragments of the first step; the second step's are read during the first step's
+            // last tile, each right after its last use.
+            const uint8_t *xa0 = xb + r * kSlabRowBytes + 16 * ((4 * q + 2 * ks + ts) ^ r);
+            const uint8_t *xa1 = xb + r * kSlabRowBytes + 16 * ((4 * q + 2 * ks + 1 - ts) ^ r);
+            u32x4_t av[RB];
+#pragma unroll
+            for (int b = 0; b < RB; b++)
+                av[b] = *reinterpret_cast<const u32x4_t *>(xa0 + 16 * b * kSlabRowBytes);
             __builtin_amdgcn_sched_barrier(0);
+            // One k-step over NT tiles (the main ones, then in the first step the remainder
+            // tile): the B fragment of tile j + 1 is decoded into other registers while the
+            // MFMAs of tile j run, a few decode instructions after each MFMA.
 #pragma unroll
             for (int step = 0; step < 2; step++) {
-                const int d = 2 * ks + step;
-                u32x4_t av[RB];
-#pragma unroll
-                for (int b = 0; b < RB; b++)
-                    av[b] = *reinterpret_cast<const u32x4_t *>(
-                        xb + (16 * b + r) * kSlabRowBytes + 16 * ((4 * q + d) ^ r));
+                constexpr int kMaxNT = HT + NR;
+                const int NT = step == 0 ? HT + NR : HT;   // compile-time after unrolling
+                uint32_t cw[kMaxNT];
+                float cs[kMaxNT];
 #pragma unroll
                 for (int j = 0; j < HT; j++) {
-                    const bf16x8_t bfr = decode8_scaled(code[j][step], sc[j]);
-#pragma unroll
-                    for (int b = 0; b < RB; b++)
-                        acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[b]), bfr,
-                                                                           acc[j][b], 0, 0, 0);
+                    cw[j] = code[j][step];
+                    cs[j] = sc[j];
                 }
                 if constexpr (NR) {
-                    if (ts == step) {
-                        const bf16x8_t bfr = decode8_scaled(rcode, rsc);
+                    cw[HT] = rcode;
+                    cs[HT] = rsc;
+                }
+                bf16x8_t bcur = decode8_scaled(cw[0], cs[0]);
 #pragma unroll
-                        for (int b = 0; b < RB; b++)
-                            racc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(av[b]), bfr, racc[b], 0, 0, 0);
+                for (int j = 0; j < kMaxNT; j++) {
+                    if (j < NT) {
+                        bf16x8_t bnext = bcur;
+                        if (j + 1 < NT)
+                            bnext = decode8_scaled(cw[j + 1 < kMaxNT ? j + 1 : 0],
+                                                   cs[j + 1 < kMaxNT ? j + 1 : 0]);
+                        const bool refill = step == 0 && j == NT - 1;
+#pragma unroll
+                        for (int b = 0; b < RB; b++) {
+                            f32x4_t &acc_jb = (j < HT) ? acc[j < HT ? j : 0][b] : racc[NR ? b : 0];
+                            acc_jb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(av[b]), bcur, acc_jb, 0, 0, 0);
+                            if (refill)
+                                av[b] = *reinterpret_cast<const u32x4_t *>(
+                                    xa1 + 16 * b * kSlabRowBytes);
+                        }
+#pragma unroll
+                        for (int b = 0; b < RB; b++) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                            if (j + 1 < NT)
+                                __builtin_amdgcn_sched_group_barrier(0x002, 16 / RB + 1, 0);
+                            if (refill)
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next A
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        bcur = bnext;
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
-        // ---- end of pass: partial sums meet in LDS ----
+        // ---- end of pass: the partial sums meet in LDS as a row-major tile of Y ----
         slab_wait_vm<0>();   // the loads in flight (next pass, or zeros past the end) landed
-        slab_barrier();      // every wavefront is done with the window buffers
-        // The lane's exchange address is made opaque here, so that the compiler computes the
-        // exchange addresses in the epilogue instead of hoisting all of them out of the pass
-        // loop (where they would stay live, in registers, across every window).
-        uint32_t red_lane = 4u * (uint32_t)lane;
-        asm volatile("" : "+v"(red_lane));
-        float *red = reinterpret_cast<float *>(lds + red_lane);
-        auto red_main = [&](int tsx, int j, int b, int e) -> float & {
-            return red[(((tsx * HT + j) * RB + b) * 4 + e) * kWave];
-        };
-        auto red_rem = [&](int c, int b, int e) -> float & {
-            return red[S::RED_MAIN / 4 + ((c * RB + b) * 4 + e) * kWave];
-        };
+        slab_barrier();      // every wavefront is done with the ring buffers
+        // The lane's part of the LDS addresses is made opaque here, so that the compiler computes
+        // the exchange addresses in the epilogue instead of hoisting them out of the pass loop
+        // (where they would stay live, in registers, across every window).
+        uint32_t lane_off = 4u * (uint32_t)((4 * q) * S::YST + r);
+        asm volatile("" : "+v"(lane_off));
+        float *ys = reinterpret_cast<float *>(lds + lane_off);          // + (row0 * YST + col)
+        float *rs = reinterpret_cast<float *>(lds + S::YBYTES + 4u * (uint32_t)((4 * q) * 20 + r));
+        // (1) the k-step half ks = 1 writes its partial sums; every consumer its remainder part.
         if (ks == 1) {
 #pragma unroll
             for (int j = 0; j < HT; j++)
@@ -328,7 +400,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                 for (int b = 0; b < RB; b++) {
 #pragma unroll
                     for (int e = 0; e < 4; e++)
-                        red_main(ts, j, b, e) = acc[j][b][e];
+                        ys[(16 * b + e) * S::YST + 16 * (2 * j + ts)] = acc[j][b][e];
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
@@ -337,81 +409,116 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
             for (int b = 0; b < RB; b++)
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    red_rem(wave, b, e) = racc[b][e];
+                    rs[(wave * 16 * RB + 16 * b + e) * 20] = racc[b][e];
         }
         slab_barrier();
-
-        // out(t, b, e, v): v is the unscaled sum of Y[m0 + 16 b + 4 q + e][c0 + 16 t + r].
-        const rsrc_t ry = make_rsrc(MODE == kSlabStore ? (const void *)(a.Y + (size_t)m0 * N)
-                                                       : (const void *)a.X,
-                                    MODE == kSlabStore ? (uint32_t)max(mrows, 0) * (uint32_t)N * 4u
-                                                       : 0u);
-        auto out = [&](int t, int b, int e, float v) {
-            const int col = 16 * t + r;
-            const int row = 16 * b + 4 * q + e;
-            if constexpr (MODE == kSlabStore) {
-                __builtin_amdgcn_raw_buffer_store_b32(
-                    __float_as_uint(v * g), ry,
-                    off_if(col < ncols, ((uint32_t)row * (uint32_t)N + (uint32_t)(c0 + col)) * 4u),
-                    0, 0);
-            } else if constexpr (MODE == kSlabArgmax) {
-                if (col < ncols)
-                    best[b][e] = key_max(best[b][e], argmax_key(v * g, c0 + col));
-            } else {
-                // SiLU(gate) * up: gate columns have (col & 4) == 0, their up partner is lane + 4.
-                const float up = __shfl_xor(v, 4);
-                if ((r & 4) == 0 && col < ncols && row < mrows) {
-                    const float gt = v * g, u = up * g;
-                    const float h = gt / (1.0f + __expf(-gt)) * u;
-                    const int n = c0 + col;
-                    a.H[(size_t)(m0 + row) * (size_t)(N >> 1) + 4 * (n >> 3) + (n & 3)] =
-                        __builtin_bit_cast(uint16_t, (__bf16)h);
-                }
-            }
-        };
+        // (2) the half ks = 0 adds its own (ks1 + ks0: the same bits as ks0 + ks1); the four
+        // remainder parts are added in consumer order.
         if (ks == 0) {
 #pragma unroll
             for (int j = 0; j < HT; j++)
 #pragma unroll
                 for (int b = 0; b < RB; b++) {
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        out(pass * TW + 2 * j + ts, b, e, acc[j][b][e] + red_main(ts, j, b, e));
-                    __builtin_amdgcn_sched_barrier(0);   // one fragment at a time
+                    for (int e = 0; e < 4; e++) {
+                        float &y = ys[(16 * b + e) * S::YST + 16 * (2 * j + ts)];
+                        y = y + acc[j][b][e];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
         }
+        float *ybase = reinterpret_cast<float *>(lds);
         if constexpr (NR) {
-#pragma unroll
-            for (int b = 0; b < RB; b++) {
-                if ((b & 3) == wave) {
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const float v = ((red_rem(0, b, e) + red_rem(1, b, e)) + red_rem(2, b, e)) +
-                                        red_rem(3, b, e);
-                        out(pass * TW + 2 * HT, b, e, v);
-                    }
-                }
+            const float *rbase = reinterpret_cast<const float *>(lds + S::YBYTES);
+            for (int idx = threadIdx.x; idx < 16 * RB * 16; idx += kWave * kSlabWaves) {
+                const int row = idx >> 4, c = idx & 15;
+                const float v = ((rbase[(0 * 16 * RB + row) * 20 + c] +
+                                  rbase[(1 * 16 * RB + row) * 20 + c]) +
+                                 rbase[(2 * 16 * RB + row) * 20 + c]) +
+                                rbase[(3 * 16 * RB + row) * 20 + c];
+                ybase[row * S::YST + 16 * (2 * HT) + c] = v;
             }
         }
-        slab_barrier();   // the exchange area is reused by the next pass's windows
-        if (pass + 1 < L.passes) {
+        slab_barrier();
+        // (3) the finished tile leaves LDS row by row: columns c0 + 16 TW pass + col.
+        const int pc0 = c0 + 16 * TW * pass;                      // first column of the pass
+        const int pcols = min(ncols - 16 * TW * pass, 16 * TW);   // columns of the pass
+        if constexpr (MODE == kSlabStore) {
+            const rsrc_t ry = make_rsrc(a.Y + (size_t)m0 * N, (uint32_t)mrows * (uint32_t)N * 4u);
+            const int quads = (pcols + 3) >> 2;
+            for (int idx = threadIdx.x; idx < mrows * quads; idx += kWave * kSlabWaves) {
+                const int row = idx / quads;
+                const int col = 4 * (idx - row * quads);
+                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + col);
+                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)(pc0 + col)) * 4u;
+                if (L.vec && col + 3 < pcols) {
+                    u32x4_t o;
 #pragma unroll
-            for (int i = 0; i < D - 1; i++)
-                issue(pass + 1, i, i);
+                    for (int e = 0; e < 4; e++)
+                        o[e] = __float_as_uint(v[e] * g);
+                    __builtin_amdgcn_raw_buffer_store_b128(o, ry, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (col + e < pcols)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e] * g), ry,
+                                                                  off + 4u * e, 0, 0);
+                }
+            }
+        } else if constexpr (MODE == kSlabSilu) {
+            // Column block p of 8: gate columns 8 p .. 8 p + 3, up 8 p + 4 .. 8 p + 7 give
+            // H[m][(pc0 >> 1) + 4 p .. + 3] (pc0 and pcols are multiples of 8).
+            const int blocks = pcols >> 3;
+            const size_t hstride = (size_t)(N >> 1);
+            for (int idx = threadIdx.x; idx < mrows * blocks; idx += kWave * kSlabWaves) {
+                const int row = idx / blocks;
+                const int p8 = idx - row * blocks;
+                const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + 8 * p8);
+                const f32x4_t uv =
+                    *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + 8 * p8 + 4);
+                uint16_t hb[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float gt = gv[e] * g, u = uv[e] * g;
+                    hb[e] = __builtin_bit_cast(uint16_t, (__bf16)(gt / (1.0f + __expf(-gt)) * u));
+                }
+                uint16_t *dst = a.H + (size_t)(m0 + row) * hstride + (size_t)(pc0 >> 1) + 4 * p8;
+                if (L.vec) {
+                    *reinterpret_cast<u32x2_t *>(dst) =
+                        u32x2_t{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16),
+                                (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        dst[e] = hb[e];
+                }
+            }
+        } else {
+            // Greedy token: TPR threads per row scan its columns (col = part, part + TPR, ...)
+            // and fold them into one key; the row's key over all passes stays with those threads.
+            constexpr int TPR = (kWave * kSlabWaves) / (16 * RB);
+            const int row = threadIdx.x / TPR;
+            const int part = threadIdx.x - row * TPR;
+            argkey_t k = 0;
+            if (row < mrows)
+                for (int col = part; col < pcols; col += TPR)
+                    k = key_max(k, argmax_key(ybase[row * S::YST + col] * g, pc0 + col));
+#pragma unroll
+            for (int d = 1; d < TPR; d <<= 1)
+                k = key_max(k, shfl_xor_key(k, d));
+            best = key_max(best, k);
         }
+        slab_barrier();   // the exchange area is reused by the next pass's windows
+        if (pass + 1 < L.passes)
+            prologue(pass + 1);
     }
 
     if constexpr (MODE == kSlabArgmax) {
-        // Every consumer writes a key for every row of the slab's group (0 where it saw nothing).
-#pragma unroll
-        for (int b = 0; b < RB; b++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const argkey_t k = key_max_16(best[b][e]);
-                const int row = 16 * b + 4 * q + e;
-                if (r == 0 && row < mrows)
-                    a.keys[(size_t)(m0 + row) * L.key_slots + kSlabWaves * set + wave] = k;
-            }
+        // One key per row and workgroup: slot `set` of the row.
+        constexpr int TPR = (kWave * kSlabWaves) / (16 * RB);
+        const int row = threadIdx.x / TPR;
+        if (threadIdx.x - row * TPR == 0 && row < mrows)
+            a.keys[(size_t)(m0 + row) * L.key_slots + set] = best;
     }
 }
 
