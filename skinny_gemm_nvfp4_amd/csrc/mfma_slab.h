@@ -24,9 +24,9 @@
 //     while the MFMAs of the current one run.
 //   * Per 128-k window the whole workgroup stages X (16 RB rows x 256 bytes), the codes (1 KB
 //     per tile) and the scales (128 bytes per tile) in LDS through direct-to-LDS buffer loads
-//     (16 bytes per lane, no registers), with one barrier per window: X in a ring of 3
-//     windows loaded by wavefronts 0 and 1, the weights (from HBM, higher latency) in a ring of up
-//     to 6 loaded by wavefronts 2 and 3. Loads past the end of a row, of K or of the workgroup's
+//     (16 bytes per lane, no registers), with one barrier per window: X in a ring of 3 to 5
+//     windows loaded by wavefronts 0 and 1, the weights (from HBM, higher latency) in a ring of 4
+//     to 8 loaded by wavefronts 2 and 3. Loads past the end of a row, of K or of the workgroup's
 //     groups read zeros.
 //   * Step d of lane (r, q) covers k = 32 q + 8 d .. + 7 of the window: dword d of the lane's 16
 //     code bytes of column r, chunk q is its B fragment (decoded to bf16 with its block scale,
@@ -66,12 +66,16 @@ struct SlabShape {
     static constexpr int NSC = (TW + 7) / 8;                   // scale loads per window
     static constexpr int WBYTES = CBYTES + NSC * 1024;         // weights of one window
     static constexpr int SINK = 1024;                          // target of padding loads
-    // X comes from L2 (every workgroup of a row group reads it), the weights from HBM: the
-    // weight ring is deeper. Three X windows and as many weight windows (up to 6) as fit.
-    static constexpr int DX = 3;
+    // Ring depths from the LDS budget: X (from L2) as deep as room for 4 weight windows allows
+    // (at most 5), then the weights (from HBM) in what is left (at most 8). A window's loads are
+    // issued D - 1 windows ahead of its use, and the bytes in flight per compute unit are what
+    // sets the rate at which L2 and HBM deliver them.
+    static constexpr int DXMAX = (kSlabMaxLds - SINK - 4 * WBYTES) / XBYTES;
+    static constexpr int DX = DXMAX >= 5 ? 5 : DXMAX;
+    static_assert(DX >= 3, "slab buffers do not fit in LDS");
     static constexpr int DWMAX = (kSlabMaxLds - SINK - DX * XBYTES) / WBYTES;
-    static constexpr int DW = DWMAX >= 6 ? 6 : DWMAX;
-    static_assert(DW >= 3, "slab buffers do not fit in LDS");
+    static constexpr int DW = DWMAX >= 8 ? 8 : DWMAX;
+    static_assert(DW >= 4, "slab buffers do not fit in LDS");
     static constexpr int XOFF = 0;
     static constexpr int WOFF = DX * XBYTES;
     static constexpr int SINKOFF = WOFF + DW * WBYTES;

@@ -6,9 +6,10 @@ Inputs are the CSV files rocprofv3 writes with ``-f csv``:
 
 GEMM dispatches are the kernels of the ``nvfp4::`` namespace other than the pack kernels. They
 are matched in launch order with the labels ``bench.py --launch-log`` wrote, so every duration
-and counter is attributed to a named GEMM of a named workload. A split-K call is two dispatches
-(the batch kernel, then ``batch_reduce_kernel``); the second is folded into the first: the
-duration spans both, counters are summed.
+and counter is attributed to a named GEMM of a named workload. A call of two dispatches (the
+greedy-token call: GEMM then ``argmax_finalize_kernel``; a fused call above the dot-product rows:
+``rmsnorm_rows_kernel`` then the GEMM) counts as one: the duration spans both, counters are
+summed.
 
 HBM traffic: FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch but, on this part, do not
 necessarily count every memory channel; each is therefore scaled by bytes / counter of the
@@ -37,12 +38,11 @@ from collections import OrderedDict
 
 PACK_KERNELS = ("pack_clear_kernel", "pack_amax_kernel", "pack_scale_kernel",
                 "pack_quant_kernel")
-# Dispatches that finish a GEMM call started by the dispatch before them: the split-K reduce (plain
-# or folding into argmax keys) and the greedy-token finalize of nvfp4_gemm_argmax.
-FOLLOW_KERNELS = ("batch_reduce_kernel", "batch_reduce_argmax_kernel", "argmax_finalize_kernel",
-                  "silu_mul_kernel")
+# Dispatches that finish a GEMM call started by the dispatch before them: the greedy-token
+# finalize of nvfp4_gemm_argmax.
+FOLLOW_KERNELS = ("argmax_finalize_kernel",)
 # Dispatches that open a GEMM call whose GEMM dispatch comes next: the row-wise RMSNorm of a
-# fused call above 16 rows.
+# fused call that does not normalise inside the dot-product kernel.
 LEAD_KERNELS = ("rmsnorm_rows_kernel",)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -114,8 +114,8 @@ def _merge(into, d):
 
 
 def fold_reductions(gemms):
-    """Folds each follow-on dispatch (split-K reduce, argmax finalize, SiLU * up) into the GEMM
-    dispatch before it, and each lead dispatch (RMSNorm) into the GEMM dispatch after it."""
+    """Folds each follow-on dispatch (argmax finalize) into the GEMM dispatch before it, and each
+    lead dispatch (RMSNorm) into the GEMM dispatch after it."""
     out = []
     lead = None
     for d in gemms:
@@ -138,10 +138,6 @@ def fold_reductions(gemms):
                     prev[k] = prev.get(k, 0.0) + v
             if "argmax" in d["name"]:
                 prev["argmax"] = True
-            if "batch_reduce" in d["name"]:
-                prev["split_k"] = True
-            if "silu_mul" in d["name"]:
-                prev["fused"] = True
             continue
         out.append(d)
     if lead is not None:
@@ -174,9 +170,8 @@ def trace_summary(trace_csv: str, labels_path: str) -> str:
     for lab, ds in group(gemms).items():
         us = [d["ns"] / 1e3 for d in ds]
         d0 = ds[0]
-        kname = (short_name(d0["name"]) + (" +reduce" if d0.get("split_k") else "") +
-                 (" +argmax" if d0.get("argmax") else "") +
-                 (" +norm/silu" if d0.get("fused") else ""))
+        kname = (short_name(d0["name"]) + (" +argmax" if d0.get("argmax") else "") +
+                 (" +norm" if d0.get("fused") else ""))
         lines.append(
             f"{lab:44s} {kname[:56]:56s} {len(us):4d} "
             f"{statistics.fmean(us):8.2f} {statistics.median(us):8.2f} {min(us):8.2f}  "

@@ -77,24 +77,14 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path):
     assert r["bytes_per_launch"] == r["fetch_bytes"] + r["write_bytes"]
 
 
-BATCH = "void nvfp4::mfma_batch_kernel<3, 8, 1, 0>(nvfp4::GemmArgs)"
-REDUCE = "nvfp4::batch_reduce_kernel(float const*, int, long long, long long, float const*, float*)"
+BATCH = "void nvfp4::mfma_slab_kernel<8, 4, 1, 0>(nvfp4::GemmArgs, nvfp4::SlabLayout)"
+FINALIZE = ("nvfp4::argmax_finalize_kernel(unsigned long long const*, int, int*, float*)")
 
 
-def test_split_k_reduce_is_folded_into_its_gemm(tmp_path):
-    # batch kernel 100..2100 ns, its reduce 2200..2700: one GEMM of 2.6 us; then a plain GEMM
-    _trace(tmp_path / "t.csv", [(BATCH, 100, 2000), (REDUCE, 2200, 500), (GEMM, 5000, 1000)])
-    (tmp_path / "l.txt").write_text("s M=128 N=16 K=64\np M=1 N=16 K=64\n")
-    lines = ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt")).splitlines()
-    assert len(lines) == 3
-    assert "+reduce" in lines[1] and "    2.60" in lines[1]
-    assert "+reduce" not in lines[2] and "    1.00" in lines[2]
-
-
-def test_split_k_counters_are_summed(tmp_path):
+def test_follow_on_counters_are_summed(tmp_path):
     copy = "__amd_rocclr_copyBuffer"
-    _pmc(tmp_path / "f.csv", [(copy, [512.0]), (BATCH, [100.0]), (REDUCE, [50.0])], "FETCH_SIZE")
-    _pmc(tmp_path / "w.csv", [(copy, [1024.0]), (BATCH, [10.0]), (REDUCE, [5.0])], "WRITE_SIZE")
+    _pmc(tmp_path / "f.csv", [(copy, [512.0]), (BATCH, [100.0]), (FINALIZE, [50.0])], "FETCH_SIZE")
+    _pmc(tmp_path / "w.csv", [(copy, [1024.0]), (BATCH, [10.0]), (FINALIZE, [5.0])], "WRITE_SIZE")
     (tmp_path / "l.txt").write_text("s M=128 N=16 K=64\n")
     _, _, rows = ps.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
                                     str(tmp_path / "l.txt"), 1 << 20)
@@ -102,8 +92,8 @@ def test_split_k_counters_are_summed(tmp_path):
     assert rows["s M=128 N=16 K=64"]["write_bytes"] == 15 * 1024
 
 
-def test_reduce_without_a_gemm_is_an_error(tmp_path):
-    _trace(tmp_path / "t.csv", [(REDUCE, 100, 500)])
+def test_follow_on_without_a_gemm_is_an_error(tmp_path):
+    _trace(tmp_path / "t.csv", [(FINALIZE, 100, 500)])
     (tmp_path / "l.txt").write_text("s\n")
     with pytest.raises(ValueError):
         ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt"))
@@ -124,22 +114,16 @@ def test_mfma_busy_fraction(tmp_path):
     assert lines[1].startswith("m M=128") and lines[1].rstrip().endswith("15.6")
 
 
-FINALIZE = ("nvfp4::argmax_finalize_kernel(unsigned long long const*, int, int*, float*)")
-REDUCE_ARGMAX = ("nvfp4::batch_reduce_argmax_kernel(float const*, int, int, long long, "
-                 "float const*, unsigned long long*, int)")
-
-
 def test_argmax_follow_on_dispatches_are_folded(tmp_path):
-    # greedy-token call: GEMM 0..1000 then finalize 1100..1300 (1.3 us); a split-K greedy-token
-    # call: batch 2000..4000, reduce-argmax 4100..4400, finalize 4500..4600 (2.6 us); a plain GEMM
+    # greedy-token call: GEMM 0..1000 then finalize 1100..1300 (1.3 us); a 128-row greedy-token
+    # call: slab kernel 2000..4000, finalize 4500..4600 (2.6 us); a plain GEMM
     _trace(tmp_path / "t.csv", [(GEMM, 0, 1000), (FINALIZE, 1100, 200), (BATCH, 2000, 2000),
-                                (REDUCE_ARGMAX, 4100, 300), (FINALIZE, 4500, 100),
-                                (GEMM, 6000, 1000)])
+                                (FINALIZE, 4500, 100), (GEMM, 6000, 1000)])
     (tmp_path / "l.txt").write_text("a M=1 N=16 K=64\nb M=128 N=16 K=64\np M=1 N=16 K=64\n")
     lines = ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt")).splitlines()
     assert len(lines) == 4
     assert "+argmax" in lines[1] and "    1.30" in lines[1]
-    assert "+reduce +argmax" in lines[2] and "    2.60" in lines[2]
+    assert "+argmax" in lines[2] and "    2.60" in lines[2]
     assert "+argmax" not in lines[3] and "    1.00" in lines[3]
 
 
@@ -155,16 +139,14 @@ def test_calibration_is_the_first_copy_of_its_size(tmp_path):
 
 
 NORM = "nvfp4::rmsnorm_rows_kernel(unsigned short const*, unsigned short const*, float, int, unsigned short*)"
-SILU = "nvfp4::silu_mul_kernel(float const*, long long, int, unsigned short*)"
 
 
-def test_fused_lead_and_follow_dispatches_are_folded(tmp_path):
-    # fused call above 16 rows: RMSNorm 0..500, batch GEMM 600..2600, SiLU 2700..2900 (2.9 us);
-    # then a plain GEMM
-    _trace(tmp_path / "t.csv", [(NORM, 0, 500), (BATCH, 600, 2000), (SILU, 2700, 200),
-                                (GEMM, 5000, 1000)])
+def test_fused_lead_dispatch_is_folded(tmp_path):
+    # fused call above the dot-product rows: RMSNorm 0..500, slab GEMM (SiLU * up epilogue)
+    # 600..2600 (2.6 us); then a plain GEMM
+    _trace(tmp_path / "t.csv", [(NORM, 0, 500), (BATCH, 600, 2000), (GEMM, 5000, 1000)])
     (tmp_path / "l.txt").write_text("f M=128 N=16 K=64\np M=1 N=16 K=64\n")
     lines = ps.trace_summary(str(tmp_path / "t.csv"), str(tmp_path / "l.txt")).splitlines()
     assert len(lines) == 3
-    assert "+norm/silu" in lines[1] and "    2.90" in lines[1]
-    assert "+norm/silu" not in lines[2] and "    1.00" in lines[2]
+    assert "+norm" in lines[1] and "    2.60" in lines[1]
+    assert "+norm" not in lines[2] and "    1.00" in lines[2]
