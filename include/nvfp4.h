@@ -76,7 +76,8 @@ typedef enum {
     NVFP4_SUCCESS = 0,
     NVFP4_ERROR_INVALID_VALUE = 1,  /* bad size, null pointer or unknown path */
     NVFP4_ERROR_MISALIGNED = 2,     /* a pointer breaks the alignment rules above */
-    NVFP4_ERROR_LAUNCH = 3          /* the HIP runtime refused a kernel launch */
+    NVFP4_ERROR_LAUNCH = 3,         /* the HIP runtime refused a kernel launch */
+    NVFP4_ERROR_SCRATCH_LIMIT = 4   /* more rows than nvfp4_gemm_argmax_noalloc's scratch holds */
 } nvfp4_status_t;
 
 /*
@@ -208,6 +209,29 @@ nvfp4_status_t nvfp4_gemm_argmax_path(int path, int split, int M, int N, int K,
                                       float *value, void *workspace, uint64_t workspace_bytes,
                                       void *stream);
 
+/*
+ * nvfp4_gemm_argmax_noalloc -- nvfp4_gemm_argmax for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture that must not call hipMalloc, tight serving
+ * loops, and harnesses that forbid allocation.
+ *
+ * Same result as nvfp4_gemm_argmax with the same arguments (bit for bit: the same kernels and
+ * plan). The per-row keys go to a 4 MiB array in device memory that the library holds for the
+ * process's lifetime, one copy per GPU; its device address is looked up on the first call on each
+ * device (with that device current). The call never calls hipMalloc, hipFree or any allocating
+ * routine, and writes every key it reads, so nothing needs clearing between calls.
+ *
+ *   M, N, K, X, Wq, Wscale, gscale, index, value, stream   as for nvfp4_gemm_argmax
+ * Limit: M <= 4 MiB / (8 * 16 * compute units), i.e. 128 rows on a 256-CU MI355X; more returns
+ * NVFP4_ERROR_SCRATCH_LIMIT (use nvfp4_gemm_argmax with a workspace, or split the rows).
+ * Concurrency: every call on one GPU shares the array; calls that overlap in time on one GPU
+ * (other streams, other host threads, other graphs replaying) race and give undefined results.
+ * Calls on different GPUs do not interfere. Other errors as for nvfp4_gemm_argmax.
+ */
+nvfp4_status_t nvfp4_gemm_argmax_noalloc(int M, int N, int K, const uint16_t *X,
+                                         const uint8_t *Wq, const uint8_t *Wscale,
+                                         const float *gscale, int32_t *index, float *value,
+                                         void *stream);
+
 /* Workspace bytes nvfp4_gemm_argmax needs for M rows on the current device:
  * 8 * 16 * (compute units) per row (room for 16 8-byte keys per compute unit; the kernels write
  * at most 4 per compute unit); 0 if M < 1. */
@@ -316,7 +340,7 @@ uint64_t nvfp4_scales_bytes(int N, int K);
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define NVFP4_ABI_VERSION 6
+#define NVFP4_ABI_VERSION 7
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

@@ -18,6 +18,7 @@ SUCCESS = 0
 ERROR_INVALID_VALUE = 1
 ERROR_MISALIGNED = 2
 ERROR_LAUNCH = 3
+ERROR_SCRATCH_LIMIT = 4
 
 PATH_AUTO = 0
 PATH_DOT = 1
@@ -65,6 +66,8 @@ def load_library() -> ctypes.CDLL:
     L.nvfp4_gemm_argmax_path.argtypes = [ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp,
                                          ctypes.c_uint64, vp]
     L.nvfp4_gemm_argmax_path.restype = ci
+    L.nvfp4_gemm_argmax_noalloc.argtypes = [ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_gemm_argmax_noalloc.restype = ci
     L.nvfp4_argmax_workspace_bytes.argtypes = [ci]
     L.nvfp4_argmax_workspace_bytes.restype = ctypes.c_uint64
     L.nvfp4_gemm_grouped.argtypes = [ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, ci, vp]
@@ -123,6 +126,12 @@ def nvfp4_gemm_argmax_path(path: int, split: int, M: int, N: int, K: int, X: int
                            workspace_bytes: int, stream: Optional[int]) -> int:
     return load_library().nvfp4_gemm_argmax_path(path, split, M, N, K, X, Wq, Wscale, gscale,
                                                  index, value, workspace, workspace_bytes, stream)
+
+
+def nvfp4_gemm_argmax_noalloc(M: int, N: int, K: int, X: int, Wq: int, Wscale: int, gscale: int,
+                              index: int, value: int, stream: Optional[int]) -> int:
+    return load_library().nvfp4_gemm_argmax_noalloc(M, N, K, X, Wq, Wscale, gscale, index, value,
+                                                    stream)
 
 
 def nvfp4_argmax_workspace_bytes(M: int) -> int:

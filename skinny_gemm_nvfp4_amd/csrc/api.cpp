@@ -152,6 +152,41 @@ nvfp4_status_t nvfp4_gemm_argmax(int M, int N, int K, const uint16_t *X, const u
                                   workspace, workspace_bytes, stream);
 }
 
+nvfp4_status_t nvfp4_gemm_argmax_noalloc(int M, int N, int K, const uint16_t *X,
+                                         const uint8_t *Wq, const uint8_t *Wscale,
+                                         const float *gscale, int32_t *index, float *value,
+                                         void *stream)
+{
+    if (!sizes_ok(M, N, K))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!X || !Wq || !Wscale || !gscale || !index || !value)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(gscale, 4) ||
+        !aligned(index, 4) || !aligned(value, 4))
+        return NVFP4_ERROR_MISALIGNED;
+    if (M > nvfp4::argmax_scratch_rows())
+        return NVFP4_ERROR_SCRATCH_LIMIT;
+    int p = NVFP4_PATH_AUTO, s = 0;
+    if (!nvfp4::choose_config(M, N, K, &p, &s))
+        return NVFP4_ERROR_INVALID_VALUE;
+    unsigned long long *keys = nullptr;
+    if (nvfp4::argmax_scratch(&keys) != hipSuccess)
+        return NVFP4_ERROR_LAUNCH;
+    nvfp4::GemmArgs a;
+    a.X = X;
+    a.Wq = Wq;
+    a.Ws = Wscale;
+    a.gscale = gscale;
+    a.Y = nullptr;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.keys = keys;
+    a.key_slots = 0;
+    return from_hip(nvfp4::launch_gemm_argmax(p, s, a, index, value,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status_t nvfp4_gemm_grouped(int T, int E, int N, int K, const uint16_t *X,
                                   const int32_t *offsets, const uint8_t *Wq,
                                   const uint8_t *Wscale, const float *gscale, float *Y,
@@ -244,6 +279,8 @@ const char *nvfp4_status_string(nvfp4_status_t status)
     case NVFP4_ERROR_INVALID_VALUE: return "invalid value (size, null pointer or path)";
     case NVFP4_ERROR_MISALIGNED: return "misaligned pointer";
     case NVFP4_ERROR_LAUNCH: return "kernel launch failed";
+    case NVFP4_ERROR_SCRATCH_LIMIT:
+        return "more rows than the static scratch of nvfp4_gemm_argmax_noalloc holds";
     }
     return "unknown status";
 }

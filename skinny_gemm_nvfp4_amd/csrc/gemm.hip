@@ -600,6 +600,42 @@ hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *i
 
 int device_compute_units() { return compute_units(); }
 
+// Keys of nvfp4_gemm_argmax_noalloc: a fixed 4 MiB array in device memory, one copy per GPU the
+// library runs on, held until the process ends. Every call on a GPU uses the same array (calls
+// that overlap in time on one GPU race on it). Host code never passes `scratch` itself to a
+// kernel: on the host the name is only a handle, and its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) argkey_t scratch[kScratchKeys];
+
+int argmax_scratch_rows()
+{
+    return (int)(kScratchKeys / ((size_t)kArgmaxSlotsPerCu * (size_t)compute_units()));
+}
+
+hipError_t argmax_scratch(argkey_t **keys)
+{
+    static std::atomic<argkey_t *> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    argkey_t *p = cache[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void *q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (q == nullptr)
+            return hipErrorInvalidSymbol;
+        p = static_cast<argkey_t *>(q);
+        cache[dev].store(p, std::memory_order_release);
+    }
+    *keys = p;
+    return hipSuccess;
+}
+
 namespace {
 
 // Whether nvfp4_gemm_fused runs everything inside the dot-product kernel (up to 4 rows, X in LDS).

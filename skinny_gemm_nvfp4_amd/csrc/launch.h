@@ -108,6 +108,16 @@ constexpr int kArgmaxSlotsPerCu = 16;
 hipError_t launch_gemm_argmax(int path, int split, const GemmArgs &a, int32_t *index,
                               float *value, hipStream_t stream);
 
+// nvfp4_gemm_argmax_noalloc keeps its keys in a static device array of kScratchKeys keys (4 MiB).
+constexpr size_t kScratchKeys = (size_t)(4u << 20) / sizeof(unsigned long long);
+
+// Rows that array holds on the current device: kScratchKeys / (kArgmaxSlotsPerCu * compute
+// units), 128 on a 256-CU device.
+int argmax_scratch_rows();
+
+// Device address of that array on the current device (looked up once per device).
+hipError_t argmax_scratch(unsigned long long **keys);
+
 // Launch of nvfp4_gemm_fused: RMSNorm prologue (a.gamma) and/or SiLU(gate) * up epilogue (a.H).
 // The normalised X goes to a.workspace when fused_workspace_bytes() is not zero.
 hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t stream);

@@ -54,8 +54,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert nv.abi_version() == 6
-    for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH):
+    assert nv.abi_version() == 7
+    for st in (nv.SUCCESS, nv.ERROR_INVALID_VALUE, nv.ERROR_MISALIGNED, nv.ERROR_LAUNCH,
+               nv.ERROR_SCRATCH_LIMIT):
         assert nv.status_string(st)
     assert nv.status_string(99) == "unknown status"
 
@@ -210,6 +211,31 @@ def test_argmax_rejects_small_workspace_and_bad_paths(lib):
     assert _argmax(1, 16, 256, path=6) == nv.ERROR_INVALID_VALUE
     assert _argmax(9, 16, 256, path=nv.PATH_DOT) == nv.ERROR_INVALID_VALUE
     assert _argmax(16, 16, 256, path=nv.PATH_INVARIANT, split=2) == nv.ERROR_INVALID_VALUE
+
+
+def test_argmax_noalloc_host_checks(lib):
+    """nvfp4_gemm_argmax_noalloc: the same size, pointer and alignment rules as the workspace
+    entry point, and more rows than its 4 MiB key array holds (128 on 256 compute units, the
+    count the library assumes without a device) return NVFP4_ERROR_SCRATCH_LIMIT, all before
+    any HIP call."""
+    good = [A16, A16B, A16C, A16D, A8F, A8G]
+
+    def call(M, N, K, p=None):
+        return nv.nvfp4_gemm_argmax_noalloc(M, N, K, *(p or good), None)
+
+    assert call(0, 16, 256) == nv.ERROR_INVALID_VALUE
+    assert call(1, 16, 24) == nv.ERROR_INVALID_VALUE
+    for i in range(len(good)):
+        bad = list(good)
+        bad[i] = 0
+        assert call(1, 16, 256, bad) == nv.ERROR_INVALID_VALUE, i
+    for i, off in [(0, 8), (1, 8), (2, 4), (3, 2), (4, 2), (5, 2)]:
+        bad = list(good)
+        bad[i] += off
+        assert call(1, 16, 256, bad) == nv.ERROR_MISALIGNED, i
+    assert call(129, 16, 256) == nv.ERROR_SCRATCH_LIMIT
+    assert call(4096, 16, 256) == nv.ERROR_SCRATCH_LIMIT
+    assert "static scratch" in nv.status_string(nv.ERROR_SCRATCH_LIMIT)
 
 
 # ---- nvfp4_gemm_grouped: sizes, experts, pointers, alignment, rows per item ----
