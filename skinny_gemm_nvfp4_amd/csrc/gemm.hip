@@ -290,15 +290,9 @@ int mfma_default_waves(int N, int K)
     return kMfmaTiles[P.tc_index] >= 6 ? 4 : 8;
 }
 
-// Slab kernel plan for a slab of `rows` <= 128 rows: row groups of RG = 16 RB rows, tile sets,
-// tiles per pass (TW = 2 HT + NR) and passes, from a cycle estimate per compute unit and window
-// (128 k). A window costs the slowest of: a consumer's MFMAs (about 17 cycles each, plus a fifth
-// for the decode of its B fragments, measured with interleaved decode on gfx950); the X and weight
-// bytes through the compute unit's L2 port (64 bytes per cycle); the LDS traffic (128 bytes per
-// cycle: the staged window, plus every consumer's A fragments of its two k-steps); the weight
-// bytes at the compute unit's share of HBM (13 bytes per cycle, counting each weight once per
-// tile set: the row groups of a set share an XCD and its L2). Each pass also pays one pipeline
-// fill (about 4000 cycles).
+// Slab kernel plan for a slab of `rows` <= 128 rows: row groups of RG = 16 RB rows, tile sets
+// (S = compute units / row groups, a multiple of 8), tiles per pass (TW = 2 HT + NR, at most 9) and
+// passes.
 struct SlabPlan {
     int rbi, rb;    // row blocks of a row group: index into 1, 2, 4, 8, and the count
     int rg;         // rows per row group: 16 * (the plan's row blocks), before trimming to the slab
@@ -308,8 +302,6 @@ struct SlabPlan {
     int lds;
     int gunit;
 };
-
-constexpr double kSlabFill = 4000.0;
 
 int rb_index(int rb) { return rb <= 1 ? 0 : rb <= 2 ? 1 : rb <= 4 ? 2 : 3; }
 
@@ -340,54 +332,54 @@ bool slab_plan(int rows, int N, int K, bool pair, int rg_req, SlabPlan *P)
     const int units = num_groups(N) / unit;
     if (units < 1)
         return false;
-    const double nwin = (K + kSlabWindow - 1) / kSlabWindow;
-    bool found = false;
-    double best = 0.0;
-    for (int rg = 16; rg <= 128; rg *= 2) {
-        if (rg_req != 0 && rg != rg_req)
-            continue;
+    // Automatic choice: 128-row groups when every compute unit has at least 4 tiles with them,
+    // else 64-row groups (measured on the layer shapes at M = 128: q/k/v 28.4 us with 64-row
+    // groups against 31.5 with 128 and 31.6 with 32; o_proj 25.9 / 31.3 / 28.6; down (K = 17408)
+    // 73.7 / 90.8 / 82.6; gate/up, 8.5 tiles per compute unit, 73 with 128 against 88 with 64).
+    int rg_auto = 128;
+    if (rg_req == 0) {
+        const int S1 = std::max(1, std::min(cus - cus % 8, units));
+        const int tiles1 = (unit * ((units + S1 - 1) / S1) + 3) / 4;
+        rg_auto = (tiles1 >= 4 || rows <= 64) ? 128 : 64;
+    }
+    auto try_rg = [&](int rg) {
         const int Pg = (rows + rg - 1) / rg;
         if (Pg > cus)
-            continue;
+            return false;
         int S = cus / Pg;
         if (S >= 8)
             S -= S % 8;
         S = std::max(1, std::min(S, units));
         const int gmax = unit * ((units + S - 1) / S);
         if (!bytes_fit(N, K, S, pair))
-            continue;
+            return false;
         const int T = (gmax + 3) / 4;
         int ht, nr, passes;
         slab_passes(T, &ht, &nr, &passes);
         const int rb = rb_for_rows(std::min(rows, rg));
         const int lds = kSlabLds[rb_index(rb)][ht - 1][nr];
         if (lds > kMaxLds)
-            continue;
-        const int tw = 2 * ht + nr;
-        const double mfma = 17.0 * 1.2 * tw * rb;                 // per consumer and window
-        const double wbytes = tw * (kSlabTileBytes + 128.0);
-        const double xbytes = 16.0 * rb * kSlabRowBytes;
-        const double l2 = (wbytes + xbytes) / 64.0;
-        const double ldsc = (wbytes + xbytes + kSlabWaves * 2.0 * rb * 1024.0) / 128.0;
-        const double hbm = wbytes / Pg / 13.0 * (double)(Pg * S) / cus;
-        const double win = std::max(std::max(mfma, l2), std::max(ldsc, hbm));
-        const double cost = passes * (nwin * win + kSlabFill);
-        if (!found || cost < best - 1e-9) {
-            found = true;
-            best = cost;
-            P->rg = rg;
-            P->rb = rb;
-            P->rbi = rb_index(rb);
-            P->P = Pg;
-            P->S = S;
-            P->ht = ht;
-            P->nr = nr;
-            P->passes = passes;
-            P->lds = lds;
-            P->gunit = unit;
-        }
-    }
-    return found;
+            return false;
+        P->rg = rg;
+        P->rb = rb;
+        P->rbi = rb_index(rb);
+        P->P = Pg;
+        P->S = S;
+        P->ht = ht;
+        P->nr = nr;
+        P->passes = passes;
+        P->lds = lds;
+        P->gunit = unit;
+        return true;
+    };
+    if (rg_req != 0)
+        return try_rg(rg_req);
+    if (try_rg(rg_auto))
+        return true;
+    for (int rg = 128; rg >= 16; rg /= 2)   // any plan that fits
+        if (try_rg(rg))
+            return true;
+    return false;
 }
 
 // Batch-invariant mode: one plan per (N, K), the plan of a full 128-row slab, used for every

@@ -16,28 +16,30 @@
 //     of X; the row groups of one tile set get workgroup ids that are equal modulo 8, which the
 //     dispatcher places on the same XCD, so the weights they share are fetched from HBM once and
 //     served to the others by that XCD's L2.
-//   * Workgroup of 4 wavefronts, one per SIMD. Consumer c = 2 ts + ks takes the main tiles ts,
-//     ts + 2, ... (HT of them) and, of every 128-k window, the MFMA k-steps 2 ks and 2 ks + 1
-//     (in the order 2 ks + ts, 2 ks + 1 - ts); with NR = 1 the last tile's four k-steps go one to
-//     each consumer (step 2 ks + ts, its first). Every consumer thus multiplies the same number
-//     of tile-steps, and each weight is decoded once. The B fragment of the next tile is decoded
-//     while the MFMAs of the current one run.
+//   * Workgroup of 8 wavefronts, two per SIMD (wavefront w runs on SIMD w % 4), so that one
+//     wavefront's MFMAs run while the other of its SIMD decodes, reads LDS or waits. Consumer w
+//     takes k-step ks = w % 4 of every 128-k window and the main tiles ts, ts + 2, ... (HT of
+//     them), ts = w / 4; with NR = 1 the last tile's four k-steps go one to each SIMD (k-step
+//     ks to the wavefront with ts = ks % 2). Every weight is decoded once, every A fragment read
+//     from LDS by the two wavefronts of its k-step. Per window a wavefront decodes the B
+//     fragments of all its tiles, then runs the MFMAs row block by row block; the other
+//     wavefront of its SIMD issues MFMAs while it decodes or waits.
 //   * Per 128-k window the whole workgroup stages X (16 RB rows x 256 bytes), the codes (1 KB
 //     per tile) and the scales (128 bytes per tile) in LDS through direct-to-LDS buffer loads
 //     (16 bytes per lane, no registers), with one barrier per window: X in a ring of 3 to 5
-//     windows loaded by wavefronts 0 and 1, the weights (from HBM, higher latency) in a ring of 4
-//     to 8 loaded by wavefronts 2 and 3. Loads past the end of a row, of K or of the workgroup's
-//     groups read zeros.
+//     windows loaded by wavefronts 0-3, the weights (from HBM, higher latency) in a ring of 4 to
+//     8 loaded by wavefronts 4-7, one loader of each kind per SIMD. Loads past the end of a row,
+//     of K or of the workgroup's groups read zeros.
 //   * Step d of lane (r, q) covers k = 32 q + 8 d .. + 7 of the window: dword d of the lane's 16
 //     code bytes of column r, chunk q is its B fragment (decoded to bf16 with its block scale,
 //     exact), and row 16 b + r of X at those k its A fragment of row block b
 //     (v_mfma_f32_16x16x32_bf16). X rows sit in LDS with piece kp of row m at slot kp ^ (m & 15),
 //     so the 16 rows of an A fragment hit 16 different bank groups.
-//   * At the end of a pass the ks = 1 consumers' partial sums (and all four of the remainder
-//     tile) meet the others' in LDS, in a fixed order, as a row-major tile of Y; then all 256
-//     threads write whole rows of it (16-byte stores), Y = sum * g. Results are reproducible.
-//     Weights with more tiles per workgroup than TW are done in several passes, each streaming
-//     X again.
+//   * At the end of a pass the four k-step partial sums of every output meet in LDS in a fixed
+//     order (((ks3 + ks2) + ks1) + ks0, and the remainder tile's four parts likewise) as a
+//     row-major tile of Y; then all 512 threads write whole rows of it (16-byte stores),
+//     Y = sum * g. Results are reproducible. Weights with more tiles per workgroup than TW are
+//     done in several passes, each streaming X again.
 //   * MODE 0 stores Y; MODE 1 folds Y into argmax keys (argmax.h), one slot per row and tile
 //     set; MODE 2 writes H = bf16(SiLU(gate) * up) of an interleaved gate/up weight.
 #pragma once
@@ -49,7 +51,7 @@
 namespace nvfp4 {
 
 constexpr int kSlabWindow = 128;
-constexpr int kSlabWaves = 4;
+constexpr int kSlabWaves = 8;
 constexpr int kSlabRowBytes = 256;      // one 128-k row of bf16 X
 constexpr int kSlabTileBytes = 1024;    // codes of one 16-column tile and window
 constexpr int kSlabMaxLds = 160 * 1024;
@@ -79,11 +81,12 @@ struct SlabShape {
     static constexpr int XOFF = 0;
     static constexpr int WOFF = DX * XBYTES;
     static constexpr int SINKOFF = WOFF + DW * WBYTES;
-    // Waves 0 and 1 issue the X loads (2 RB each per window), waves 2 and 3 the weight loads
-    // (codes then scales, the same count each, padded).
-    static constexpr int XL = 2 * RB;
+    // Waves 0-3 issue the X loads (16 RB rows, 4 per load: RB loads each per window), waves 4-7
+    // the weight loads (codes then scales, the same count each, padded).
+    static constexpr int XL = RB;
     static constexpr int NWL = TW + NSC;
-    static constexpr int WL = (NWL + 1) / 2;
+    static constexpr int WL = (NWL + 3) / 4;
+    static_assert((DX - 2) * XL < 64 && (DW - 2) * WL < 64, "vmcnt range");
     // End of a pass: Y as a row-major tile [16 RB][YST] (the row padding keeps the four rows a
     // fragment writes on different banks), and the remainder tile's four parts [4][16 RB][20].
     static constexpr int YST = 16 * TW + 4;
@@ -140,13 +143,15 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
 {
     using S = SlabShape<RB, HT, NR>;
     constexpr int TW = S::TW;
+    constexpr int kThreads = kWave * kSlabWaves;
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int r = lane & 15;
     const int q = lane >> 4;
-    const int ks = wave & 1;
-    const int ts = wave >> 1;
+    const int ks = wave & 3;    // k-step of every window (= the SIMD)
+    const int ts = wave >> 2;   // main tiles ts, ts + 2, ...
+    const bool rem = NR != 0 && ts == (ks & 1);   // takes k-step ks of the remainder tile
     const int K = a.K;
     const int N = a.N;
     const int CH = num_chunks(K);
@@ -184,66 +189,62 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
     const float g = *a.gscale;
 
     // ---- load side ----
-    // Waves 0 and 1 load X windows into the X ring, waves 2 and 3 weight windows into the
-    // weight ring (each load kind in waves of its own, so that waiting for a fast X load never
-    // waits for older weight loads: loads complete in issue order). Every call issues the same
-    // number of loads whatever the window (past the pass's last window they read zeros; padding
-    // loads write zeros into the sink), so waiting for a window is a fixed count of outstanding
-    // loads. A load's lane offset is a loop-invariant register plus a scalar part; rows past the
-    // group and column groups past the workgroup's lie beyond the descriptors' ranges and read
-    // zeros by themselves, so only the window holding the end of K masks lanes.
-    //   X: load i of X wave xw covers rows 4 u .. 4 u + 3 of the window, u = xw + 2 i; lane l
-    //      fetches piece (l % 16) ^ (row & 15) of row 4 u + l / 16 into LDS slot l % 16 (the
-    //      piece depends on u only through u % 4, i.e. on xw and i % 2).
-    //   W: load v = (wave - 2) + 2 j of the window's list: v < TW the codes of tile v (lane l:
+    // Waves 0-3 load X windows into the X ring, waves 4-7 weight windows into the weight ring
+    // (each load kind in waves of its own, so that waiting for a fast X load never waits for
+    // older weight loads: loads complete in issue order). Every call issues the same number of
+    // loads whatever the window (past the pass's last window they read zeros; padding loads write
+    // zeros into the sink), so waiting for a window is a fixed count of outstanding loads. A
+    // load's lane offset is a loop-invariant register plus a scalar part; rows past the group and
+    // column groups past the workgroup's lie beyond the descriptors' ranges and read zeros by
+    // themselves, so only the window holding the end of K masks lanes.
+    //   X: load i of X wave xw covers rows 4 u .. 4 u + 3 of the window, u = xw + 4 i; lane l
+    //      fetches piece (l % 16) ^ (row & 15) of row 4 u + l / 16 into LDS slot l % 16 (row & 15
+    //      = (4 xw + l / 16) & 15 does not depend on i).
+    //   W: load v = (wave - 4) + 4 j of the window's list: v < TW the codes of tile v (lane l:
     //      group l / 16 of the tile, 16-byte piece l % 16 of its 256 bytes, = LDS order); then
     //      the scales of tiles 8 (v - TW) .. + 7 (lane l: tile 8 (v - TW) + l / 8, group
     //      (l / 2) % 4, 16-byte half l % 2 of its 32 bytes: chunks 2 (l % 2), 2 (l % 2) + 1).
-    const bool xwave = wave < 2;
-    const int xw = wave & 1;
-    const int xrow0 = 4 * xw + (lane >> 4);                   // row of load 0 (u = xw)
-    const int xrow1 = 4 * (xw + 2) + (lane >> 4);             // row of load 1 (u = xw + 2)
-    const int xkp0 = (lane & 15) ^ (xrow0 & 15);
-    const int xkp1 = (lane & 15) ^ (xrow1 & 15);
-    const uint32_t xlane0 = (uint32_t)xrow0 * (uint32_t)K * 2u + (uint32_t)xkp0 * 16u;
-    const uint32_t xlane1 = (uint32_t)xrow1 * (uint32_t)K * 2u + (uint32_t)xkp1 * 16u;
-    const uint32_t xstep = 16u * (uint32_t)K * 2u;            // 16 rows: load i to i + 2
+    const bool xwave = wave < 4;
+    const int xw = wave & 3;
+    const int xrow = 4 * xw + (lane >> 4);                    // row of load 0 (u = xw)
+    const int xkp = (lane & 15) ^ (xrow & 15);
+    const uint32_t xlane = (uint32_t)xrow * (uint32_t)K * 2u + (uint32_t)xkp * 16u;
+    const uint32_t xstep = 16u * (uint32_t)K * 2u;            // 16 rows: load i to i + 1
     const uint32_t clane = (uint32_t)(lane >> 4) * gq + (uint32_t)(lane & 15) * 16u;
     const uint32_t slane = (uint32_t)(4 * (lane >> 3) + ((lane >> 1) & 3)) * gs +
                            (uint32_t)(lane & 1) * 16u;
     const int nfull = K / kSlabWindow;                        // windows with no K tail
     auto issue_x = [&](int w, int slot) {
         uint8_t *base = lds + S::XOFF + slot * S::XBYTES;
-        const bool full = w < nfull;
-        const bool live = w < nwin;
-        const uint32_t xwo = (uint32_t)w * (kSlabWindow * 2);
-        const bool ok0 = full || (live && kSlabWindow * w + 8 * xkp0 < K);
-        const bool ok1 = full || (live && kSlabWindow * w + 8 * xkp1 < K);
+        // Only the window holding the end of K (and those past it) masks lanes.
+        const uint32_t lo = (w < nfull || (w < nwin && kSlabWindow * w + 8 * xkp < K))
+                                ? xlane + (uint32_t)w * (kSlabWindow * 2)
+                                : kOutOfRange;
+        // (kOutOfRange plus any row step stays beyond every descriptor's range.)
 #pragma unroll
-        for (int i = 0; i < S::XL; i++) {
-            const int u = xw + 2 * i;
-            const bool ok = (i & 1) ? ok1 : ok0;
-            const uint32_t lo = ((i & 1) ? xlane1 : xlane0) + xwo + (uint32_t)(i >> 1) * xstep;
-            slab_lds_load16(rx, base + u * 1024, ok ? lo : kOutOfRange);
-        }
+        for (int i = 0; i < S::XL; i++)
+            slab_lds_load16(rx, base + (xw + 4 * i) * 1024, lo + (uint32_t)i * xstep);
     };
     auto issue_w = [&](int pass, int w, int slot) {
         uint8_t *base = lds + S::WOFF + slot * S::WBYTES;
         const bool full = w < nfull;
         const bool live = w < nwin;
+        const uint32_t cw0 = (uint32_t)(4 * pass * TW) * gq + (uint32_t)w * 256u;
+        const uint32_t sw0 = (uint32_t)(4 * pass * TW) * gs + (uint32_t)w * 32u;
+        // Lanes past K (and every lane past the last window) start at kOutOfRange; adding a
+        // tile's offset keeps them beyond every descriptor's range.
+        const uint32_t cl = (full || (live && 4 * w + ((lane & 15) >> 2) < CH)) ? clane + cw0
+                                                                               : kOutOfRange;
+        const uint32_t sl = (full || (live && 4 * w + 2 * (lane & 1) < CH)) ? slane + sw0
+                                                                          : kOutOfRange;
 #pragma unroll
         for (int j = 0; j < S::WL; j++) {
-            const int v = (wave - 2) + 2 * j;
+            const int v = (wave - 4) + 4 * j;
             if (v < TW) {
-                const bool ok = full || (live && 4 * w + ((lane & 15) >> 2) < CH);
-                const uint32_t sc = (uint32_t)(4 * (pass * TW + v)) * gq + (uint32_t)w * 256u;
-                slab_lds_load16(rq, base + v * kSlabTileBytes, ok ? clane + sc : kOutOfRange);
+                slab_lds_load16(rq, base + v * kSlabTileBytes, cl + (uint32_t)(4 * v) * gq);
             } else if (v < S::NWL) {
-                const bool ok = full || (live && 4 * w + 2 * (lane & 1) < CH);
-                const uint32_t sc =
-                    (uint32_t)(4 * (pass * TW + 8 * (v - TW))) * gs + (uint32_t)w * 32u;
                 slab_lds_load16(rs, base + S::CBYTES + (v - TW) * 1024,
-                                ok ? slane + sc : kOutOfRange);
+                                sl + (uint32_t)(32 * (v - TW)) * gs);
             } else {
                 slab_lds_load16(rq, lds + S::SINKOFF, kOutOfRange);
             }
@@ -263,9 +264,15 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
     };
 
     // ---- consume side ----
-    const uint32_t code_lane = (uint32_t)(r >> 2) * 256u + (uint32_t)q * 64u + (uint32_t)(r & 3) * 16u;
-    const uint32_t scale_lane = (uint32_t)(r >> 2) * 32u + (uint32_t)q * 8u + (uint32_t)(r & 2) * 2u;
-    const uint32_t sshift = 16u * (uint32_t)(r & 1) + 8u * (uint32_t)ks;
+    // Lane (r, q) of k-step d: dword d of the 16 code bytes of column r, chunk q (k = 32 q + 8 d
+    // .. + 7), whose block scale is byte d / 2 of the column's two for the chunk (scale bytes of
+    // a tile and window: group r / 4 at 32 (r / 4), chunk q at + 8 q, column r % 4 at + 2 (r % 4)).
+    const uint32_t code_lane = (uint32_t)(r >> 2) * 256u + (uint32_t)q * 64u +
+                               (uint32_t)(r & 3) * 16u + 4u * (uint32_t)ks;
+    const uint32_t scale_lane = (uint32_t)(r >> 2) * 32u + (uint32_t)q * 8u +
+                                (uint32_t)(r & 3) * 2u + (uint32_t)(ks >> 1);
+    // A fragment of k-step ks, row block b: row 16 b + r, 16-byte piece 4 q + ks (slot ^ r).
+    const uint32_t a_lane = (uint32_t)r * kSlabRowBytes + 16u * (uint32_t)((4 * q + ks) ^ r);
 
     prologue(0);
 
@@ -293,96 +300,62 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                 issue_x(w + S::DX - 1, (w + S::DX - 1) % S::DX);
             else
                 issue_w(pass, w + S::DW - 1, (w + S::DW - 1) % S::DW);
-            const uint8_t *xb = lds + S::XOFF + (w % S::DX) * S::XBYTES;
-            const uint8_t *wb = lds + S::WOFF + (w % S::DW) * S::WBYTES;
-            const uint8_t *cb = wb;
-            const uint8_t *sb = wb + S::CBYTES;
+            // Per-window LDS bases of this lane (made opaque so that the compiler adds the
+            // per-tile and per-row-block offsets as immediates instead of keeping one address
+            // register per tile across the loop).
+            uint32_t xoff = (uint32_t)(S::XOFF + (w % S::DX) * S::XBYTES) + a_lane;
+            uint32_t woff = (uint32_t)(S::WOFF + (w % S::DW) * S::WBYTES);
+            uint32_t coff = woff + code_lane;
+            uint32_t soff = woff + (uint32_t)S::CBYTES + scale_lane;
+            asm volatile("" : "+v"(xoff), "+v"(coff), "+v"(soff));
             // Scale bytes of chunks past K may hold the next group's scales (a 16-byte load
             // spans two chunks); their codes are zero, and the scale is zeroed so that a NaN
-            // scale there cannot reach the sum.
-            const bool kvalid = 4 * w + q < CH;
-            // Step s of this consumer is k-step d_s = 2 ks + (s ^ ts) of the window (consumers
-            // with ts = 1 take their two steps in the other order), so that the remainder
-            // tile's step, 2 ks + ts, is every consumer's first.
-            uint32_t code[HT][2];
-            float sc[HT];
+            // scale there cannot reach the sum (only in the window holding the end of K).
+            const bool kvalid = w < nfull || 4 * w + q < CH;
+            constexpr int NT = HT + (NR ? 1 : 0);
+            uint32_t cw[NT];
+            uint32_t sb[NT];
 #pragma unroll
-            for (int j = 0; j < HT; j++) {
-                const int t = 2 * j + ts;
-                const uint8_t *cp = cb + t * kSlabTileBytes + code_lane + 8 * ks;
-                code[j][0] = *reinterpret_cast<const uint32_t *>(cp + 4 * ts);
-                code[j][1] = *reinterpret_cast<const uint32_t *>(cp + 4 * (1 - ts));
-                const uint32_t sw = *reinterpret_cast<const uint32_t *>(
-                    sb + (t >> 3) * 1024 + (t & 7) * 128 + scale_lane);
-                sc[j] = kvalid ? e4m3_to_f32<0>(sw >> sshift) : 0.0f;
+            for (int j = 0; j < NT; j++) {
+                const int t = j < HT ? 2 * j + ts : 2 * HT;
+                if (j < HT || rem) {
+                    cw[j] = *reinterpret_cast<const uint32_t *>(lds + coff + t * kSlabTileBytes);
+                    sb[j] = lds[soff + (t >> 3) * 1024 + (t & 7) * 128];
+                } else {
+                    cw[j] = 0;
+                    sb[j] = 0;
+                }
             }
-            uint32_t rcode = 0;
-            float rsc = 0.0f;
-            if constexpr (NR) {
-                constexpr int t = 2 * HT;
-                rcode = *reinterpret_cast<const uint32_t *>(cb + t * kSlabTileBytes + code_lane +
-                                                            4 * (2 * ks + ts));
-                const uint32_t sw = *reinterpret_cast<const uint32_t *>(
-                    sb + (t >> 3) * 1024 + (t & 7) * 128 + scale_lane);
-                rsc = kvalid ? e4m3_to_f32<0>(sw >> sshift) : 0.0f;
-            }
-            // A fragments of the first step; the second step's are read during the first step's
-            // last tile, each right after its last use.
-            const uint8_t *xa0 = xb + r * kSlabRowBytes + 16 * ((4 * q + 2 * ks + ts) ^ r);
-            const uint8_t *xa1 = xb + r * kSlabRowBytes + 16 * ((4 * q + 2 * ks + 1 - ts) ^ r);
             u32x4_t av[RB];
 #pragma unroll
             for (int b = 0; b < RB; b++)
-                av[b] = *reinterpret_cast<const u32x4_t *>(xa0 + 16 * b * kSlabRowBytes);
-            __builtin_amdgcn_sched_barrier(0);
-            // One k-step over NT tiles (the main ones, then in the first step the remainder
-            // tile): the B fragment of tile j + 1 is decoded into other registers while the
-            // MFMAs of tile j run, a few decode instructions after each MFMA.
+                av[b] = *reinterpret_cast<const u32x4_t *>(lds + xoff + 16 * b * kSlabRowBytes);
+            // Tile by tile: the B fragment of tile j + 1 is decoded while the MFMAs of tile j
+            // run, a few decode instructions after each MFMA.
+            bf16x8_t bcur = decode8_scaled(cw[0], kvalid ? e4m3_to_f32<0>(sb[0]) : 0.0f);
 #pragma unroll
-            for (int step = 0; step < 2; step++) {
-                constexpr int kMaxNT = HT + NR;
-                const int NT = step == 0 ? HT + NR : HT;   // compile-time after unrolling
-                uint32_t cw[kMaxNT];
-                float cs[kMaxNT];
+            for (int j = 0; j < NT; j++) {
+                if (j == HT && !rem)
+                    break;
+                bf16x8_t bnext = bcur;
+                if (j + 1 < NT)
+                    bnext = decode8_scaled(cw[j + 1 < NT ? j + 1 : j],
+                                           kvalid ? e4m3_to_f32<0>(sb[j + 1 < NT ? j + 1 : j])
+                                                  : 0.0f);
 #pragma unroll
-                for (int j = 0; j < HT; j++) {
-                    cw[j] = code[j][step];
-                    cs[j] = sc[j];
+                for (int b = 0; b < RB; b++) {
+                    f32x4_t &c = j < HT ? acc[j < HT ? j : 0][b] : racc[NR ? b : 0];
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[b]), bcur, c, 0, 0,
+                                                                0);
                 }
-                if constexpr (NR) {
-                    cw[HT] = rcode;
-                    cs[HT] = rsc;
+#pragma unroll
+                for (int b = 0; b < RB; b++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    if (j + 1 < NT)
+                        __builtin_amdgcn_sched_group_barrier(0x002, 16 / RB + 1, 0);
                 }
-                bf16x8_t bcur = decode8_scaled(cw[0], cs[0]);
-#pragma unroll
-                for (int j = 0; j < kMaxNT; j++) {
-                    if (j < NT) {
-                        bf16x8_t bnext = bcur;
-                        if (j + 1 < NT)
-                            bnext = decode8_scaled(cw[j + 1 < kMaxNT ? j + 1 : 0],
-                                                   cs[j + 1 < kMaxNT ? j + 1 : 0]);
-                        const bool refill = step == 0 && j == NT - 1;
-#pragma unroll
-                        for (int b = 0; b < RB; b++) {
-                            f32x4_t &acc_jb = (j < HT) ? acc[j < HT ? j : 0][b] : racc[NR ? b : 0];
-                            acc_jb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(av[b]), bcur, acc_jb, 0, 0, 0);
-                            if (refill)
-                                av[b] = *reinterpret_cast<const u32x4_t *>(
-                                    xa1 + 16 * b * kSlabRowBytes);
-                        }
-#pragma unroll
-                        for (int b = 0; b < RB; b++) {
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                            if (j + 1 < NT)
-                                __builtin_amdgcn_sched_group_barrier(0x002, 16 / RB + 1, 0);
-                            if (refill)
-                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next A
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        bcur = bnext;
-                    }
-                }
+                __builtin_amdgcn_sched_barrier(0);
+                bcur = bnext;
             }
         }
 
@@ -396,61 +369,54 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
         asm volatile("" : "+v"(lane_off));
         float *ys = reinterpret_cast<float *>(lds + lane_off);          // + (row0 * YST + col)
         float *rs = reinterpret_cast<float *>(lds + S::YBYTES + 4u * (uint32_t)((4 * q) * 20 + r));
-        // (1) the k-step half ks = 1 writes its partial sums; every consumer its remainder part.
-        if (ks == 1) {
+        // k-steps 3, 2, 1, 0 in turn: the first writes its sums, the others add theirs. The
+        // remainder holders write their part to their k-step's slot with the first round.
 #pragma unroll
-            for (int j = 0; j < HT; j++)
+        for (int round = 3; round >= 0; round--) {
+            if (ks == round) {
 #pragma unroll
-                for (int b = 0; b < RB; b++) {
+                for (int j = 0; j < HT; j++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        ys[(16 * b + e) * S::YST + 16 * (2 * j + ts)] = acc[j][b][e];
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-        }
-        if constexpr (NR) {
+                    for (int b = 0; b < RB; b++) {
 #pragma unroll
-            for (int b = 0; b < RB; b++)
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    rs[(wave * 16 * RB + 16 * b + e) * 20] = racc[b][e];
-        }
-        slab_barrier();
-        // (2) the half ks = 0 adds its own (ks1 + ks0: the same bits as ks0 + ks1); the four
-        // remainder parts are added in consumer order.
-        if (ks == 0) {
-#pragma unroll
-            for (int j = 0; j < HT; j++)
-#pragma unroll
-                for (int b = 0; b < RB; b++) {
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        float &y = ys[(16 * b + e) * S::YST + 16 * (2 * j + ts)];
-                        y = y + acc[j][b][e];
+                        for (int e = 0; e < 4; e++) {
+                            float &y = ys[(16 * b + e) * S::YST + 16 * (2 * j + ts)];
+                            y = round == 3 ? acc[j][b][e] : y + acc[j][b][e];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (NR != 0) {
+                if (round == 3 && rem) {
+#pragma unroll
+                    for (int b = 0; b < RB; b++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            rs[(ks * 16 * RB + 16 * b + e) * 20] = racc[b][e];
                 }
+            }
+            slab_barrier();
         }
         float *ybase = reinterpret_cast<float *>(lds);
-        if constexpr (NR) {
+        if constexpr (NR != 0) {
             const float *rbase = reinterpret_cast<const float *>(lds + S::YBYTES);
-            for (int idx = threadIdx.x; idx < 16 * RB * 16; idx += kWave * kSlabWaves) {
+            for (int idx = threadIdx.x; idx < 16 * RB * 16; idx += kThreads) {
                 const int row = idx >> 4, c = idx & 15;
-                const float v = ((rbase[(0 * 16 * RB + row) * 20 + c] +
-                                  rbase[(1 * 16 * RB + row) * 20 + c]) +
-                                 rbase[(2 * 16 * RB + row) * 20 + c]) +
-                                rbase[(3 * 16 * RB + row) * 20 + c];
+                const float v = ((rbase[(3 * 16 * RB + row) * 20 + c] +
+                                  rbase[(2 * 16 * RB + row) * 20 + c]) +
+                                 rbase[(1 * 16 * RB + row) * 20 + c]) +
+                                rbase[(0 * 16 * RB + row) * 20 + c];
                 ybase[row * S::YST + 16 * (2 * HT) + c] = v;
             }
+            slab_barrier();
         }
-        slab_barrier();
-        // (3) the finished tile leaves LDS row by row: columns c0 + 16 TW pass + col.
+        // The finished tile leaves LDS row by row: columns c0 + 16 TW pass + col.
         const int pc0 = c0 + 16 * TW * pass;                      // first column of the pass
         const int pcols = min(ncols - 16 * TW * pass, 16 * TW);   // columns of the pass
         if constexpr (MODE == kSlabStore) {
             const rsrc_t ry = make_rsrc(a.Y + (size_t)m0 * N, (uint32_t)mrows * (uint32_t)N * 4u);
             const int quads = (pcols + 3) >> 2;
-            for (int idx = threadIdx.x; idx < mrows * quads; idx += kWave * kSlabWaves) {
+            for (int idx = threadIdx.x; idx < mrows * quads; idx += kThreads) {
                 const int row = idx / quads;
                 const int col = 4 * (idx - row * quads);
                 const f32x4_t v = *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + col);
@@ -474,7 +440,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
             // H[m][(pc0 >> 1) + 4 p .. + 3] (pc0 and pcols are multiples of 8).
             const int blocks = pcols >> 3;
             const size_t hstride = (size_t)(N >> 1);
-            for (int idx = threadIdx.x; idx < mrows * blocks; idx += kWave * kSlabWaves) {
+            for (int idx = threadIdx.x; idx < mrows * blocks; idx += kThreads) {
                 const int row = idx / blocks;
                 const int p8 = idx - row * blocks;
                 const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + 8 * p8);
@@ -500,7 +466,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
         } else {
             // Greedy token: TPR threads per row scan its columns (col = part, part + TPR, ...)
             // and fold them into one key; the row's key over all passes stays with those threads.
-            constexpr int TPR = (kWave * kSlabWaves) / (16 * RB);
+            constexpr int TPR = kThreads / (16 * RB);
             const int row = threadIdx.x / TPR;
             const int part = threadIdx.x - row * TPR;
             argkey_t k = 0;
@@ -519,7 +485,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
 
     if constexpr (MODE == kSlabArgmax) {
         // One key per row and workgroup: slot `set` of the row.
-        constexpr int TPR = (kWave * kSlabWaves) / (16 * RB);
+        constexpr int TPR = kThreads / (16 * RB);
         const int row = threadIdx.x / TPR;
         if (threadIdx.x - row * TPR == 0 && row < mrows)
             a.keys[(size_t)(m0 + row) * L.key_slots + set] = best;
