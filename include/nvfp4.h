@@ -133,9 +133,9 @@ typedef enum {
                              one 16-row block of X per workgroup; any M */
     NVFP4_PATH_BATCH = 3, /* matrix cores, every weight decoded once per workgroup for slabs of
                              up to 128 rows of X: X, codes and scales staged in LDS by
-                             direct-to-LDS loads, four wavefronts splitting each tile's k-steps;
-                             narrow weights cut the rows into row groups. Any M, meant for
-                             M > 16. (Value 4 is not a path.) */
+                             direct-to-LDS loads, eight wavefronts (two per SIMD) splitting each
+                             window's four k-steps; narrow weights cut the rows into row groups.
+                             Any M, meant for M > 16. (Value 4 is not a path.) */
     NVFP4_PATH_INVARIANT = 5 /* batch-invariant mode: row m of Y is the same bits for every M
                              and whatever the other rows of X hold. A request verified alone
                              or with others then gets exactly the bits its own M = 1 call in
@@ -144,8 +144,11 @@ typedef enum {
                              sections). Every call that must agree, plain decode included, has
                              to use this mode: nvfp4_gemm at M = 1 picks another kernel and
                              other bits, and nvfp4_gemm_fused has no invariant mode. The slab
-                             kernel with one plan per (N, K) for all M, the plan nvfp4_gemm
-                             takes for 128 rows; slower than NVFP4_PATH_AUTO at small M.
+                             kernel for all M: its sum for an output runs over the 128-k
+                             windows in order in each of four k-step lanes, then adds the lanes
+                             in a fixed order, so no plan choice (row groups, tile sets, tiles
+                             per pass) changes a row's bits, and each call takes the plan that
+                             suits its rows; slower than NVFP4_PATH_AUTO at small M.
                              split must be 0. */
 } nvfp4_path_t;
 

@@ -69,23 +69,22 @@ struct SlabShape {
     static constexpr int WBYTES = CBYTES + NSC * 1024;         // weights of one window
     static constexpr int SINK = 1024;                          // target of padding loads
     // Ring depths from the LDS budget: X (from L2) as deep as room for 4 weight windows allows
-    // (at most 5), then the weights (from HBM) in what is left (at most 8). A window's loads are
-    // issued D - 1 windows ahead of its use, and the bytes in flight per compute unit are what
-    // sets the rate at which L2 and HBM deliver them.
-    static constexpr int DXMAX = (kSlabMaxLds - SINK - 4 * WBYTES) / XBYTES;
-    static constexpr int DX = DXMAX >= 5 ? 5 : DXMAX;
-    static_assert(DX >= 3, "slab buffers do not fit in LDS");
-    static constexpr int DWMAX = (kSlabMaxLds - SINK - DX * XBYTES) / WBYTES;
-    static constexpr int DW = DWMAX >= 8 ? 8 : DWMAX;
-    static_assert(DW >= 4, "slab buffers do not fit in LDS");
+    // (3 to 5 windows), then the weights (from HBM) in what is left (4 to 8). A window's loads
+    // are issued D - 1 windows ahead of its use. (Deeper rings measured slower: 16 X and 24
+    // weight windows took q/k/v at one row from 21 to 25 us.)
+    static constexpr int XL = RB;                 // X loads per X wavefront and window
+    static constexpr int NWL = TW + NSC;
+    static constexpr int WL = (NWL + 3) / 4;      // weight loads per weight wavefront and window
+    static constexpr int BUDGET = kSlabMaxLds - SINK;
+    static constexpr int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
+    static constexpr int DX = clampi((BUDGET - 4 * WBYTES) / XBYTES, 3, 5);
+    static constexpr int DW = clampi((BUDGET - DX * XBYTES) / WBYTES, 4, 8);
+    static_assert(DX * XBYTES + DW * WBYTES <= BUDGET, "slab buffers do not fit in LDS");
     static constexpr int XOFF = 0;
     static constexpr int WOFF = DX * XBYTES;
     static constexpr int SINKOFF = WOFF + DW * WBYTES;
     // Waves 0-3 issue the X loads (16 RB rows, 4 per load: RB loads each per window), waves 4-7
     // the weight loads (codes then scales, the same count each, padded).
-    static constexpr int XL = RB;
-    static constexpr int NWL = TW + NSC;
-    static constexpr int WL = (NWL + 3) / 4;
     static_assert((DX - 2) * XL < 64 && (DW - 2) * WL < 64, "vmcnt range");
     // End of a pass: Y as a row-major tile [16 RB][YST] (the row padding keeps the four rows a
     // fragment writes on different banks), and the remainder tile's four parts [4][16 RB][20].
