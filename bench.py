@@ -691,7 +691,7 @@ def main() -> int:
             err = np.abs(y.cpu().numpy().astype(np.float64) - Yref)
             worst = max(worst, float((err / oracle.tolerance(A)).max()))
         parity = {"workload": "dense_layer_m1 (seeds 1-6)",
-                  "worst_err_over_bound": round(worst, 4), "pass": worst <= 1.0}
+                  "worst_err_over_bound": float(f"{worst:.3g}"), "pass": worst <= 1.0}
         if worst > 1.0:
             raise RuntimeError(f"GPU output outside tolerance (worst ratio {worst})")
 

@@ -214,9 +214,11 @@ int stream_wg_per_cu(int M, int N, int K, bool pair)
 }
 
 // Workgroups and LDS layout of the dot-product kernel; false if X does not fit in LDS.
-bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L, bool pair = false)
+// (norm: the kernel normalises X itself, once per workgroup: one workgroup per CU.)
+bool stream_plan(int M, int N, int K, int MR, int W, int *grid, StreamLayout *L, bool pair = false,
+                 bool norm = false)
 {
-    const int G = std::max(1, std::min(compute_units() * stream_wg_per_cu(M, N, K, pair),
+    const int G = std::max(1, std::min(compute_units() * stream_wg_per_cu(M, N, K, pair || norm),
                                        num_groups(N) / (pair ? 2 : 1)));
     const int u = pair ? 2 : 1;   // groups are dealt in units of u
     L->nwin = (K + kStreamWindow - 1) / kStreamWindow;
@@ -464,7 +466,8 @@ hipError_t launch_impl(int path, int split, const GemmArgs &a0, int32_t *index, 
     if (path == kPathDot) {
         StreamLayout L;
         int grid = 0;
-        if (!stream_plan(a.M, a.N, a.K, a.M, split, &grid, &L, a.H != nullptr))
+        if (!stream_plan(a.M, a.N, a.K, a.M, split, &grid, &L, a.H != nullptr,
+                         a.gamma != nullptr))
             return hipErrorInvalidValue;
         const int fast = (a.K % kStreamWindow == 0) ? 1 : 0;
         const StreamFn fn = kStream[fast][a.M - 1][wave_index(split)];
@@ -617,10 +620,12 @@ hipError_t argmax_scratch(argkey_t **keys)
 namespace {
 
 // Whether nvfp4_gemm_fused runs everything inside the dot-product kernel (up to 4 rows, X in LDS).
+// (One row takes 12 wavefronts in one workgroup per CU here, whatever the weight's size: the
+// RMSNorm prologue runs once per workgroup.)
 bool fused_in_dot(int M, int N, int K, bool pair, int *waves, StreamLayout *L, int *grid)
 {
-    *waves = dot_default_waves(M, N, K);
-    return M <= 4 && stream_plan(M, N, K, M, *waves, grid, L, pair);
+    *waves = M == 1 ? 12 : dot_default_waves(M, N, K);
+    return M <= 4 && stream_plan(M, N, K, M, *waves, grid, L, pair, true);
 }
 
 }  // namespace
