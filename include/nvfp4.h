@@ -77,7 +77,12 @@ typedef enum {
     NVFP4_ERROR_INVALID_VALUE = 1,  /* bad size, null pointer or unknown path */
     NVFP4_ERROR_MISALIGNED = 2,     /* a pointer breaks the alignment rules above */
     NVFP4_ERROR_LAUNCH = 3,         /* the HIP runtime refused a kernel launch */
-    NVFP4_ERROR_SCRATCH_LIMIT = 4   /* more rows than nvfp4_gemm_argmax_noalloc's scratch holds */
+    NVFP4_ERROR_SCRATCH_LIMIT = 4,  /* more rows than nvfp4_gemm_argmax_noalloc's scratch holds */
+    /* Not statuses: they make the type span every int, so that any int a caller passes to
+     * nvfp4_status_string is a valid value of it (a C++ enumeration only holds the values its
+     * enumerators' bits can express). */
+    NVFP4_STATUS_ENUM_MIN_ = -2147483647 - 1,
+    NVFP4_STATUS_ENUM_MAX_ = 2147483647
 } nvfp4_status_t;
 
 /*

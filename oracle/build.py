@@ -12,14 +12,14 @@ SRC = os.path.join(HERE, "nvfp4_oracle.c")
 LIB = os.path.join(HERE, "libnvfp4_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, extra_flags: tuple = (), out: str = LIB) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", *extra_flags, "-o", out + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

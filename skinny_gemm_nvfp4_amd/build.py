@@ -48,9 +48,9 @@ def compile_flags() -> list:
             "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, flags: list, out_dir: str) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,20 +64,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libnvfp4.so. Always recompiles."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _build(out: str, flags: list, link_flags: list, obj_dir: str, verbose: bool) -> str:
+    os.makedirs(obj_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, flags, obj_dir), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_flags, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("link of libnvfp4.so failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libnvfp4.so. Always recompiles."""
+    return _build(LIB, compile_flags(), [], BUILD_DIR, verbose)
 
 
 if __name__ == "__main__":

@@ -281,6 +281,7 @@ const char *nvfp4_status_string(nvfp4_status_t status)
     case NVFP4_ERROR_LAUNCH: return "kernel launch failed";
     case NVFP4_ERROR_SCRATCH_LIMIT:
         return "more rows than the static scratch of nvfp4_gemm_argmax_noalloc holds";
+    default: break;
     }
     return "unknown status";
 }

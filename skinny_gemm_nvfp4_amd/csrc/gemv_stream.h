@@ -85,7 +85,6 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     const int K = a.K;
     const int N = a.N;
     const int CH = num_chunks(K);
-    const int NG = num_groups(N);
     const int b = blockIdx.x;
     const int g0 = L.gunit * (b * L.gq + min(b, L.gr));
     const int ngroups = L.gunit * (L.gq + (b < L.gr ? 1 : 0));

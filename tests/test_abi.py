@@ -325,3 +325,71 @@ def test_fused_workspace_rules(lib):
         nv.ERROR_INVALID_VALUE                                                          # null
     assert _fused(nv.FUSE_RMSNORM, 128, 16, 5120, ws=A16F + 8, ws_bytes=need) == \
         nv.ERROR_MISALIGNED
+
+
+# ---- plan choice with no GPU: every configuration is either rejected or reaches the launch ----
+
+def _device_visible() -> bool:
+    """False when the HIP runtime reports no device: then no call can start a kernel, so the
+    library may be handed plausible-looking addresses that pass every host check."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return True
+    n = ctypes.c_int(0)
+    return hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0
+
+
+SWEEP_M = (1, 2, 3, 4, 5, 8, 9, 16, 17, 33, 48, 49, 64, 65, 127, 128, 129, 257, 1000)
+SWEEP_N = (16, 48, 80, 1040, 4352, 5120, 7168, 34816, 151936, 262144)
+SWEEP_K = (16, 272, 640, 2176, 5120, 17408, 65536)
+SPLITS = (0, 4, 8, 12, 16, 32, 64, 128)
+
+
+def test_plans_cover_every_shape_without_a_device(lib):
+    """Every planner runs on the host: for each shape, path and split the call either rejects the
+    configuration (NVFP4_ERROR_INVALID_VALUE) or chooses a plan and reaches the first HIP call,
+    which fails without a device (NVFP4_ERROR_LAUNCH). The automatic path, the batch and
+    batch-invariant paths and the matrix-core path accept every shape here; the dot path every
+    M <= 8. Planners assume 256 compute units when no device answers."""
+    if _device_visible():
+        pytest.skip("a GPU is visible: this sweep passes addresses that must never reach a kernel")
+    inv, launch = nv.ERROR_INVALID_VALUE, nv.ERROR_LAUNCH
+    ptrs = [A16, A16B, A16C, A16D, A16E]
+    for M in SWEEP_M:
+        for N in SWEEP_N:
+            for K in SWEEP_K:
+                for path in range(6):
+                    for split in SPLITS:
+                        st = nv.nvfp4_gemm_path(path, split, M, N, K, *ptrs, None)
+                        assert st in (inv, launch), (M, N, K, path, split, st)
+                accepts = [nv.PATH_AUTO, nv.PATH_MFMA, nv.PATH_BATCH, nv.PATH_INVARIANT]
+                if M <= 8:
+                    accepts.append(nv.PATH_DOT)
+                for path in accepts:
+                    st = nv.nvfp4_gemm_path(path, 0, M, N, K, *ptrs, None)
+                    assert st == launch, (M, N, K, path, st)
+                st = _argmax(M, N, K)
+                assert st == launch, (M, N, K, st)
+                for path in range(6):
+                    assert _argmax(M, N, K, path=path) in (inv, launch), (M, N, K, path)
+                st = nv.nvfp4_gemm_argmax_noalloc(M, N, K, A16, A16B, A16C, A16D, A8F, A8G, None)
+                assert st == (launch if M <= 128 else nv.ERROR_SCRATCH_LIMIT), (M, N, K, st)
+                for fuse in (nv.FUSE_RMSNORM, nv.FUSE_SILU_MUL,
+                             nv.FUSE_RMSNORM | nv.FUSE_SILU_MUL):
+                    need = nv.nvfp4_fused_workspace_bytes(fuse, M, N, K)
+                    st = _fused(fuse, M, N, K, ws=A16F if need else 0, ws_bytes=need)
+                    assert st == launch, (M, N, K, fuse, st)
+
+
+def test_grouped_plans_without_a_device(lib):
+    """The grouped call's plan for any token count, expert count and rows per item: accepted
+    configurations reach the first HIP call (NVFP4_ERROR_LAUNCH without a device)."""
+    if _device_visible():
+        pytest.skip("a GPU is visible: this sweep passes addresses that must never reach a kernel")
+    for T in (1, 2, 8, 15, 16, 17, 128, 1000):
+        for E in (1, 8, 64, 128, 2048):
+            for N, K in ((16, 16), (1536, 2048), (2048, 768), (5120, 17408)):
+                for rpi in (0, 1, 2, 4):
+                    st = _grouped(T, E, N, K, rpi=rpi)
+                    assert st == nv.ERROR_LAUNCH, (T, E, N, K, rpi, st)
