@@ -308,30 +308,31 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
             uint32_t soff = woff + (uint32_t)S::CBYTES + scale_lane;
             asm volatile("" : "+v"(xoff), "+v"(coff), "+v"(soff));
             // Scale bytes of chunks past K may hold the next group's scales (a 16-byte load
-            // spans two chunks); their codes are zero, and the scale is zeroed so that a NaN
-            // scale there cannot reach the sum (only in the window holding the end of K).
-            const bool kvalid = w < nfull || 4 * w + q < CH;
+            // spans two chunks); their codes are zero, and the scale byte is cleared so that a
+            // NaN scale there cannot reach the sum (only in the window holding the end of K).
+            // The clearing is a mask on the byte, not a condition on its conversion: a condition
+            // splits the tile loop into blocks the scheduler cannot interleave.
+            const uint32_t smask = (w < nfull || 4 * w + q < CH) ? 0xFFu : 0u;
             constexpr int NT = HT + (NR ? 1 : 0);
             uint32_t cw[NT];
             uint32_t sb[NT];
+            // Every LDS read of the window goes out before any arithmetic, the remainder tile's
+            // too (its slot exists when NR = 1; a wave that does not own it ignores the values).
 #pragma unroll
             for (int j = 0; j < NT; j++) {
                 const int t = j < HT ? 2 * j + ts : 2 * HT;
-                if (j < HT || rem) {
-                    cw[j] = *reinterpret_cast<const uint32_t *>(lds + coff + t * kSlabTileBytes);
-                    sb[j] = lds[soff + (t >> 3) * 1024 + (t & 7) * 128];
-                } else {
-                    cw[j] = 0;
-                    sb[j] = 0;
-                }
+                cw[j] = *reinterpret_cast<const uint32_t *>(lds + coff + t * kSlabTileBytes);
+                sb[j] = lds[soff + (t >> 3) * 1024 + (t & 7) * 128] & smask;
             }
             u32x4_t av[RB];
 #pragma unroll
             for (int b = 0; b < RB; b++)
                 av[b] = *reinterpret_cast<const u32x4_t *>(lds + xoff + 16 * b * kSlabRowBytes);
+            __builtin_amdgcn_sched_barrier(0);
             // Tile by tile: the B fragment of tile j + 1 is decoded while the MFMAs of tile j
-            // run, a few decode instructions after each MFMA.
-            bf16x8_t bcur = decode8_scaled(cw[0], kvalid ? e4m3_to_f32<0>(sb[0]) : 0.0f);
+            // run, a few decode instructions after each MFMA. The remainder tile's fragment is
+            // decoded with the last main tile, before the branch on who owns it.
+            bf16x8_t bcur = decode8_scaled(cw[0], e4m3_to_f32<0>(sb[0]));
 #pragma unroll
             for (int j = 0; j < NT; j++) {
                 if (j == HT && !rem)
@@ -339,8 +340,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                 bf16x8_t bnext = bcur;
                 if (j + 1 < NT)
                     bnext = decode8_scaled(cw[j + 1 < NT ? j + 1 : j],
-                                           kvalid ? e4m3_to_f32<0>(sb[j + 1 < NT ? j + 1 : j])
-                                                  : 0.0f);
+                                           e4m3_to_f32<0>(sb[j + 1 < NT ? j + 1 : j]));
 #pragma unroll
                 for (int b = 0; b < RB; b++) {
                     f32x4_t &c = j < HT ? acc[j < HT ? j : 0][b] : racc[NR ? b : 0];
@@ -354,6 +354,8 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                         __builtin_amdgcn_sched_group_barrier(0x002, 16 / RB + 1, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                if (NR && j + 1 == HT)
+                    asm volatile("" : "+v"(bnext));   // keeps the decode ahead of the branch
                 bcur = bnext;
             }
         }
