@@ -44,6 +44,8 @@
 //     set; MODE 2 writes H = bf16(SiLU(gate) * up) of an interleaved gate/up weight.
 #pragma once
 
+#include <type_traits>
+
 #include "argmax.h"
 #include "device.h"
 #include "launch.h"
@@ -213,19 +215,28 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
     const uint32_t slane = (uint32_t)(4 * (lane >> 3) + ((lane >> 1) & 3)) * gs +
                            (uint32_t)(lane & 1) * 16u;
     const int nfull = K / kSlabWindow;                        // windows with no K tail
-    auto issue_x = [&](int w, int slot) {
-        uint8_t *base = lds + S::XOFF + slot * S::XBYTES;
+    // A window's loads: a set-up per window, then one call per load, so that the loads can go
+    // out one at a time between the MFMAs of the window before.
+    struct XIssue {
+        uint8_t *base;
+        uint32_t lo;
+    };
+    auto x_setup = [&](int w, int slot) -> XIssue {
         // Only the window holding the end of K (and those past it) masks lanes.
         const uint32_t lo = (w < nfull || (w < nwin && kSlabWindow * w + 8 * xkp < K))
                                 ? xlane + (uint32_t)w * (kSlabWindow * 2)
                                 : kOutOfRange;
         // (kOutOfRange plus any row step stays beyond every descriptor's range.)
-#pragma unroll
-        for (int i = 0; i < S::XL; i++)
-            slab_lds_load16(rx, base + (xw + 4 * i) * 1024, lo + (uint32_t)i * xstep);
+        return XIssue{lds + S::XOFF + slot * S::XBYTES, lo};
     };
-    auto issue_w = [&](int pass, int w, int slot) {
-        uint8_t *base = lds + S::WOFF + slot * S::WBYTES;
+    auto x_load = [&](const XIssue &x, int i) {
+        slab_lds_load16(rx, x.base + (xw + 4 * i) * 1024, x.lo + (uint32_t)i * xstep);
+    };
+    struct WIssue {
+        uint8_t *base;
+        uint32_t cl, sl;
+    };
+    auto w_setup = [&](int pass, int w, int slot) -> WIssue {
         const bool full = w < nfull;
         const bool live = w < nwin;
         const uint32_t cw0 = (uint32_t)(4 * pass * TW) * gq + (uint32_t)w * 256u;
@@ -236,29 +247,41 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                                                                                : kOutOfRange;
         const uint32_t sl = (full || (live && 4 * w + 2 * (lane & 1) < CH)) ? slane + sw0
                                                                           : kOutOfRange;
-#pragma unroll
-        for (int j = 0; j < S::WL; j++) {
-            const int v = (wave - 4) + 4 * j;
-            if (v < TW) {
-                slab_lds_load16(rq, base + v * kSlabTileBytes, cl + (uint32_t)(4 * v) * gq);
-            } else if (v < S::NWL) {
-                slab_lds_load16(rs, base + S::CBYTES + (v - TW) * 1024,
-                                sl + (uint32_t)(32 * (v - TW)) * gs);
-            } else {
-                slab_lds_load16(rq, lds + S::SINKOFF, kOutOfRange);
-            }
-        }
+        return WIssue{lds + S::WOFF + slot * S::WBYTES, cl, sl};
+    };
+    // Load j of a weight wave: item v = (wave - 4) + 4 j of the window's list. The kind of item
+    // depends on the wave, so it is chosen by selects rather than branches (a branch would cut
+    // the tile loop the load sits in into pieces the scheduler cannot interleave).
+    auto w_load = [&](const WIssue &x, int j) {
+        const int v = (wave - 4) + 4 * j;
+        const bool code = v < TW;
+        const bool scale = !code && v < S::NWL;
+        uint8_t *dst = code    ? x.base + v * kSlabTileBytes
+                       : scale ? x.base + S::CBYTES + (v - TW) * 1024
+                               : lds + S::SINKOFF;
+        const uint32_t off = code    ? x.cl + (uint32_t)(4 * v) * gq
+                             : scale ? x.sl + (uint32_t)(32 * (v - TW)) * gs
+                                     : kOutOfRange;
+        slab_lds_load16(code ? rq : rs, dst, off);
     };
     // The first windows of a pass: D - 1 windows ahead of their use, in each ring.
     auto prologue = [&](int pass) {
         if (xwave) {
 #pragma unroll
-            for (int i = 0; i < S::DX - 1; i++)
-                issue_x(i, i);
+            for (int i = 0; i < S::DX - 1; i++) {
+                const XIssue x = x_setup(i, i);
+#pragma unroll
+                for (int l = 0; l < S::XL; l++)
+                    x_load(x, l);
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < S::DW - 1; i++)
-                issue_w(pass, i, i);
+            for (int i = 0; i < S::DW - 1; i++) {
+                const WIssue x = w_setup(pass, i, i);
+#pragma unroll
+                for (int l = 0; l < S::WL; l++)
+                    w_load(x, l);
+            }
         }
     };
 
@@ -289,76 +312,106 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
         for (int b = 0; b < (NR ? RB : 1); b++)
             racc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-        for (int w = 0; w < nwin; w++) {
-            if (xwave)
-                slab_wait_vm<(S::DX - 2) * S::XL>();   // this wave's X loads of window w landed
-            else
-                slab_wait_vm<(S::DW - 2) * S::WL>();   // this wave's weight loads of window w
-            slab_barrier();   // ... everyone's; the slots of window w - 1 are free
-            if (xwave)
-                issue_x(w + S::DX - 1, (w + S::DX - 1) % S::DX);
-            else
-                issue_w(pass, w + S::DW - 1, (w + S::DW - 1) % S::DW);
-            // Per-window LDS bases of this lane (made opaque so that the compiler adds the
-            // per-tile and per-row-block offsets as immediates instead of keeping one address
-            // register per tile across the loop).
-            uint32_t xoff = (uint32_t)(S::XOFF + (w % S::DX) * S::XBYTES) + a_lane;
-            uint32_t woff = (uint32_t)(S::WOFF + (w % S::DW) * S::WBYTES);
-            uint32_t coff = woff + code_lane;
-            uint32_t soff = woff + (uint32_t)S::CBYTES + scale_lane;
-            asm volatile("" : "+v"(xoff), "+v"(coff), "+v"(soff));
-            // Scale bytes of chunks past K may hold the next group's scales (a 16-byte load
-            // spans two chunks); their codes are zero, and the scale byte is cleared so that a
-            // NaN scale there cannot reach the sum (only in the window holding the end of K).
-            // The clearing is a mask on the byte, not a condition on its conversion: a condition
-            // splits the tile loop into blocks the scheduler cannot interleave.
-            const uint32_t smask = (w < nfull || 4 * w + q < CH) ? 0xFFu : 0u;
-            constexpr int NT = HT + (NR ? 1 : 0);
-            uint32_t cw[NT];
-            uint32_t sb[NT];
-            // Every LDS read of the window goes out before any arithmetic, the remainder tile's
-            // too (its slot exists when NR = 1; a wave that does not own it ignores the values).
+        // The window loop, one copy per loader role, so that the role's loads (known at compile
+        // time) can be placed between the MFMAs: issued all at once after the barrier they queue
+        // behind each other in the compute unit's load pipeline, and the waves issuing them
+        // stall before their first MFMA.
+        auto windows = [&](auto role) {
+            constexpr bool XR = decltype(role)::value;
+            constexpr int D = XR ? S::DX : S::DW;    // ring depth of this role's loads
+            constexpr int NL = XR ? S::XL : S::WL;   // its loads per window
+            for (int w = 0; w < nwin; w++) {
+                slab_wait_vm<(D - 2) * NL>();   // this wave's loads of window w landed
+                slab_barrier();                 // ... everyone's; the slots of window w - 1 are free
+                // The loads of window w + D - 1 (into the slot of window w - 1).
+                const int lw = w + D - 1;
+                XIssue xi{};
+                WIssue wi{};
+                if constexpr (XR)
+                    xi = x_setup(lw, lw % D);
+                else
+                    wi = w_setup(pass, lw, lw % D);
+                // Per-window LDS bases of this lane (made opaque so that the compiler adds the
+                // per-tile and per-row-block offsets as immediates instead of keeping one address
+                // register per tile across the loop).
+                uint32_t xoff = (uint32_t)(S::XOFF + (w % S::DX) * S::XBYTES) + a_lane;
+                uint32_t woff = (uint32_t)(S::WOFF + (w % S::DW) * S::WBYTES);
+                uint32_t coff = woff + code_lane;
+                uint32_t soff = woff + (uint32_t)S::CBYTES + scale_lane;
+                asm volatile("" : "+v"(xoff), "+v"(coff), "+v"(soff));
+                // Scale bytes of chunks past K may hold the next group's scales (a 16-byte load
+                // spans two chunks); their codes are zero, and the scale byte is cleared so that
+                // a NaN scale there cannot reach the sum (only in the window holding the end of
+                // K). The clearing is a mask on the byte, not a condition on its conversion: a
+                // condition splits the tile loop into blocks the scheduler cannot interleave.
+                const uint32_t smask = (w < nfull || 4 * w + q < CH) ? 0xFFu : 0u;
+                constexpr int NT = HT + (NR ? 1 : 0);
+                uint32_t cw[NT];
+                uint32_t sb[NT];
+                // Every LDS read of the window goes out before any arithmetic, the remainder
+                // tile's too (its slot exists when NR = 1; a wave that does not own it ignores
+                // the values).
 #pragma unroll
-            for (int j = 0; j < NT; j++) {
-                const int t = j < HT ? 2 * j + ts : 2 * HT;
-                cw[j] = *reinterpret_cast<const uint32_t *>(lds + coff + t * kSlabTileBytes);
-                sb[j] = lds[soff + (t >> 3) * 1024 + (t & 7) * 128] & smask;
-            }
-            u32x4_t av[RB];
-#pragma unroll
-            for (int b = 0; b < RB; b++)
-                av[b] = *reinterpret_cast<const u32x4_t *>(lds + xoff + 16 * b * kSlabRowBytes);
-            __builtin_amdgcn_sched_barrier(0);
-            // Tile by tile: the B fragment of tile j + 1 is decoded while the MFMAs of tile j
-            // run, a few decode instructions after each MFMA. The remainder tile's fragment is
-            // decoded with the last main tile, before the branch on who owns it.
-            bf16x8_t bcur = decode8_scaled(cw[0], e4m3_to_f32<0>(sb[0]));
-#pragma unroll
-            for (int j = 0; j < NT; j++) {
-                if (j == HT && !rem)
-                    break;
-                bf16x8_t bnext = bcur;
-                if (j + 1 < NT)
-                    bnext = decode8_scaled(cw[j + 1 < NT ? j + 1 : j],
-                                           e4m3_to_f32<0>(sb[j + 1 < NT ? j + 1 : j]));
-#pragma unroll
-                for (int b = 0; b < RB; b++) {
-                    f32x4_t &c = j < HT ? acc[j < HT ? j : 0][b] : racc[NR ? b : 0];
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[b]), bcur, c, 0, 0,
-                                                                0);
+                for (int j = 0; j < NT; j++) {
+                    const int t = j < HT ? 2 * j + ts : 2 * HT;
+                    cw[j] = *reinterpret_cast<const uint32_t *>(lds + coff + t * kSlabTileBytes);
+                    sb[j] = lds[soff + (t >> 3) * 1024 + (t & 7) * 128] & smask;
                 }
+                u32x4_t av[RB];
 #pragma unroll
-                for (int b = 0; b < RB; b++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    if (j + 1 < NT)
-                        __builtin_amdgcn_sched_group_barrier(0x002, 16 / RB + 1, 0);
-                }
+                for (int b = 0; b < RB; b++)
+                    av[b] =
+                        *reinterpret_cast<const u32x4_t *>(lds + xoff + 16 * b * kSlabRowBytes);
                 __builtin_amdgcn_sched_barrier(0);
-                if (NR && j + 1 == HT)
-                    asm volatile("" : "+v"(bnext));   // keeps the decode ahead of the branch
-                bcur = bnext;
+                // Tile by tile: the B fragment of tile j + 1 is decoded while the MFMAs of tile
+                // j run, a few decode instructions after each MFMA; main tile j also sends its
+                // share of the next loads, spread over its MFMAs. The remainder tile's fragment
+                // is decoded with the last main tile, before the branch on who owns it.
+                bf16x8_t bcur = decode8_scaled(cw[0], e4m3_to_f32<0>(sb[0]));
+#pragma unroll
+                for (int j = 0; j < NT; j++) {
+                    if (j == HT && !rem)
+                        break;
+                    bf16x8_t bnext = bcur;
+                    if (j + 1 < NT)
+                        bnext = decode8_scaled(cw[j + 1 < NT ? j + 1 : j],
+                                               e4m3_to_f32<0>(sb[j + 1 < NT ? j + 1 : j]));
+#pragma unroll
+                    for (int b = 0; b < RB; b++) {
+                        f32x4_t &c = j < HT ? acc[j < HT ? j : 0][b] : racc[NR ? b : 0];
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[b]), bcur, c, 0,
+                                                                    0, 0);
+                    }
+                    const int l0 = j < HT ? j * NL / HT : 0;          // this tile's loads
+                    const int l1 = j < HT ? (j + 1) * NL / HT : 0;
+#pragma unroll
+                    for (int l = l0; l < l1; l++) {
+                        if constexpr (XR)
+                            x_load(xi, l);
+                        else
+                            w_load(wi, l);
+                    }
+#pragma unroll
+                    for (int b = 0; b < RB; b++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                        if (j + 1 < NT)
+                            __builtin_amdgcn_sched_group_barrier(0x002, 16 / RB + 1, 0);
+                        // the tile's loads after MFMAs b = (l - l0) RB / (l1 - l0)
+                        for (int l = l0; l < l1; l++)
+                            if ((l - l0) * RB / (l1 - l0) == b)
+                                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (NR && j + 1 == HT)
+                        asm volatile("" : "+v"(bnext));   // keeps the decode ahead of the branch
+                    bcur = bnext;
+                }
             }
-        }
+        };
+        if (xwave)
+            windows(std::true_type{});
+        else
+            windows(std::false_type{});
 
         // ---- end of pass: the partial sums meet in LDS as a row-major tile of Y ----
         slab_wait_vm<0>();   // the loads in flight (next pass, or zeros past the end) landed
