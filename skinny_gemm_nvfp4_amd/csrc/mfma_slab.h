@@ -19,8 +19,10 @@
 //   * Workgroup of 8 wavefronts, two per SIMD (wavefront w runs on SIMD w % 4), so that one
 //     wavefront's MFMAs run while the other of its SIMD decodes, reads LDS or waits. Consumer w
 //     takes k-step ks = w % 4 of every 128-k window and the main tiles ts, ts + 2, ... (HT of
-//     them), ts = w / 4; with NR = 1 the last tile's four k-steps go one to each SIMD (k-step
-//     ks to the wavefront with ts = ks % 2). Every weight is decoded once, every A fragment read
+//     them), ts = w / 4; with NR = 1 the last tile's four k-steps go one to each SIMD, to its
+//     X-loading wavefront (ts = 0): the weight loaders, whose loads take longer to issue and who
+//     yield the SIMD to the older X loaders, are the last to finish a window (measured: o_proj
+//     and down at M = 128 about 6% faster than with the remainder on ts = ks % 2). Every weight is decoded once, every A fragment read
 //     from LDS by the two wavefronts of its k-step. Per window a wavefront decodes the B
 //     fragments of all its tiles, then runs the MFMAs row block by row block; the other
 //     wavefront of its SIMD issues MFMAs while it decodes or waits.
@@ -29,7 +31,10 @@
 //     (16 bytes per lane, no registers), with one barrier per window: X in a ring of 3 to 5
 //     windows loaded by wavefronts 0-3, the weights (from HBM, higher latency) in a ring of 4 to
 //     8 loaded by wavefronts 4-7, one loader of each kind per SIMD. Loads past the end of a row,
-//     of K or of the workgroup's groups read zeros.
+//     of K or of the workgroup's groups read zeros. A wavefront sends its loads one at a time
+//     between its MFMAs of the window before: sent together after the barrier they queue in the
+//     compute unit's load pipeline (several hundred cycles per window) and hold back the first
+//     MFMAs.
 //   * Step d of lane (r, q) covers k = 32 q + 8 d .. + 7 of the window: dword d of the lane's 16
 //     code bytes of column r, chunk q is its B fragment (decoded to bf16 with its block scale,
 //     exact), and row 16 b + r of X at those k its A fragment of row block b
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
     const int q = lane >> 4;
     const int ks = wave & 3;    // k-step of every window (= the SIMD)
     const int ts = wave >> 2;   // main tiles ts, ts + 2, ...
-    const bool rem = NR != 0 && ts == (ks & 1);   // takes k-step ks of the remainder tile
+    const bool rem = NR != 0 && ts == 0;   // takes k-step ks of the remainder tile
     const int K = a.K;
     const int N = a.N;
     const int CH = num_chunks(K);
