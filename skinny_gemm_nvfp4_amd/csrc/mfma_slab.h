@@ -348,7 +348,10 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                 // spans two chunks); their codes are zero, and the scale byte is cleared so that
                 // a NaN scale there cannot reach the sum (only in the window holding the end of
                 // K). The clearing is a mask on the byte, not a condition on its conversion: a
-                // condition splits the tile loop into blocks the scheduler cannot interleave.
+                // condition splits the tile loop into blocks the scheduler cannot interleave. The
+                // mask is applied where the byte is converted, not where it is read: applied at
+                // the read, each read waited for the one before (registers reused under the
+                // register budget), and the window's reads went out one at a time.
                 const uint32_t smask = (w < nfull || 4 * w + q < CH) ? 0xFFu : 0u;
                 constexpr int NT = HT + (NR ? 1 : 0);
                 uint32_t cw[NT];
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                 for (int j = 0; j < NT; j++) {
                     const int t = j < HT ? 2 * j + ts : 2 * HT;
                     cw[j] = *reinterpret_cast<const uint32_t *>(lds + coff + t * kSlabTileBytes);
-                    sb[j] = lds[soff + (t >> 3) * 1024 + (t & 7) * 128] & smask;
+                    sb[j] = lds[soff + (t >> 3) * 1024 + (t & 7) * 128];
                 }
                 u32x4_t av[RB];
 #pragma unroll
@@ -372,15 +375,16 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
                 // j run, a few decode instructions after each MFMA; main tile j also sends its
                 // share of the next loads, spread over its MFMAs. The remainder tile's fragment
                 // is decoded with the last main tile, before the branch on who owns it.
-                bf16x8_t bcur = decode8_scaled(cw[0], e4m3_to_f32<0>(sb[0]));
+                bf16x8_t bcur = decode8_scaled(cw[0], e4m3_to_f32<0>(sb[0] & smask));
 #pragma unroll
                 for (int j = 0; j < NT; j++) {
                     if (j == HT && !rem)
                         break;
                     bf16x8_t bnext = bcur;
                     if (j + 1 < NT)
-                        bnext = decode8_scaled(cw[j + 1 < NT ? j + 1 : j],
-                                               e4m3_to_f32<0>(sb[j + 1 < NT ? j + 1 : j]));
+                        bnext = decode8_scaled(
+                            cw[j + 1 < NT ? j + 1 : j],
+                            e4m3_to_f32<0>(sb[j + 1 < NT ? j + 1 : j] & smask));
 #pragma unroll
                     for (int b = 0; b < RB; b++) {
                         f32x4_t &c = j < HT ? acc[j < HT ? j : 0][b] : racc[NR ? b : 0];
