@@ -22,10 +22,12 @@
 //     them), ts = w / 4; with NR = 1 the last tile's four k-steps go one to each SIMD, to its
 //     X-loading wavefront (ts = 0): the weight loaders, whose loads take longer to issue and who
 //     yield the SIMD to the older X loaders, are the last to finish a window (measured: o_proj
-//     and down at M = 128 about 6% faster than with the remainder on ts = ks % 2). Every weight is decoded once, every A fragment read
-//     from LDS by the two wavefronts of its k-step. Per window a wavefront decodes the B
-//     fragments of all its tiles, then runs the MFMAs row block by row block; the other
-//     wavefront of its SIMD issues MFMAs while it decodes or waits.
+//     and down at M = 128 about 6% faster than with the remainder on ts = ks % 2). Every weight
+//     is decoded once, every A fragment read from LDS by the two wavefronts of its k-step. Per
+//     window a wavefront reads all its LDS operands first (codes, scale bytes, A fragments),
+//     then goes tile by tile: the MFMAs of tile j for every row block, with the decode of tile
+//     j + 1 placed between them; the other wavefront of its SIMD issues MFMAs while it decodes
+//     or waits.
 //   * Per 128-k window the whole workgroup stages X (16 RB rows x 256 bytes), the codes (1 KB
 //     per tile) and the scales (128 bytes per tile) in LDS through direct-to-LDS buffer loads
 //     (16 bytes per lane, no registers), with one barrier per window: X in a ring of 3 to 5
