@@ -398,6 +398,11 @@ int tiles_per_workgroup(int N)
 
 }  // namespace
 
+hipError_t allow_dynamic_lds(const void *fn, int bytes)
+{
+    return allow_lds(fn, bytes);
+}
+
 bool choose_config(int M, int N, int K, int *path, int *split)
 {
     // Automatic choice (measured on the layer shapes): the dot-product kernel for the smallest M;

@@ -25,6 +25,9 @@
 //   * At the end of an item the 16 lanes of each column are summed in a fixed order, times the
 //     expert's g, and stored. No item is split between wavefronts, so there are no partial sums
 //     to exchange, and a row's result does not depend on MR, the grid or the other rows.
+//   * A chunk with fewer rows than MR (an expert with few rows) skips the dot products of the
+//     missing rows, so a larger MR costs only the decode it shares: each expert's weights are
+//     then read once for up to MR rows instead of once per row.
 //   * Offsets are clamped to [0, T] and made non-decreasing (a running maximum), so the experts'
 //     rows never overlap and add up to at most T: bad offsets move rows between experts, never
 //     an access outside X, Y or the weights.
@@ -280,6 +283,10 @@ __global__ __launch_bounds__(kWave *W) void grouped_gemv_kernel(GroupedArgs a, i
                 decode32_bf16(c.code, w);
 #pragma unroll
                 for (int m = 0; m < MR; m++) {
+                    // Rows past the chunk's last (an expert with fewer rows than MR) cost
+                    // nothing: the weights are decoded once for the rows there are.
+                    if (m > 0 && m >= cit.rows)
+                        break;
                     u32x4_t xv[4];
                     if constexpr (LDSX) {
                         // row m of the item's chunk, window wc, the lane's 32-k chunk j

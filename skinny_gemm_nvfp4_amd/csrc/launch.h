@@ -94,6 +94,10 @@ constexpr int kMaxK = 1 << 22;
 // A dot-product request whose X does not fit in LDS becomes the matrix-core path.
 bool choose_config(int M, int N, int K, int *path, int *split);
 
+// Lets kernel `fn` take `bytes` of dynamic LDS (above the 64 KB default it must opt in, once per
+// kernel and device).
+hipError_t allow_dynamic_lds(const void *fn, int bytes);
+
 // Launch the GEMM with a resolved path and split. Returns the hipError_t of the launch.
 hipError_t launch_gemm(int path, int split, const GemmArgs &a, hipStream_t stream);
 
