@@ -12,8 +12,9 @@
 //   * A unit is one (group, 512-k window) pair: 16 chunks of 32 k x 4 columns, 1 KB of codes in
 //     one contiguous piece of the packed layout. Lane l of a wavefront reads its 16 bytes at
 //     16 l: column l % 4 of the group, chunk l / 4 of the window. The units of a workgroup,
-//     ordered group-major, are dealt to the W wavefronts in W contiguous runs of equal length
-//     (to within one unit).
+//     ordered group-major, are dealt to the W wavefronts in W contiguous runs, shorter for the
+//     second and later wavefronts of a SIMD, which the hardware serves later
+//     (stream_run_start).
 //   * X (all M rows, all of K) is staged once in LDS, so the weight loads are the only global
 //     traffic of the loop. Each 32-k chunk of X sits in an 80-byte slot; the 16 chunks a
 //     wavefront reads at once then fall into different bank groups, and each is broadcast to the
@@ -54,10 +55,32 @@ struct StreamLayout {
     int gunit;       // groups dealt together: 2 keeps the gate/up pairs of a workgroup whole
 };
 
-// First wavefront of the W whose run [u0(w), u0(w+1)), u0(w) = floor(w units / W), holds unit u.
-__host__ __device__ inline int stream_owner(long long u, int W, long long units)
+// Share of the units per wavefront. Wavefront w runs on SIMD w % 4, as the (w / 4)-th
+// wavefront there; a SIMD's later wavefronts end their runs later (measured on gate_up at one
+// row, 12 wavefronts of equal runs: the second and third of a SIMD 0.6-1.0 and 1.0-1.5 us after
+// the first), so they get shorter runs: weight 32 - 2 (w / 4). C(w) is the weight of wavefronts
+// 0 .. w - 1; with one wavefront per SIMD (W <= 4) the split is the plain even one.
+__host__ __device__ inline uint32_t stream_weight_before(int w)
 {
-    return (int)(((u + 1) * W - 1) / units);
+    const uint32_t f = (uint32_t)w >> 2, r = (uint32_t)w & 3u;
+    return 4u * (32u * f - f * (f - 1u)) + r * (32u - 2u * f);
+}
+
+// First unit of wavefront w's run, of `units` < 2^21 units dealt to W <= 16 wavefronts.
+__host__ __device__ inline int stream_run_start(int w, int W, uint32_t units)
+{
+    if (W <= 4)
+        return (int)(((uint32_t)w * units) / (uint32_t)W);
+    return (int)((stream_weight_before(w) * units) / stream_weight_before(W));
+}
+
+// The wavefront of the W whose run holds unit u.
+inline int stream_owner(long long u, int W, long long units)
+{
+    int w = 0;
+    while (w + 1 < W && stream_run_start(w + 1, W, (uint32_t)units) <= u)
+        w++;
+    return w;
 }
 
 // floor(x / d) for x < 2^22, given rd = 1.0f / d rounded to nearest. The float estimate is within
@@ -92,7 +115,7 @@ __global__ __launch_bounds__(kWave *W) void gemv_stream_kernel(GemmArgs a, Strea
     const int ncols = min(N - c0, kGroupCols * ngroups);
     const int nwin = L.nwin;
     const uint32_t units = (uint32_t)ngroups * (uint32_t)nwin;   // < 2^21
-    auto run_start = [&](int w) { return (int)(((uint32_t)w * units) / (uint32_t)W); };
+    auto run_start = [&](int w) { return stream_run_start(w, W, units); };
     const int u0 = run_start(wave);
     const int u1 = run_start(wave + 1);
     const int gstart = (int)div_small((uint32_t)u0, (uint32_t)nwin, L.rnwin);
