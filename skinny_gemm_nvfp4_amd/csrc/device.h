@@ -113,6 +113,34 @@ __device__ __forceinline__ uint32_t off_if(bool valid, uint32_t off)
     return valid ? off : kOutOfRange;
 }
 
+// Wait until at most N vector memory operations of this wavefront are outstanding (they complete
+// in issue order; direct-to-LDS loads count among them).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// A buffer descriptor the compiler keeps in scalar registers: the direct-to-LDS loads need one,
+// and a descriptor it cannot prove uniform costs a readfirstlane loop around every load.
+__device__ __forceinline__ rsrc_t uniform_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return make_rsrc(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo), n);
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at dst + 16 l (dst the same in
+// every lane), without passing through registers.
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint8_t *dst, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+}
+
 // One chunk of one output column: 32 consecutive k, i.e. 16 code bytes and the aligned 4-byte
 // word that holds the chunk's 2 scale bytes (and those of the neighbouring column of the group).
 struct Chunk {

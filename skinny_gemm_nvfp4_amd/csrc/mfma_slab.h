@@ -114,36 +114,11 @@ struct SlabLayout {
     int vec;        // 1: Y (or H) rows may be written 16 (8) bytes at a time
 };
 
-// Wait until at most N vector memory operations of this wavefront are outstanding.
-template <int N>
-__device__ __forceinline__ void slab_wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 __device__ __forceinline__ void slab_barrier()
 {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// A buffer descriptor the compiler keeps in scalar registers: the LDS-DMA loads need one, and a
-// descriptor it cannot prove uniform costs a readfirstlane loop around every load.
-__device__ __forceinline__ rsrc_t slab_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-    return make_rsrc(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo), n);
-}
-
-__device__ __forceinline__ void slab_lds_load16(rsrc_t r, uint8_t *dst, uint32_t off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
 }
 
 template <int RB, int HT, int NR, int MODE>
@@ -190,9 +165,9 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
 
     const uint32_t gq = (uint32_t)CH * kChunkCodeBytes;
     const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;
-    const rsrc_t rq = slab_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
-    const rsrc_t rs = slab_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
-    const rsrc_t rx = slab_rsrc(a.X + (size_t)m0 * (size_t)K, (uint32_t)max(mrows, 0) *
+    const rsrc_t rq = uniform_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
+    const rsrc_t rs = uniform_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
+    const rsrc_t rx = uniform_rsrc(a.X + (size_t)m0 * (size_t)K, (uint32_t)max(mrows, 0) *
                                                                    (uint32_t)K * 2u);
     const float g = *a.gscale;
 
@@ -237,7 +212,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
         return XIssue{lds + S::XOFF + slot * S::XBYTES, lo};
     };
     auto x_load = [&](const XIssue &x, int i) {
-        slab_lds_load16(rx, x.base + (xw + 4 * i) * 1024, x.lo + (uint32_t)i * xstep);
+        lds_load16(rx, x.base + (xw + 4 * i) * 1024, x.lo + (uint32_t)i * xstep);
     };
     struct WIssue {
         uint8_t *base;
@@ -269,7 +244,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
         const uint32_t off = code    ? x.cl + (uint32_t)(4 * v) * gq
                              : scale ? x.sl + (uint32_t)(32 * (v - TW)) * gs
                                      : kOutOfRange;
-        slab_lds_load16(code ? rq : rs, dst, off);
+        lds_load16(code ? rq : rs, dst, off);
     };
     // The first windows of a pass: D - 1 windows ahead of their use, in each ring.
     auto prologue = [&](int pass) {
@@ -328,7 +303,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
             constexpr int D = XR ? S::DX : S::DW;    // ring depth of this role's loads
             constexpr int NL = XR ? S::XL : S::WL;   // its loads per window
             for (int w = 0; w < nwin; w++) {
-                slab_wait_vm<(D - 2) * NL>();   // this wave's loads of window w landed
+                wait_vm<(D - 2) * NL>();   // this wave's loads of window w landed
                 slab_barrier();                 // ... everyone's; the slots of window w - 1 are free
                 // The loads of window w + D - 1 (into the slot of window w - 1).
                 const int lw = w + D - 1;
@@ -425,7 +400,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
             windows(std::false_type{});
 
         // ---- end of pass: the partial sums meet in LDS as a row-major tile of Y ----
-        slab_wait_vm<0>();   // the loads in flight (next pass, or zeros past the end) landed
+        wait_vm<0>();   // the loads in flight (next pass, or zeros past the end) landed
         slab_barrier();      // every wavefront is done with the ring buffers
         // The lane's part of the LDS addresses is made opaque here, so that the compiler computes
         // the exchange addresses in the epilogue instead of hoisting them out of the pass loop

@@ -17,10 +17,14 @@
 //     4 pieces of 256 contiguous bytes of the packed layout, i.e. whole cache lines. MFMA k-slot
 //     8 q + e of step d (d = 0..3) is k = 128 w + 32 q + 8 d + e, so dword d of the lane's codes
 //     is its B fragment of step d, with the scale of block 2 (4 w + q) + d / 2.
-//   * X: the wavefront reads the 16 rows x 128 k of its window with contiguous 16-byte loads
-//     (four 1 KB pieces), stores them in its own LDS buffer (rows padded to 272 bytes) and reads
-//     its A fragments there: lane (r, q) takes row r at k = 32 q + 8 d. The loads of the next
-//     window (X first, then weights) are in flight while the current one is multiplied.
+//   * X: the 16 rows x 128 k of a window go straight from memory into the wavefront's LDS
+//     buffer of the window's ring slot (four direct-to-LDS loads of 1 KB; piece kp of row m at
+//     slot kp ^ m, so that the 16 rows of an A fragment fall on different bank groups), and the
+//     A fragments are read there: lane (r, q) takes row r at k = 32 q + 8 d. The loads of the
+//     next window (X first, then weights into registers) are in flight while the current one is
+//     multiplied; X needs no registers (measured against staging it through registers: q/k/v
+//     and o_proj at M = 32 14.2 -> 13.0 and 13.6 -> 12.4 us, o_proj at M = 8 8.6 -> 7.7, down at
+//     M = 16 19.0 -> 18.6, the wide shapes even).
 //   * B = e2m1 * s decoded to bf16 (exact); the sum over k does not depend on the slot order, so
 //     this is the plain product.
 //   * The W partial tiles are summed through LDS in wavefront order and scaled by g once.
@@ -35,38 +39,42 @@
 namespace nvfp4 {
 
 constexpr int kMfmaWindow = 128;
-constexpr int kXRowBytes = 272;                   // 256 bytes of a 128-k row + 16 of padding
+constexpr int kXRowBytes = 256;                   // one 128-k row of bf16 X
 constexpr int kXBufBytes = 16 * kXRowBytes;       // one window of 16 rows
 
-// LDS bytes of mfma_stream_kernel<TC, W>: two X buffers per wavefront, reused at the end for one
-// 16 x 16 fp32 partial per wavefront and tile.
-constexpr int mfma_stream_lds_bytes(int tc, int w)
+// LDS bytes of mfma_stream_kernel<TC, W, FAST, D>: D X buffers per wavefront (one per ring slot:
+// the direct-to-LDS loads of later windows land there while a window is multiplied), then one
+// 16 x 16 fp32 partial per wavefront and tile for the reduction.
+constexpr int mfma_stream_lds_bytes(int tc, int w, int d = 2)
 {
-    return (2 * kXBufBytes * w > w * tc * 4 * kWave * 4) ? 2 * kXBufBytes * w
-                                                         : w * tc * 4 * kWave * 4;
+    return d * kXBufBytes * w + w * tc * 4 * kWave * 4;
 }
 
 template <int TC>
 struct MfmaWindow {
-    u32x4_t x[4];      // X pieces in load order: row 4 p + l / 16, k = 8 (l % 16)
     u32x4_t c[TC];     // the lane's 16 code bytes of each tile
     uint32_t s[TC];    // the word holding the lane's 2 scale bytes of each tile
 
-    // lq/ls: the lane's code/scale offset within a tile-window at window 0; tq/ts: bytes per
-    // tile; wq/ws: bytes per window; xo: the lane's X offset at window 0.
+    // The window's loads: X straight into the LDS buffer xdst (four 1 KB loads, load p holding
+    // rows 4 p .. 4 p + 3: lane l fetches the 16-byte piece (l % 16) ^ row of row 4 p + l / 16,
+    // which lands at slot l % 16 of the row), then the codes and the scale word of each tile into
+    // registers. xo[p] / xk[p]: the lane's X byte offset / k of load p at window 0; lq/ls: its
+    // code/scale offset within a tile-window at window 0; tq/ts: bytes per tile.
     template <bool FAST>
-    __device__ __forceinline__ void load(rsrc_t rq, rsrc_t rs, rsrc_t rx, uint32_t lq,
-                                         uint32_t ls, uint32_t tq, uint32_t ts, uint32_t xo,
-                                         int xk, int w, bool live, int tc0, int nt,
-                                         int ngroups, int gr, int q, int CH, int K)
+    __device__ __forceinline__ void load(rsrc_t rq, rsrc_t rs, rsrc_t rx, uint8_t *xdst,
+                                         uint32_t lq, uint32_t ls, uint32_t tq, uint32_t ts,
+                                         const uint32_t (&xo)[4], const int (&xk)[4], int w,
+                                         bool live, int tc0, int nt, int ngroups, int gr, int q,
+                                         int CH, int K)
     {
 #pragma unroll
         for (int p = 0; p < 4; p++)
-            x[p] = __builtin_amdgcn_raw_buffer_load_b128(
-                rx,
-                off_if(live && kMfmaWindow * w + xk < K,
-                       xo + (uint32_t)p * 4u * (uint32_t)K * 2u + (uint32_t)w * (kMfmaWindow * 2)),
-                0, kAuxNormal);
+            lds_load16(rx, xdst + p * 1024,
+                       off_if(live && (FAST || kMfmaWindow * w + xk[p] < K),
+                              xo[p] + (uint32_t)w * (kMfmaWindow * 2)));
+        // The X loads go out first: the wait before a window's A fragments counts the 2 TC loads
+        // behind them (loads complete in issue order).
+        __builtin_amdgcn_sched_barrier(0);
         const bool kv = live && (FAST || 4 * w + q < CH);
 #pragma unroll
         for (int t = 0; t < TC; t++) {
@@ -80,22 +88,9 @@ struct MfmaWindow {
         }
     }
 
-    // X pieces into the wavefront's LDS buffer.
-    __device__ __forceinline__ void stage(uint8_t *buf, int lane) const
+    __device__ __forceinline__ void mul(f32x4_t (&acc)[TC], const u32x4_t (&a)[4], int nt,
+                                        uint32_t sshift) const
     {
-#pragma unroll
-        for (int p = 0; p < 4; p++)
-            *reinterpret_cast<u32x4_t *>(buf + (4 * p + (lane >> 4)) * kXRowBytes +
-                                         16 * (lane & 15)) = x[p];
-    }
-
-    __device__ __forceinline__ void mul(f32x4_t (&acc)[TC], const uint8_t *buf, int r, int q,
-                                        int nt, uint32_t sshift) const
-    {
-        u32x4_t a[4];
-#pragma unroll
-        for (int d = 0; d < 4; d++)
-            a[d] = *reinterpret_cast<const u32x4_t *>(buf + r * kXRowBytes + 64 * q + 16 * d);
 #pragma unroll
         for (int t = 0; t < TC; t++) {
             if (t < nt) {
@@ -111,6 +106,15 @@ struct MfmaWindow {
         }
     }
 };
+
+// The A fragments of a window from its X buffer: lane (r, q), step d: row r, piece 4 q + d (at
+// slot (4 q + d) ^ r, so that the 16 rows of a fragment fall on different bank groups).
+__device__ __forceinline__ void mfma_read_a(u32x4_t (&a)[4], const uint8_t *buf, int r, int q)
+{
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+        a[d] = *reinterpret_cast<const u32x4_t *>(buf + r * kXRowBytes + 16 * ((4 * q + d) ^ r));
+}
 
 template <int TC, int W, bool FAST, int D = 2>
 __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
@@ -144,7 +148,8 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;
     const rsrc_t rq = make_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
     const rsrc_t rs = make_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
-    const rsrc_t rx = make_rsrc(a.X + (size_t)m0 * (size_t)K, (uint32_t)mrows * (uint32_t)K * 2u);
+    const rsrc_t rx = uniform_rsrc(a.X + (size_t)m0 * (size_t)K,
+                                   (uint32_t)mrows * (uint32_t)K * 2u);
     const int gr = r >> 2;   // group of the lane's column within the tile
     const uint32_t lq = (uint32_t)gr * gq + (uint32_t)q * kChunkCodeBytes + (uint32_t)(r & 3) * 16u;
     const uint32_t ls = (uint32_t)gr * gs + (uint32_t)q * kChunkScaleBytes +
@@ -152,9 +157,16 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const uint32_t sshift = 16u * (uint32_t)(r & 1);
     const uint32_t tq = 4u * gq;
     const uint32_t ts = 4u * gs;
-    const int xk = 8 * r;    // k of the lane's X piece within the window
-    const uint32_t xo = ((uint32_t)(lane >> 4) * (uint32_t)K + (uint32_t)xk) * 2u;
-    uint8_t *xbuf[2] = {lds + wave * 2 * kXBufBytes, lds + wave * 2 * kXBufBytes + kXBufBytes};
+    // The lane's X pieces of a window: load p, row 4 p + lane / 16, piece (lane % 16) ^ row.
+    uint32_t xo[4];
+    int xk[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const int row = 4 * p + (lane >> 4);
+        xk[p] = 8 * ((lane & 15) ^ row);
+        xo[p] = ((uint32_t)row * (uint32_t)K + (uint32_t)xk[p]) * 2u;
+    }
+    uint8_t *xb = lds + wave * D * kXBufBytes;   // this wavefront's X buffer of ring slot u: + u 4 KB
     const float g = *a.gscale;
     // This wavefront's windows: wave, wave + W, ...; window i of the wavefront is wave + i W.
     const int nmine = (nwin - wave + W - 1) / W;
@@ -170,17 +182,17 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const int nch = (T + TC - 1) / TC;
     const int cs = T > 0 ? (T + nch - 1) / nch : TC;
     // Ring of D windows: D - 1 in flight while one is multiplied. Window i of a chunk sits in ring
-    // slot i % D and, once its X is staged, in X buffer i & 1.
+    // slot i % D: its codes and scales in that slot's registers, its X in that slot's buffer.
     MfmaWindow<TC> ring[D];
-    auto load = [&](int i, MfmaWindow<TC> &win, int tc, int n) {
+    auto load = [&](int i, int slot, int tc, int n) {
         const int w = wave + i * W;
-        win.template load<FAST>(rq, rs, rx, lq, ls, tq, ts, xo, xk, w, i < nmine, tc, n, ngroups,
-                                gr, q, CH, K);
+        ring[slot].template load<FAST>(rq, rs, rx, xb + slot * kXBufBytes, lq, ls, tq, ts, xo, xk,
+                                       w, i < nmine, tc, n, ngroups, gr, q, CH, K);
     };
     if (T > 0) {
 #pragma unroll
         for (int i = 0; i < D - 1; i++)
-            load(i, ring[i], 0, min(cs, T));
+            load(i, i, 0, min(cs, T));
     }
     for (int tc0 = 0; tc0 < T; tc0 += cs) {
         const int nt = min(cs, T - tc0);
@@ -189,18 +201,21 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
         for (int t = 0; t < TC; t++)
             acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-        ring[0].stage(xbuf[0], lane);
         for (int i0 = 0; i0 < nmine; i0 += D) {
 #pragma unroll
             for (int u = 0; u < D; u++) {
                 const int i = i0 + u;
                 if (i < nmine) {
-                    load(i + D - 1, ring[(u + D - 1) % D], tc0, nt);
+                    // Window i's X has landed: after it went out only its codes and scales and
+                    // the D - 2 windows behind it. Its A fragments are read before the next
+                    // window's loads go out, which write the buffer of window i - 1.
+                    wait_vm<(4 + 2 * TC) * (D - 1) - 4>();
+                    u32x4_t av[4];
+                    mfma_read_a(av, xb + u * kXBufBytes, r, q);
+                    load(i + D - 1, (u + D - 1) % D, tc0, nt);
                     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-                    ring[u].mul(acc, xbuf[i & 1], r, q, nt, sshift);
+                    ring[u].mul(acc, av, nt, sshift);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (i + 1 < nmine)
-                        ring[(u + 1) % D].stage(xbuf[(i + 1) & 1], lane);
                 }
             }
         }
@@ -213,12 +228,13 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
         if (tc0 + cs < T) {
 #pragma unroll
             for (int i = 0; i < D - 1; i++)
-                load(i, ring[i], tc0 + cs, min(cs, T - tc0 - cs));
+                load(i, i, tc0 + cs, min(cs, T - tc0 - cs));
+        } else {
+            wait_vm<0>();   // the loads past the last window (zeros into the X buffers) landed
         }
 
         // acc[t][e] is the partial Y[m0 + 4 q + e][c0 + 16 (tc0 + t) + r] of this wavefront.
-        __syncthreads();  // every wavefront is done with its X buffers, which red reuses
-        float *red = reinterpret_cast<float *>(lds);   // [W][TC][4][64]
+        float *red = reinterpret_cast<float *>(lds + W * D * kXBufBytes);   // [W][TC][4][64]
 #pragma unroll
         for (int t = 0; t < TC; t++)
 #pragma unroll
@@ -259,7 +275,7 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
                     best = key_max(best, argmax_key(sum * g, c0 + colx));
             }
         }
-        __syncthreads();  // red and the X buffers are reused by the next chunk
+        __syncthreads();  // red is reused by the next chunk
     }
     if (a.keys != nullptr) {
         // One key per row and group of 4 wavefronts: slot blockIdx.x (W / 4) + wave / 4.
