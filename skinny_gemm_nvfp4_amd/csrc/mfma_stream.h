@@ -24,7 +24,9 @@
 //     next window (X first, then weights into registers) are in flight while the current one is
 //     multiplied; X needs no registers (measured against staging it through registers: q/k/v
 //     and o_proj at M = 32 14.2 -> 13.0 and 13.6 -> 12.4 us, o_proj at M = 8 8.6 -> 7.7, down at
-//     M = 16 19.0 -> 18.6, the wide shapes even).
+//     M = 16 19.0 -> 18.6, the wide shapes even). With 4 wavefronts the scale bytes of a window
+//     go into the slot the same way (one 1 KB load per 8 tiles instead of a 4-byte load per
+//     tile: gate_up at M = 16 26.2 -> 25.2 us, lm_head at M = 8 106 -> 97).
 //   * B = e2m1 * s decoded to bf16 (exact); the sum over k does not depend on the slot order, so
 //     this is the plain product.
 //   * The W partial tiles are summed through LDS in wavefront order and scaled by g once.
@@ -42,38 +44,71 @@ constexpr int kMfmaWindow = 128;
 constexpr int kXRowBytes = 256;                   // one 128-k row of bf16 X
 constexpr int kXBufBytes = 16 * kXRowBytes;       // one window of 16 rows
 
-// LDS bytes of mfma_stream_kernel<TC, W, FAST, D>: D X buffers per wavefront (one per ring slot:
-// the direct-to-LDS loads of later windows land there while a window is multiplied), then one
+// Whether a window's scale bytes go straight into LDS (one 1 KB load per 8 tiles) rather than
+// into registers (one 4-byte load per tile): with 4 wavefronts, whose chunks are wide
+// (measured: gate_up at M = 16 26.0 -> 24.9 us, lm_head 106 -> 102; with 8 wavefronts and 2
+// tiles o_proj was 0.1-0.3 us slower, and 9 tiles would not fit in LDS).
+constexpr bool mfma_scales_in_lds(int w) { return w == 4; }
+
+// Direct-to-LDS scale loads per window.
+constexpr int mfma_scale_loads(int tc, int w) { return mfma_scales_in_lds(w) ? (tc + 7) / 8 : 0; }
+
+// Bytes of one ring slot of a wavefront: the window's X, then its tiles' scale bytes.
+constexpr int mfma_slot_bytes(int tc, int w) { return kXBufBytes + 1024 * mfma_scale_loads(tc, w); }
+
+// Windows in a wavefront's ring: one multiplied while the next is in flight (deeper rings
+// measured slower: gate_up at M = 16 24.9 -> 26.9 us with 3, 28.2 with 4).
+constexpr int kMfmaDepth = 2;
+
+// LDS bytes of mfma_stream_kernel<TC, W, FAST>: the ring slots of every wavefront (the
+// direct-to-LDS loads of the next window land there while a window is multiplied), then one
 // 16 x 16 fp32 partial per wavefront and tile for the reduction.
-constexpr int mfma_stream_lds_bytes(int tc, int w, int d = 2)
+constexpr int mfma_stream_lds_bytes(int tc, int w)
 {
-    return d * kXBufBytes * w + w * tc * 4 * kWave * 4;
+    return kMfmaDepth * mfma_slot_bytes(tc, w) * w + w * tc * 4 * kWave * 4;
 }
 
-template <int TC>
+template <int TC, bool SL>
 struct MfmaWindow {
-    u32x4_t c[TC];     // the lane's 16 code bytes of each tile
-    uint32_t s[TC];    // the word holding the lane's 2 scale bytes of each tile
+    static constexpr int NS = SL ? (TC + 7) / 8 : 0;
+    u32x4_t c[TC];            // the lane's 16 code bytes of each tile
+    uint32_t s[SL ? 1 : TC];  // without SL: the word holding the lane's 2 scale bytes of each tile
 
-    // The window's loads: X straight into the LDS buffer xdst (four 1 KB loads, load p holding
-    // rows 4 p .. 4 p + 3: lane l fetches the 16-byte piece (l % 16) ^ row of row 4 p + l / 16,
-    // which lands at slot l % 16 of the row), then the codes and the scale word of each tile into
-    // registers. xo[p] / xk[p]: the lane's X byte offset / k of load p at window 0; lq/ls: its
-    // code/scale offset within a tile-window at window 0; tq/ts: bytes per tile.
+    // The window's loads, into ring slot `slot` (LDS) and these registers:
+    //   * with SL, the scale bytes of its tiles straight into the slot (load j, lane l: tile
+    //     8 j + l / 8, group (l / 2) % 4, chunks 2 (l % 2) and 2 (l % 2) + 1 of the window: 16
+    //     bytes landing at 128 (l / 8) + 32 group + 16 (l % 2), i.e. tile-major, then group,
+    //     chunk, column, block);
+    //   * X straight into the slot (four 1 KB loads, load p holding rows 4 p .. 4 p + 3: lane l
+    //     fetches the 16-byte piece (l % 16) ^ row of row 4 p + l / 16, which lands at slot
+    //     l % 16 of the row);
+    //   * the codes of each tile (and without SL its scale word) into registers.
+    // xo[p] / xk[p]: the lane's X byte offset / k of load p at window 0; sv0 / sg / sh: its part
+    // of the scale loads at window 0 (SL) or ls: its scale word's offset (without); lq: its code
+    // offset within a tile-window at window 0; tq/ts: code/scale bytes per tile.
     template <bool FAST>
-    __device__ __forceinline__ void load(rsrc_t rq, rsrc_t rs, rsrc_t rx, uint8_t *xdst,
-                                         uint32_t lq, uint32_t ls, uint32_t tq, uint32_t ts,
-                                         const uint32_t (&xo)[4], const int (&xk)[4], int w,
-                                         bool live, int tc0, int nt, int ngroups, int gr, int q,
-                                         int CH, int K)
+    __device__ __forceinline__ void load(rsrc_t rq, rsrc_t rs, rsrc_t rx, uint8_t *slot,
+                                         uint32_t lq, uint32_t sv0, int sg, int sh, uint32_t ls,
+                                         uint32_t tq, uint32_t ts, const uint32_t (&xo)[4],
+                                         const int (&xk)[4], int lane, int w, bool live, int tc0,
+                                         int nt, int ngroups, int gr, int q, int CH, int K)
     {
 #pragma unroll
+        for (int j = 0; j < NS; j++) {
+            const int t = 8 * j + (lane >> 3);
+            const bool v = live && t < nt && 4 * (tc0 + t) + sg < ngroups &&
+                           (FAST || 4 * w + 2 * sh < CH);
+            lds_load16(rs, slot + kXBufBytes + j * 1024,
+                       off_if(v, sv0 + (uint32_t)(tc0 + t) * ts +
+                                     (uint32_t)w * (4u * kChunkScaleBytes)));
+        }
+#pragma unroll
         for (int p = 0; p < 4; p++)
-            lds_load16(rx, xdst + p * 1024,
+            lds_load16(rx, slot + p * 1024,
                        off_if(live && (FAST || kMfmaWindow * w + xk[p] < K),
                               xo[p] + (uint32_t)w * (kMfmaWindow * 2)));
-        // The X loads go out first: the wait before a window's A fragments counts the 2 TC loads
-        // behind them (loads complete in issue order).
+        // The LDS loads go out first: the wait before a window's LDS operands counts the loads
+        // into registers behind them (loads complete in issue order).
         __builtin_amdgcn_sched_barrier(0);
         const bool kv = live && (FAST || 4 * w + q < CH);
 #pragma unroll
@@ -82,19 +117,25 @@ struct MfmaWindow {
             c[t] = __builtin_amdgcn_raw_buffer_load_b128(
                 rq, off_if(v, lq + (uint32_t)(tc0 + t) * tq + (uint32_t)w * (4u * kChunkCodeBytes)),
                 0, kAuxNormal);
-            s[t] = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, off_if(v, ls + (uint32_t)(tc0 + t) * ts + (uint32_t)w * (4u * kChunkScaleBytes)),
-                0, kAuxNormal);
+            if constexpr (!SL)
+                s[t] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rs, off_if(v, ls + (uint32_t)(tc0 + t) * ts +
+                                      (uint32_t)w * (4u * kChunkScaleBytes)),
+                    0, kAuxNormal);
         }
     }
 
-    __device__ __forceinline__ void mul(f32x4_t (&acc)[TC], const u32x4_t (&a)[4], int nt,
-                                        uint32_t sshift) const
+    // sb: the lane's scale bytes of each tile (block of k 32 q .. + 15 in bits 0-7, of + 16 ..
+    // + 31 in bits 8-15); with SL masked to zero for a chunk past K (the 16-byte scale load of
+    // the window holding the end of K may bring the next group's bytes there; the codes are
+    // zero).
+    __device__ __forceinline__ void mul(f32x4_t (&acc)[TC], const u32x4_t (&a)[4],
+                                        const uint32_t (&sb)[TC], int nt) const
     {
 #pragma unroll
         for (int t = 0; t < TC; t++) {
             if (t < nt) {
-                const uint32_t sw = s[t] >> sshift;
+                const uint32_t sw = sb[t];
                 const float s_lo = e4m3_to_f32<0>(sw);   // k 32 q .. + 15 of the window
                 const float s_hi = e4m3_to_f32<1>(sw);   // k 32 q + 16 .. + 31
 #pragma unroll
@@ -116,7 +157,7 @@ __device__ __forceinline__ void mfma_read_a(u32x4_t (&a)[4], const uint8_t *buf,
         a[d] = *reinterpret_cast<const u32x4_t *>(buf + r * kXRowBytes + 16 * ((4 * q + d) ^ r));
 }
 
-template <int TC, int W, bool FAST, int D = 2>
+template <int TC, int W, bool FAST, int D = kMfmaDepth>
 __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -147,14 +188,21 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const uint32_t gq = (uint32_t)CH * kChunkCodeBytes;
     const uint32_t gs = (uint32_t)CH * kChunkScaleBytes;
     const rsrc_t rq = make_rsrc(a.Wq + (size_t)g0 * gq, (uint32_t)ngroups * gq);
-    const rsrc_t rs = make_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
+    const rsrc_t rs = uniform_rsrc(a.Ws + (size_t)g0 * gs, (uint32_t)ngroups * gs);
     const rsrc_t rx = uniform_rsrc(a.X + (size_t)m0 * (size_t)K,
                                    (uint32_t)mrows * (uint32_t)K * 2u);
     const int gr = r >> 2;   // group of the lane's column within the tile
     const uint32_t lq = (uint32_t)gr * gq + (uint32_t)q * kChunkCodeBytes + (uint32_t)(r & 3) * 16u;
-    const uint32_t ls = (uint32_t)gr * gs + (uint32_t)q * kChunkScaleBytes +
-                        (uint32_t)(r & 2) * 2u;   // word of columns (r & 2), (r & 2) + 1
+    // The lane's part of a window's scale loads: group sg, chunks 2 sh and 2 sh + 1.
+    const int sg = (lane >> 1) & 3;
+    const int sh = lane & 1;
+    const uint32_t sv0 = (uint32_t)sg * gs + (uint32_t)sh * 16u;
+    // Without SL: the lane's scale word (columns (r & 2), (r & 2) + 1 of chunk q), and its half.
+    const uint32_t ls = (uint32_t)gr * gs + (uint32_t)q * kChunkScaleBytes + (uint32_t)(r & 2) * 2u;
     const uint32_t sshift = 16u * (uint32_t)(r & 1);
+    // Its scale bytes within a slot's scale area: group r / 4, chunk q, column r % 4 (+ 128 t).
+    const uint32_t sread = kXBufBytes + (uint32_t)(r >> 2) * 32u + (uint32_t)q * 8u +
+                           (uint32_t)(r & 3) * 2u;
     const uint32_t tq = 4u * gq;
     const uint32_t ts = 4u * gs;
     // The lane's X pieces of a window: load p, row 4 p + lane / 16, piece (lane % 16) ^ row.
@@ -166,7 +214,11 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
         xk[p] = 8 * ((lane & 15) ^ row);
         xo[p] = ((uint32_t)row * (uint32_t)K + (uint32_t)xk[p]) * 2u;
     }
-    uint8_t *xb = lds + wave * D * kXBufBytes;   // this wavefront's X buffer of ring slot u: + u 4 KB
+    constexpr bool SL = mfma_scales_in_lds(W);
+    constexpr int SLOT = mfma_slot_bytes(TC, W);
+    constexpr int NS = mfma_scale_loads(TC, W);
+    static_assert(D == kMfmaDepth, "ring depth of the LDS plan");
+    uint8_t *xb = lds + wave * D * SLOT;   // this wavefront's ring slot u: + u SLOT
     const float g = *a.gscale;
     // This wavefront's windows: wave, wave + W, ...; window i of the wavefront is wave + i W.
     const int nmine = (nwin - wave + W - 1) / W;
@@ -183,11 +235,11 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     const int cs = T > 0 ? (T + nch - 1) / nch : TC;
     // Ring of D windows: D - 1 in flight while one is multiplied. Window i of a chunk sits in ring
     // slot i % D: its codes and scales in that slot's registers, its X in that slot's buffer.
-    MfmaWindow<TC> ring[D];
+    MfmaWindow<TC, SL> ring[D];
     auto load = [&](int i, int slot, int tc, int n) {
         const int w = wave + i * W;
-        ring[slot].template load<FAST>(rq, rs, rx, xb + slot * kXBufBytes, lq, ls, tq, ts, xo, xk,
-                                       w, i < nmine, tc, n, ngroups, gr, q, CH, K);
+        ring[slot].template load<FAST>(rq, rs, rx, xb + slot * SLOT, lq, sv0, sg, sh, ls, tq, ts,
+                                       xo, xk, lane, w, i < nmine, tc, n, ngroups, gr, q, CH, K);
     };
     if (T > 0) {
 #pragma unroll
@@ -206,15 +258,32 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
             for (int u = 0; u < D; u++) {
                 const int i = i0 + u;
                 if (i < nmine) {
-                    // Window i's X has landed: after it went out only its codes and scales and
-                    // the D - 2 windows behind it. Its A fragments are read before the next
-                    // window's loads go out, which write the buffer of window i - 1.
-                    wait_vm<(4 + 2 * TC) * (D - 1) - 4>();
+                    // Window i's LDS loads have landed: after them went out only its loads into
+                    // registers and the D - 2 windows behind it. Its LDS operands are read
+                    // before the next window's loads go out, which write the slot of window i - 1.
+                    constexpr int RL = SL ? TC : 2 * TC;   // register loads per window
+                    wait_vm<RL + (D - 2) * (NS + 4 + RL)>();
+                    const uint8_t *sl = xb + u * SLOT;
                     u32x4_t av[4];
-                    mfma_read_a(av, xb + u * kXBufBytes, r, q);
+                    mfma_read_a(av, sl, r, q);
+                    uint32_t sb[TC];
+                    if constexpr (SL) {
+                        const uint32_t smask =
+                            (FAST || 4 * (wave + i * W) + q < CH) ? 0xFFFFu : 0u;
+#pragma unroll
+                        for (int t = 0; t < TC; t++)
+                            sb[t] = *reinterpret_cast<const uint16_t *>(
+                                        sl + sread + (t >> 3) * 1024 + (t & 7) * 128) &
+                                    smask;
+                    }
                     load(i + D - 1, (u + D - 1) % D, tc0, nt);
                     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-                    ring[u].mul(acc, av, nt, sshift);
+                    if constexpr (!SL) {
+#pragma unroll
+                        for (int t = 0; t < TC; t++)
+                            sb[t] = ring[u].s[t] >> sshift;
+                    }
+                    ring[u].mul(acc, av, sb, nt);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -234,7 +303,7 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
         }
 
         // acc[t][e] is the partial Y[m0 + 4 q + e][c0 + 16 (tc0 + t) + r] of this wavefront.
-        float *red = reinterpret_cast<float *>(lds + W * D * kXBufBytes);   // [W][TC][4][64]
+        float *red = reinterpret_cast<float *>(lds + W * D * SLOT);   // [W][TC][4][64]
 #pragma unroll
         for (int t = 0; t < TC; t++)
 #pragma unroll
