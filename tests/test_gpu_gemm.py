@@ -46,6 +46,31 @@ def test_small_shapes(device, path, split):
                 check_close(Y, Yref, A, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("path,split", PATHS)
+def test_nan_scales_stay_in_their_columns(device, path, split):
+    """Odd column groups carry NaN (E4M3 0x7F) block scales in their first 32 k; K is not a
+    multiple of the kernels' windows, so a load that covers the end of one group's K (in the
+    packed layout) also fetches the next group's first scale bytes. Those must not reach the
+    sums: Y is NaN exactly where the oracle's is (every row of the odd groups' columns) and
+    within the bound elsewhere."""
+    seed = 5000
+    for K in (272, 400, 528, 1040):
+        for M in (1, 4, 16, 40, 128):
+            if path in VALU_PATHS and M > 8:
+                continue
+            N = 40
+            seed += 1
+            X, Wq, Ws, g = random_case(seed, M, N, K, FINITE_SCALES)
+            Ws = Ws.clone()
+            for grp in range(1, N // 4, 2):
+                Ws[4 * grp:4 * grp + 4, 0:2] = 0x7F
+            Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
+            assert np.isnan(Yref[:, 4:8]).all() and np.isfinite(Yref[:, 0:4]).all()
+            say(f"nan scales path={path} split={split} M={M} N={N} K={K}")
+            Y = gpu_gemm(X, to_device_packed(Wq, Ws, g, device), device, path, split)
+            check_close(Y, Yref, A, f"NaN scales M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 256), (4, 33, 528), (16, 48, 1024),
                                    (128, 40, 512), (7, 16, 17408), (1, 17, 5120)])
 def test_exact_integer_sums(device, M, N, K):
