@@ -21,8 +21,8 @@
 //     buffer of the window's ring slot (four direct-to-LDS loads of 1 KB; piece kp of row m at
 //     slot kp ^ m, so that the 16 rows of an A fragment fall on different bank groups), and the
 //     A fragments are read there: lane (r, q) takes row r at k = 32 q + 8 d. The loads of the
-//     next window (X first, then weights into registers) are in flight while the current one is
-//     multiplied; X needs no registers (measured against staging it through registers: q/k/v
+//     next window (those into LDS first, then the codes into registers) are in flight while the
+//     current one is multiplied; X needs no registers (measured against staging it through registers: q/k/v
 //     and o_proj at M = 32 14.2 -> 13.0 and 13.6 -> 12.4 us, o_proj at M = 8 8.6 -> 7.7, down at
 //     M = 16 19.0 -> 18.6, the wide shapes even). With 4 wavefronts the scale bytes of a window
 //     go into the slot the same way (one 1 KB load per 8 tiles instead of a 4-byte load per
