@@ -29,7 +29,8 @@
 //     tile: gate_up at M = 16 26.2 -> 25.2 us, lm_head at M = 8 106 -> 97).
 //   * B = e2m1 * s decoded to bf16 (exact); the sum over k does not depend on the slot order, so
 //     this is the plain product.
-//   * The W partial tiles are summed through LDS in wavefront order and scaled by g once.
+//   * The W partial tiles are summed through LDS in wavefront order and scaled by g once,
+//     four adjacent outputs per thread where the output's alignment allows.
 //     Results are reproducible.
 //   * FAST (K % 128 == 0) needs no per-lane K test; otherwise lanes past the last chunk read zeros.
 #pragma once
@@ -231,6 +232,15 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
     // last chunk keeps about as many bytes in flight as the others (lm_head at M = 8 and 16,
     // 38 tiles per workgroup: 8, 8, 8, 8, 6 instead of 9, 9, 9, 9, 2, medians of five interleaved
     // runs 100.6 vs 102.6 us and 105.4 vs 107.8 us).
+    // Whether the reduction stores 4 adjacent outputs per thread (16-byte Y, 8-byte H stores):
+    // N a multiple of 4 (8 for H) and an aligned output. The argmax keys keep the loop with one
+    // output per thread. Medians of four interleaved runs at M = 16 against one output per
+    // thread: gate_up 24.7 -> 24.1 us, with SiLU * up 27.1 -> 26.2, lm_head 101.1 -> 99.5 (the
+    // reduction and stores after the last window took 1.6 us of gate_up's 23.5).
+    const bool vec = a.keys == nullptr &&
+                     (a.H != nullptr ? (N & 7) == 0 && ((uintptr_t)a.H & 7) == 0
+                                     : (N & 3) == 0 && ((uintptr_t)a.Y & 15) == 0);
+
     const int nch = (T + TC - 1) / TC;
     const int cs = T > 0 ? (T + nch - 1) / nch : TC;
     // Ring of D windows: D - 1 in flight while one is multiplied. Window i of a chunk sits in ring
@@ -310,7 +320,53 @@ __global__ __launch_bounds__(kWave *W) void mfma_stream_kernel(GemmArgs a)
             for (int e = 0; e < 4; e++)
                 red[((wave * TC + t) * 4 + e) * kWave + lane] = acc[t][e];
         __syncthreads();
-        for (int idx = threadIdx.x; idx < nt * 4 * kWave; idx += kWave * W) {
+        // Else one pass of the loop below covers the chunk (and instances with 4 TC <= W, whose
+        // chunks are all that narrow, keep only that loop).
+        const bool vc = 4 * TC > W && vec && 4 * nt > W;
+        if (vc) {
+            // Four adjacent columns per thread: wavefront wave takes tiles wave, wave + W, ...;
+            // lane l adds up row 4 ((l / 4) % 4) + l / 16, columns 4 (l % 4) .. + 3 of the tile,
+            // in the order of the loop below (wavefront 0 first), so the sums are the same.
+            const int e = lane >> 4;
+            const int qq = (lane >> 2) & 3;
+            const int cc = lane & 3;
+            const int row = 4 * qq + e;
+            const int ln0 = 16 * qq + 4 * cc;
+            for (int t = wave; t < nt; t += W) {
+                const int colx = 16 * (tc0 + t) + 4 * cc;
+                if (row >= mrows || colx >= ncols)
+                    continue;
+                const f32x4_t *rv = reinterpret_cast<const f32x4_t *>(red + (t * 4 + e) * kWave + ln0);
+                if (a.H != nullptr) {
+                    // Gate columns 4 cc .. + 3 (cc even) and their up partners in lanes + 4.
+                    if ((cc & 1) != 0)
+                        continue;
+                    f32x4_t sg = rv[0], su = rv[1];
+                    for (int v = 1; v < W; v++) {
+                        sg += rv[v * TC * kWave];
+                        su += rv[v * TC * kWave + 1];
+                    }
+                    uint16_t h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float gate = sg[j] * g, up = su[j] * g;
+                        h[j] = __builtin_bit_cast(uint16_t,
+                                                  (__bf16)(gate / (1.0f + __expf(-gate)) * up));
+                    }
+                    const int n = c0 + colx;
+                    *reinterpret_cast<uint2 *>(a.H + (size_t)(m0 + row) * (size_t)(N >> 1) +
+                                               4 * (n >> 3)) =
+                        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                } else {
+                    f32x4_t s = rv[0];
+                    for (int v = 1; v < W; v++)
+                        s += rv[v * TC * kWave];
+                    *reinterpret_cast<f32x4_t *>(a.Y + (size_t)(m0 + row) * N + c0 + colx) = s * g;
+                }
+            }
+        }
+        for (int idx = vc ? nt * 4 * kWave : threadIdx.x; idx < nt * 4 * kWave; idx += kWave * W) {
             const int t = idx / (4 * kWave);
             const int e = (idx / kWave) % 4;
             const int ln = idx % kWave;

@@ -94,6 +94,32 @@ def test_fused_against_oracle(device, M, N, K, fuse):
         _check_y(out.cpu().numpy(), Yref, tol, label)
 
 
+@pytest.mark.parametrize("M", [5, 16, 19])
+def test_silu_store_widths_agree(device, M):
+    """SiLU(gate) * up stored four outputs per thread (H 8-byte aligned, N % 8 == 0) or one (H
+    only 2-byte aligned) gives the same bits, within the bound of the oracle; wide enough that a
+    workgroup takes several chunks of tiles, with whole gate/up pairs split unevenly."""
+    N, K = 256 * 16 * 14 + 8 * 13, 256
+    gen = inputs.generator(4100 + M)
+    Wq, Ws = inputs.random_packed(gen, N, K, FINITE_SCALES)
+    g = np.float32(0.011)
+    X = inputs.activations(gen, M, K, outliers=4)
+    label = f"silu store widths M={M} N={N} K={K}"
+    say(label)
+    p = to_device_packed(Wq, Ws, g, device)
+    Xd = X.to(device)
+    Ha = nv.gemm_fused(Xd, p.Wq, p.Ws, p.g, N, silu_mul=True)
+    buf = torch.zeros(M * (N // 2) + 1, dtype=torch.bfloat16, device=device)
+    Hb = buf[1:].view(M, N // 2)
+    nv.gemm_fused(Xd, p.Wq, p.Ws, p.g, N, silu_mul=True, out=Hb)
+    torch.cuda.synchronize()
+    a = Ha.cpu().view(torch.int16).numpy().view(np.uint16)
+    b = Hb.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(a, b), f"{label}: store widths differ"
+    Yref, tol = _ref_gemm(_bits_of(X), Wq.numpy(), Ws.numpy(), g)
+    _check_h(a, Yref, tol, label)
+
+
 def test_rmsnorm_constant_rows(device):
     """Rows of one constant c with eps = 0 normalise to gamma * sign(c) exactly, so the fused
     GEMM equals the plain GEMM of gamma (bit for bit in exact-sum cases)."""

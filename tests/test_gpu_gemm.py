@@ -162,6 +162,29 @@ def test_many_columns_per_workgroup(device, path, split):
     check_close(Y, Yref, A, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("split", [4, 8])
+def test_reduction_store_widths_agree(device, split):
+    """The 16-row kernel stores four adjacent outputs per thread when Y is 16-byte aligned and
+    N % 4 == 0, one per thread otherwise (Y only 4-byte aligned): the same bits either way, and
+    within the bound of the oracle. Several chunks of tiles per workgroup, a part-filled last
+    tile (57492 / 4 groups do not split evenly over the workgroups) and a ragged row block."""
+    N, K = 256 * 16 * 14 + 4 * 37, 256
+    for M in (5, 16, 19):
+        X, Wq, Ws, g = random_case(70 + M, M, N, K, FINITE_SCALES)
+        p = to_device_packed(Wq, Ws, g, device)
+        Xd = X.to(device)
+        say(f"store widths split={split} M={M} N={N} K={K}")
+        Ya = nv.gemm(Xd, *p, path=nv.PATH_MFMA, split=split)
+        buf = torch.full((M * N + 1,), float("nan"), dtype=torch.float32, device=device)
+        Yb = buf[1:].view(M, N)
+        nv.gemm(Xd, *p, path=nv.PATH_MFMA, split=split, out=Yb)
+        torch.cuda.synchronize()
+        a, b = Ya.cpu().numpy(), Yb.cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"M={M}: store widths differ"
+        Yref, A = oracle.gemm(inputs.bf16_bits(X), Wq.numpy(), Ws.numpy(), g)
+        check_close(a.astype(np.float64), Yref, A, f"M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M,N,split", [(16, 34813, 0), (100, 34813, 0), (128, 34813, 128),
                                        (33, 18431, 0), (128, 22521, 128), (16, 22521, 16),
                                        (128, 1795, 32), (70, 4099, 64)])
