@@ -42,11 +42,14 @@
 //     exact), and row 16 b + r of X at those k its A fragment of row block b
 //     (v_mfma_f32_16x16x32_bf16). X rows sit in LDS with piece kp of row m at slot kp ^ (m & 15),
 //     so the 16 rows of an A fragment hit 16 different bank groups.
-//   * At the end of a pass the four k-step partial sums of every output meet in LDS in a fixed
-//     order (((ks3 + ks2) + ks1) + ks0, and the remainder tile's four parts likewise) as a
-//     row-major tile of Y; then all 512 threads write whole rows of it (16-byte stores),
-//     Y = sum * g. Results are reproducible. Weights with more tiles per workgroup than TW are
-//     done in several passes, each streaming X again.
+//   * At the end of a pass the four k-step partial sums of every output meet in LDS, 64 rows at
+//     a time (LDS holds four k-steps' partials of 64 rows of 9 tiles): every wavefront writes
+//     its partials to its k-step's area at once, then all 512 threads add the four areas in a
+//     fixed order (((ks3 + ks2) + ks1) + ks0, the remainder tile's parts likewise) and write
+//     whole rows (16-byte stores), Y = sum * g. Results are reproducible. (The k-steps had taken
+//     turns adding into one tile, two wavefronts at a time: medians of two interleaved runs at
+//     M = 128, gate_up 65.4 -> 59.8 us, lm_head 267 -> 249, q/k/v 26.2 -> 25.6.) Weights with
+//     more tiles per workgroup than TW are done in several passes, each streaming X again.
 //   * MODE 0 stores Y; MODE 1 folds Y into argmax keys (argmax.h), one slot per row and tile
 //     set; MODE 2 writes H = bf16(SiLU(gate) * up) of an interleaved gate/up weight.
 #pragma once
@@ -95,11 +98,17 @@ struct SlabShape {
     // Waves 0-3 issue the X loads (16 RB rows, 4 per load: RB loads each per window), waves 4-7
     // the weight loads (codes then scales, the same count each, padded).
     static_assert((DX - 2) * XL < 64 && (DW - 2) * WL < 64, "vmcnt range");
-    // End of a pass: Y as a row-major tile [16 RB][YST] (the row padding keeps the four rows a
-    // fragment writes on different banks), and the remainder tile's four parts [4][16 RB][20].
+    // End of a pass: the rows go through in NPH phases of PR = 16 PB rows (LDS holds the four
+    // k-steps' partials of 64 rows of 9 tiles at most). In a phase, the partials of k-step k sit
+    // in area k as a row-major tile [PR][YST] of floats (the row padding keeps the four rows a
+    // fragment writes on different banks).
+    static constexpr int PB = RB < 4 ? RB : 4;
+    static constexpr int PR = 16 * PB;
+    static constexpr int NPH = RB / PB;
     static constexpr int YST = 16 * TW + 4;
-    static constexpr int YBYTES = 16 * RB * YST * 4;
-    static constexpr int EPI = YBYTES + (NR ? 4 * 16 * RB * 20 * 4 : 0);
+    static constexpr int AREA = PR * YST;         // floats of one k-step's area
+    static constexpr int EPI = 4 * AREA * 4;
+    static_assert(EPI <= kSlabMaxLds, "exchange areas do not fit in LDS");
     static constexpr int RING = SINKOFF + SINK;
     static constexpr int LDS = (RING > EPI) ? RING : EPI;
 };
@@ -280,7 +289,10 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
 
     prologue(0);
 
-    argkey_t best = 0;   // greedy token: the key of this thread's row (see the epilogue)
+    argkey_t best[S::NPH];   // greedy token: the key of this thread's row of each phase
+#pragma unroll
+    for (int h = 0; h < S::NPH; h++)
+        best[h] = 0;
 
     for (int pass = 0; pass < L.passes; pass++) {
         f32x4_t acc[HT][RB];
@@ -399,7 +411,7 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
         else
             windows(std::false_type{});
 
-        // ---- end of pass: the partial sums meet in LDS as a row-major tile of Y ----
+        // ---- end of pass: the partial sums meet in LDS, a phase of PR rows at a time ----
         wait_vm<0>();   // the loads in flight (next pass, or zeros past the end) landed
         slab_barrier();      // every wavefront is done with the ring buffers
         // The lane's part of the LDS addresses is made opaque here, so that the compiler computes
@@ -407,128 +419,132 @@ __global__ __launch_bounds__(kWave *kSlabWaves) void mfma_slab_kernel(GemmArgs a
         // (where they would stay live, in registers, across every window).
         uint32_t lane_off = 4u * (uint32_t)((4 * q) * S::YST + r);
         asm volatile("" : "+v"(lane_off));
-        float *ys = reinterpret_cast<float *>(lds + lane_off);          // + (row0 * YST + col)
-        float *rs = reinterpret_cast<float *>(lds + S::YBYTES + 4u * (uint32_t)((4 * q) * 20 + r));
-        // k-steps 3, 2, 1, 0 in turn: the first writes its sums, the others add theirs. The
-        // remainder holders write their part to their k-step's slot with the first round.
-#pragma unroll
-        for (int round = 3; round >= 0; round--) {
-            if (ks == round) {
-#pragma unroll
-                for (int j = 0; j < HT; j++)
-#pragma unroll
-                    for (int b = 0; b < RB; b++) {
-#pragma unroll
-                        for (int e = 0; e < 4; e++) {
-                            float &y = ys[(16 * b + e) * S::YST + 16 * (2 * j + ts)];
-                            y = round == 3 ? acc[j][b][e] : y + acc[j][b][e];
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-            }
-            if constexpr (NR != 0) {
-                if (round == 3 && rem) {
-#pragma unroll
-                    for (int b = 0; b < RB; b++)
-#pragma unroll
-                        for (int e = 0; e < 4; e++)
-                            rs[(ks * 16 * RB + 16 * b + e) * 20] = racc[b][e];
-                }
-            }
-            slab_barrier();
-        }
-        float *ybase = reinterpret_cast<float *>(lds);
-        if constexpr (NR != 0) {
-            const float *rbase = reinterpret_cast<const float *>(lds + S::YBYTES);
-            for (int idx = threadIdx.x; idx < 16 * RB * 16; idx += kThreads) {
-                const int row = idx >> 4, c = idx & 15;
-                const float v = ((rbase[(3 * 16 * RB + row) * 20 + c] +
-                                  rbase[(2 * 16 * RB + row) * 20 + c]) +
-                                 rbase[(1 * 16 * RB + row) * 20 + c]) +
-                                rbase[(0 * 16 * RB + row) * 20 + c];
-                ybase[row * S::YST + 16 * (2 * HT) + c] = v;
-            }
-            slab_barrier();
-        }
-        // The finished tile leaves LDS row by row: columns c0 + 16 TW pass + col.
+        float *ys = reinterpret_cast<float *>(lds + lane_off) + ks * S::AREA;   // + row * YST + col
+        const float *area = reinterpret_cast<const float *>(lds);
+        // Output (row, col) of the phase: ((ks 3 + ks 2) + ks 1) + ks 0, for four columns.
+        auto sum4 = [&](int o) -> f32x4_t {
+            const f32x4_t *p = reinterpret_cast<const f32x4_t *>(area + o);
+            constexpr int A4 = S::AREA / 4;
+            f32x4_t v = p[3 * A4] + p[2 * A4];
+            v = v + p[A4];
+            return v + p[0];
+        };
+        // The pass's columns: c0 + 16 TW pass + col.
         const int pc0 = c0 + 16 * TW * pass;                      // first column of the pass
         const int pcols = min(ncols - 16 * TW * pass, 16 * TW);   // columns of the pass
-        if constexpr (MODE == kSlabStore) {
-            const rsrc_t ry = make_rsrc(a.Y + (size_t)m0 * N, (uint32_t)mrows * (uint32_t)N * 4u);
-            const int quads = (pcols + 3) >> 2;
-            for (int idx = threadIdx.x; idx < mrows * quads; idx += kThreads) {
-                const int row = idx / quads;
-                const int col = 4 * (idx - row * quads);
-                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + col);
-                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)(pc0 + col)) * 4u;
-                if (L.vec && col + 3 < pcols) {
-                    u32x4_t o;
+#pragma unroll
+        for (int h = 0; h < S::NPH; h++) {
+            // Every wavefront writes its partials of row blocks PB h .. PB h + PB - 1 to its
+            // k-step's area (tiles 2 j + ts, and the remainder tile's k-step ks if it holds it),
+            // all wavefronts at once: no reads, no rounds.
+#pragma unroll
+            for (int j = 0; j < HT; j++)
+#pragma unroll
+                for (int b = 0; b < S::PB; b++)
 #pragma unroll
                     for (int e = 0; e < 4; e++)
-                        o[e] = __float_as_uint(v[e] * g);
-                    __builtin_amdgcn_raw_buffer_store_b128(o, ry, off, 0, 0);
-                } else {
+                        ys[(16 * b + e) * S::YST + 16 * (2 * j + ts)] = acc[j][S::PB * h + b][e];
+            if constexpr (NR != 0) {
+                if (rem) {
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        if (col + e < pcols)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e] * g), ry,
-                                                                  off + 4u * e, 0, 0);
+                    for (int b = 0; b < S::PB; b++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            ys[(16 * b + e) * S::YST + 16 * (2 * HT)] = racc[S::PB * h + b][e];
                 }
             }
-        } else if constexpr (MODE == kSlabSilu) {
-            // Column block p of 8: gate columns 8 p .. 8 p + 3, up 8 p + 4 .. 8 p + 7 give
-            // H[m][(pc0 >> 1) + 4 p .. + 3] (pc0 and pcols are multiples of 8).
-            const int blocks = pcols >> 3;
-            const size_t hstride = (size_t)(N >> 1);
-            for (int idx = threadIdx.x; idx < mrows * blocks; idx += kThreads) {
-                const int row = idx / blocks;
-                const int p8 = idx - row * blocks;
-                const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + 8 * p8);
-                const f32x4_t uv =
-                    *reinterpret_cast<const f32x4_t *>(ybase + row * S::YST + 8 * p8 + 4);
-                uint16_t hb[4];
+            slab_barrier();
+            const int r0 = S::PR * h;                   // first row of the phase in the group
+            const int prows = min(S::PR, mrows - r0);   // its rows that exist (may be <= 0)
+            if constexpr (MODE == kSlabStore) {
+                const rsrc_t ry =
+                    make_rsrc(a.Y + (size_t)m0 * N, (uint32_t)mrows * (uint32_t)N * 4u);
+                const int quads = (pcols + 3) >> 2;
+                for (int idx = threadIdx.x; idx < prows * quads; idx += kThreads) {
+                    const int row = idx / quads;
+                    const int col = 4 * (idx - row * quads);
+                    const f32x4_t v = sum4(row * S::YST + col);
+                    const uint32_t off =
+                        ((uint32_t)(r0 + row) * (uint32_t)N + (uint32_t)(pc0 + col)) * 4u;
+                    if (L.vec && col + 3 < pcols) {
+                        u32x4_t o;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float gt = gv[e] * g, u = uv[e] * g;
-                    hb[e] = __builtin_bit_cast(uint16_t, (__bf16)(gt / (1.0f + __expf(-gt)) * u));
-                }
-                uint16_t *dst = a.H + (size_t)(m0 + row) * hstride + (size_t)(pc0 >> 1) + 4 * p8;
-                if (L.vec) {
-                    *reinterpret_cast<u32x2_t *>(dst) =
-                        u32x2_t{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16),
-                                (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
-                } else {
+                        for (int e = 0; e < 4; e++)
+                            o[e] = __float_as_uint(v[e] * g);
+                        __builtin_amdgcn_raw_buffer_store_b128(o, ry, off, 0, 0);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        dst[e] = hb[e];
+                        for (int e = 0; e < 4; e++)
+                            if (col + e < pcols)
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e] * g),
+                                                                      ry, off + 4u * e, 0, 0);
+                    }
                 }
+            } else if constexpr (MODE == kSlabSilu) {
+                // Column block p of 8: gate columns 8 p .. 8 p + 3, up 8 p + 4 .. 8 p + 7 give
+                // H[m][(pc0 >> 1) + 4 p .. + 3] (pc0 and pcols are multiples of 8).
+                const int blocks = pcols >> 3;
+                const size_t hstride = (size_t)(N >> 1);
+                for (int idx = threadIdx.x; idx < prows * blocks; idx += kThreads) {
+                    const int row = idx / blocks;
+                    const int p8 = idx - row * blocks;
+                    const f32x4_t gv = sum4(row * S::YST + 8 * p8);
+                    const f32x4_t uv = sum4(row * S::YST + 8 * p8 + 4);
+                    uint16_t hb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float gt = gv[e] * g, u = uv[e] * g;
+                        hb[e] = __builtin_bit_cast(uint16_t, (__bf16)(gt / (1.0f + __expf(-gt)) * u));
+                    }
+                    uint16_t *dst =
+                        a.H + (size_t)(m0 + r0 + row) * hstride + (size_t)(pc0 >> 1) + 4 * p8;
+                    if (L.vec) {
+                        *reinterpret_cast<u32x2_t *>(dst) =
+                            u32x2_t{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16),
+                                    (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            dst[e] = hb[e];
+                    }
+                }
+            } else {
+                // Greedy token: TPR threads per row of the phase scan its columns (col = part,
+                // part + TPR, ...) and fold them into one key; the key of that row over all
+                // passes stays with those threads.
+                constexpr int TPR = kThreads / S::PR;
+                const int row = threadIdx.x / TPR;
+                const int part = threadIdx.x - row * TPR;
+                argkey_t k = 0;
+                if (row < prows)
+                    for (int col = part; col < pcols; col += TPR) {
+                        const int o = row * S::YST + col;
+                        const float y = ((area[o + 3 * S::AREA] + area[o + 2 * S::AREA]) +
+                                         area[o + S::AREA]) +
+                                        area[o];
+                        k = key_max(k, argmax_key(y * g, pc0 + col));
+                    }
+#pragma unroll
+                for (int d = 1; d < TPR; d <<= 1)
+                    k = key_max(k, shfl_xor_key(k, d));
+                best[h] = key_max(best[h], k);
             }
-        } else {
-            // Greedy token: TPR threads per row scan its columns (col = part, part + TPR, ...)
-            // and fold them into one key; the row's key over all passes stays with those threads.
-            constexpr int TPR = kThreads / (16 * RB);
-            const int row = threadIdx.x / TPR;
-            const int part = threadIdx.x - row * TPR;
-            argkey_t k = 0;
-            if (row < mrows)
-                for (int col = part; col < pcols; col += TPR)
-                    k = key_max(k, argmax_key(ybase[row * S::YST + col] * g, pc0 + col));
-#pragma unroll
-            for (int d = 1; d < TPR; d <<= 1)
-                k = key_max(k, shfl_xor_key(k, d));
-            best = key_max(best, k);
+            slab_barrier();   // the areas are written again by the next phase or pass
         }
-        slab_barrier();   // the exchange area is reused by the next pass's windows
         if (pass + 1 < L.passes)
             prologue(pass + 1);
     }
 
     if constexpr (MODE == kSlabArgmax) {
         // One key per row and workgroup: slot `set` of the row.
-        constexpr int TPR = kThreads / (16 * RB);
+        constexpr int TPR = kThreads / S::PR;
         const int row = threadIdx.x / TPR;
-        if (threadIdx.x - row * TPR == 0 && row < mrows)
-            a.keys[(size_t)(m0 + row) * L.key_slots + set] = best;
+        if (threadIdx.x - row * TPR == 0) {
+#pragma unroll
+            for (int h = 0; h < S::NPH; h++)
+                if (S::PR * h + row < mrows)
+                    a.keys[(size_t)(m0 + S::PR * h + row) * L.key_slots + set] = best[h];
+        }
     }
 }
 
