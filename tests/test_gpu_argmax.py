@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 CASES = [(nv.PATH_DOT, 16, 1), (nv.PATH_DOT, 4, 3), (nv.PATH_DOT, 8, 8),
          (nv.PATH_MFMA, 4, 5), (nv.PATH_MFMA, 8, 16), (nv.PATH_MFMA, 8, 33),
          (nv.PATH_BATCH, 0, 40), (nv.PATH_BATCH, 32, 128), (nv.PATH_BATCH, 64, 130),
-         (nv.PATH_BATCH, 16, 64), (nv.PATH_BATCH, 128, 129),
+         (nv.PATH_BATCH, 16, 64), (nv.PATH_BATCH, 128, 129), (nv.PATH_BATCH, 128, 100),
          (nv.PATH_INVARIANT, 0, 1), (nv.PATH_INVARIANT, 0, 17),
          (nv.PATH_AUTO, 0, 1), (nv.PATH_AUTO, 0, 16), (nv.PATH_AUTO, 0, 128)]
 

@@ -94,11 +94,12 @@ def test_fused_against_oracle(device, M, N, K, fuse):
         _check_y(out.cpu().numpy(), Yref, tol, label)
 
 
-@pytest.mark.parametrize("M", [5, 16, 19])
+@pytest.mark.parametrize("M", [5, 16, 19, 100])
 def test_silu_store_widths_agree(device, M):
     """SiLU(gate) * up stored four outputs per thread (H 8-byte aligned, N % 8 == 0) or one (H
     only 2-byte aligned) gives the same bits, within the bound of the oracle; wide enough that a
-    workgroup takes several chunks of tiles, with whole gate/up pairs split unevenly."""
+    workgroup takes several chunks of tiles, with whole gate/up pairs split unevenly (M = 100:
+    the slab kernel's 128-row group, its rows in two halves, the second ragged)."""
     N, K = 256 * 16 * 14 + 8 * 13, 256
     gen = inputs.generator(4100 + M)
     Wq, Ws = inputs.random_packed(gen, N, K, FINITE_SCALES)

@@ -162,22 +162,26 @@ def test_many_columns_per_workgroup(device, path, split):
     check_close(Y, Yref, A, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("split", [4, 8])
-def test_reduction_store_widths_agree(device, split):
-    """The 16-row kernel stores four adjacent outputs per thread when Y is 16-byte aligned and
-    N % 4 == 0, one per thread otherwise (Y only 4-byte aligned): the same bits either way, and
-    within the bound of the oracle. Several chunks of tiles per workgroup, a part-filled last
-    tile (57492 / 4 groups do not split evenly over the workgroups) and a ragged row block."""
+@pytest.mark.parametrize("path,split,Ms", [(nv.PATH_MFMA, 4, (5, 16, 19)),
+                                           (nv.PATH_MFMA, 8, (5, 16, 19)),
+                                           (nv.PATH_BATCH, 128, (19, 100, 128)),
+                                           (nv.PATH_BATCH, 0, (100,))])
+def test_reduction_store_widths_agree(device, path, split, Ms):
+    """The 16-row and slab kernels store four adjacent outputs per thread when Y is 16-byte
+    aligned and N % 4 == 0, one per thread otherwise (Y only 4-byte aligned): the same bits
+    either way, and within the bound of the oracle. Several chunks (passes) of tiles per
+    workgroup, a part-filled last tile (57492 / 4 groups do not split evenly over the
+    workgroups), ragged row blocks, and 128-row groups whose rows go through in two halves."""
     N, K = 256 * 16 * 14 + 4 * 37, 256
-    for M in (5, 16, 19):
+    for M in Ms:
         X, Wq, Ws, g = random_case(70 + M, M, N, K, FINITE_SCALES)
         p = to_device_packed(Wq, Ws, g, device)
         Xd = X.to(device)
-        say(f"store widths split={split} M={M} N={N} K={K}")
-        Ya = nv.gemm(Xd, *p, path=nv.PATH_MFMA, split=split)
+        say(f"store widths path={path} split={split} M={M} N={N} K={K}")
+        Ya = nv.gemm(Xd, *p, path=path, split=split)
         buf = torch.full((M * N + 1,), float("nan"), dtype=torch.float32, device=device)
         Yb = buf[1:].view(M, N)
-        nv.gemm(Xd, *p, path=nv.PATH_MFMA, split=split, out=Yb)
+        nv.gemm(Xd, *p, path=path, split=split, out=Yb)
         torch.cuda.synchronize()
         a, b = Ya.cpu().numpy(), Yb.cpu().numpy()
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"M={M}: store widths differ"
