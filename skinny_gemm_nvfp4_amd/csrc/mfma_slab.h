@@ -89,8 +89,13 @@ struct SlabShape {
     static constexpr int WL = (NWL + 3) / 4;      // weight loads per weight wavefront and window
     static constexpr int BUDGET = kSlabMaxLds - SINK;
     static constexpr int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
-    static constexpr int DX = clampi((BUDGET - 4 * WBYTES) / XBYTES, 3, 5);
-    static constexpr int DW = clampi((BUDGET - DX * XBYTES) / WBYTES, 4, 8);
+    // Row groups of at most 32 rows with 8-9 tiles per pass (gate/up and the lm_head at small M)
+    // keep at most 4 and 6: medians of two interleaved runs, the batch-invariant mode at one row
+    // gate_up 32.1 -> 30.3 us, lm_head 121.2 -> 118.2; at M = 32 gate_up 38.1 -> 37.2, the lm_head
+    // 145.3 -> 143.4 (on the narrow shapes shallower rings were slower: down 38.7 -> 42.4).
+    static constexpr bool SHALLOW = RB <= 2 && HT == 4;
+    static constexpr int DX = clampi((BUDGET - 4 * WBYTES) / XBYTES, 3, SHALLOW ? 4 : 5);
+    static constexpr int DW = clampi((BUDGET - DX * XBYTES) / WBYTES, 4, SHALLOW ? 6 : 8);
     static_assert(DX * XBYTES + DW * WBYTES <= BUDGET, "slab buffers do not fit in LDS");
     static constexpr int XOFF = 0;
     static constexpr int WOFF = DX * XBYTES;
