@@ -89,13 +89,21 @@ struct SlabShape {
     static constexpr int WL = (NWL + 3) / 4;      // weight loads per weight wavefront and window
     static constexpr int BUDGET = kSlabMaxLds - SINK;
     static constexpr int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
-    // Row groups of at most 32 rows with 8-9 tiles per pass (gate/up and the lm_head at small M)
-    // keep at most 4 and 6: medians of two interleaved runs, the batch-invariant mode at one row
-    // gate_up 32.1 -> 30.3 us, lm_head 121.2 -> 118.2; at M = 32 gate_up 38.1 -> 37.2, the lm_head
-    // 145.3 -> 143.4 (on the narrow shapes shallower rings were slower: down 38.7 -> 42.4).
-    static constexpr bool SHALLOW = RB <= 2 && HT == 4;
-    static constexpr int DX = clampi((BUDGET - 4 * WBYTES) / XBYTES, 3, SHALLOW ? 4 : 5);
-    static constexpr int DW = clampi((BUDGET - DX * XBYTES) / WBYTES, 4, SHALLOW ? 6 : 8);
+    // Caps by instance, measured (medians of interleaved runs):
+    //   * row groups of at most 32 rows with 8-9 tiles per pass (gate/up and the lm_head at small
+    //     M) keep at most 4 and 6: the batch-invariant mode at one row gate_up 32.1 -> 30.3 us,
+    //     lm_head 121.2 -> 118.2; at M = 32 gate_up 38.1 -> 37.2, the lm_head 145.3 -> 143.4 (the
+    //     narrow shapes of those row groups were slower so: down 38.7 -> 42.4);
+    //   * 64-row groups with at most 5 tiles per pass (q/k/v, o_proj and down at M = 128) keep 3
+    //     and 4: q/k/v 25.9 -> 25.2, o_proj 23.6 -> 22.4, down 65.2 -> 63.2 (three runs; with 4 and
+    //     6 down was slower, 65.0 -> 66.0);
+    //   * the others at most 5 and 8.
+    static constexpr bool WIDE_SMALL = RB <= 2 && HT == 4;
+    static constexpr bool NARROW_64 = RB == 4 && HT <= 2;
+    static constexpr int XCAP = WIDE_SMALL ? 4 : NARROW_64 ? 3 : 5;
+    static constexpr int WCAP = WIDE_SMALL ? 6 : NARROW_64 ? 4 : 8;
+    static constexpr int DX = clampi((BUDGET - 4 * WBYTES) / XBYTES, 3, XCAP);
+    static constexpr int DW = clampi((BUDGET - DX * XBYTES) / WBYTES, 4, WCAP);
     static_assert(DX * XBYTES + DW * WBYTES <= BUDGET, "slab buffers do not fit in LDS");
     static constexpr int XOFF = 0;
     static constexpr int WOFF = DX * XBYTES;
