@@ -97,11 +97,15 @@ struct SlabShape {
     //   * 64-row groups with at most 5 tiles per pass (q/k/v, o_proj and down at M = 128) keep 3
     //     and 4: q/k/v 25.9 -> 25.2, o_proj 23.6 -> 22.4, down 65.2 -> 63.2 (three runs; with 4 and
     //     6 down was slower, 65.0 -> 66.0);
+    //   * 128-row groups with an even number of tiles per pass (the lm_head at M > 64) keep at
+    //     most 4 weight windows: the lm_head at M = 128 251.4 -> 247.5 us, at M = 96 229.7 ->
+    //     226.9 (four runs; gate/up, with a remainder tile, was even);
     //   * the others at most 5 and 8.
     static constexpr bool WIDE_SMALL = RB <= 2 && HT == 4;
     static constexpr bool NARROW_64 = RB == 4 && HT <= 2;
+    static constexpr bool EVEN_128 = RB == 8 && NR == 0;
     static constexpr int XCAP = WIDE_SMALL ? 4 : NARROW_64 ? 3 : 5;
-    static constexpr int WCAP = WIDE_SMALL ? 6 : NARROW_64 ? 4 : 8;
+    static constexpr int WCAP = WIDE_SMALL ? 6 : (NARROW_64 || EVEN_128) ? 4 : 8;
     static constexpr int DX = clampi((BUDGET - 4 * WBYTES) / XBYTES, 3, XCAP);
     static constexpr int DW = clampi((BUDGET - DX * XBYTES) / WBYTES, 4, WCAP);
     static_assert(DX * XBYTES + DW * WBYTES <= BUDGET, "slab buffers do not fit in LDS");
